@@ -1,0 +1,247 @@
+#!/usr/bin/env python3
+"""Benchmark of the prefill attention-unit path on one MI355X.
+
+One step = the whole path on one batch of synthetic input, on one HIP stream:
+  qkv_proj (fused QKV GEMM) -> prefill_attention (causal GQA flash attention,
+  reading Q/K/V as strided views of the projection output) -> kv_cache_write
+  (paged scatter into 16-token pages).
+Inputs are seeded draws (``workloads``) already resident in HBM before timing.
+
+Printed: one JSON line.  ``value`` is the attention throughput in TFLOP/s
+(causal FLOPs counted as 2*2*s^2*head_dim*n_head/2, summed over sequences)
+over the attention kernel's average duration inside the timed steps, measured
+with HIP events on the stream the kernels run on; ``ms_per_step`` is the wall
+time of a whole step.  ``roofline`` describes the attention kernel against the
+bf16 dense MFMA peak, ``kernels`` every kernel, ``cpu_baseline`` the fp64 CPU
+oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
+METRIC = "prefill attention TFLOPS + % bf16 MFMA peak, s=8192 GQA 32q/8kv hd128"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gqa_s8192",
+                    help="gqa_s8192 (default), mha_s2048, varlen16_gqa, long_gqa_s32768_fp8kv")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU oracle sample time")
+    ap.add_argument("--kv-cold-reps", type=int, default=20)
+    return ap.parse_args()
+
+
+def source_sha(name):
+    p = os.path.join(ROOT, "prefill_causal_attention_amd", "csrc", name)
+    with open(p, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    if t.get("attn_fwd_sha") != source_sha("attn_fwd.hip"):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, target_s):
+    """Time the fp64 oracle's attention on a sample of query rows (all heads)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import workloads
+    from oracle import attention as A
+
+    buf, *_ = workloads.qkv_inputs(w)
+    b = buf.view(__import__("torch").int16).numpy().view(np.uint16)
+    q, k, v = A.head_split(b, w.n_head, w.n_kv_head, w.head_dim)
+    cu = workloads.cu_seqlens(w)
+    rng = np.random.default_rng(12345)
+
+    def run(n):
+        rows = np.sort(rng.choice(w.total_tokens, size=n, replace=False))
+        t0 = time.perf_counter()
+        A.varlen_causal_attention(q, k, v, cu, rows=rows)
+        dt = time.perf_counter() - t0
+        seq = np.searchsorted(cu, rows, side="right") - 1
+        pos = rows - cu[seq]
+        flops = float(np.sum(4.0 * (pos + 1) * w.head_dim * w.n_head))   # causal work of these rows
+        return dt, flops
+
+    dt, _ = run(32)
+    n = int(min(w.total_tokens, max(64, 32 * target_s / max(dt, 1e-3))))
+    dt, flops = run(n)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} query rows drawn uniformly from {w.total_tokens}, all {w.n_head} heads, "
+                      f"fp64 numpy oracle (full-width masked score rows, two-pass softmax); "
+                      f"causal FLOPs of those rows / {dt:.1f} s; BLAS threads={threads}, host cpus={os.cpu_count()}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this path has no multi-GPU form.",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import prefill_causal_attention_amd as pca
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    pca.load()
+    w = workloads.BY_NAME[args.workload]
+    dev = torch.device("cuda:0")
+    T, nk = w.total_tokens, w.n_kv_head * w.head_dim
+    lay = pca.kv_layout(w.n_head, w.n_kv_head, w.head_dim, 16, "fp8_e4m3" if w.cache == "fp8" else "bf16")
+
+    x, wq = workloads.projection_inputs(w)
+    x = x.to(dev)
+    wt = wq.t().contiguous().to(dev)          # weight pre-transposed once, untimed
+    del wq
+    y = torch.empty((T, lay["qkv_ld"]), dtype=torch.bfloat16, device=dev)
+    o = torch.empty((T, w.n_head * w.head_dim), dtype=torch.bfloat16, device=dev)
+    cu = torch.from_numpy(workloads.cu_seqlens(w)).to(dev)
+    bt_h = workloads.block_table(w)
+    bt = torch.from_numpy(np.where(bt_h < 0, 0, bt_h).astype(np.int32)).to(dev)
+    shape = (w.num_pages, 16, w.n_kv_head, w.head_dim)
+    fp8 = w.cache == "fp8"
+    kc = torch.zeros(shape, dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev)
+    vc = torch.zeros_like(kc)
+    ks = torch.zeros(shape[:3], dtype=torch.float32, device=dev) if fp8 else None
+    vs = torch.zeros_like(ks) if fp8 else None
+    q = y[:, lay["q_off"]:lay["q_off"] + w.n_head * w.head_dim]
+    k = y[:, lay["k_off"]:lay["k_off"] + nk]
+    v = y[:, lay["v_off"]:lay["v_off"] + nk]
+    cache_dtype = "fp8_e4m3" if fp8 else "bf16"
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        pca.qkv_proj(x, wt, y)
+        if ev is not None:
+            ev[1].record(stream)
+        pca.prefill_attention(q, k, v, o, w.n_head, w.n_kv_head, w.head_dim, cu_seqlens=cu,
+                              max_seqlen=w.max_seqlen)
+        if ev is not None:
+            ev[2].record(stream)
+        pca.kv_cache_write(k, v, bt, kc, vc, w.n_kv_head, w.head_dim, cu_seqlens=cu,
+                           cache_dtype=cache_dtype, k_scale=ks, v_scale=vs)
+        if ev is not None:
+            ev[3].record(stream)
+
+    print(f"[bench] workload={w.name} T={T} warmup={args.warmup} steps={args.steps}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    t_gemm = np.array([e[0].elapsed_time(e[1]) for e in events])
+    t_attn = np.array([e[1].elapsed_time(e[2]) for e in events])
+    t_kv = np.array([e[2].elapsed_time(e[3]) for e in events])
+    print(f"[bench] timed {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
+
+    # cold KV write: evict L2 and the MALL with a 1 GiB write before each launch
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cold = []
+    for _ in range(args.kv_cold_reps):
+        flush.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        pca.kv_cache_write(k, v, bt, kc, vc, w.n_kv_head, w.head_dim, cu_seqlens=cu,
+                           cache_dtype=cache_dtype, k_scale=ks, v_scale=vs)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    del flush
+    t_kv_cold = np.array(cold)
+
+    att_flops = w.attention_flops()
+    gemm_flops = w.gemm_flops()
+    eb = 1 if fp8 else 2
+    kv_bytes = 2 * T * nk * 2 + 2 * T * nk * eb + (2 * T * w.n_kv_head * 4 if fp8 else 0) + 4 * T // 16
+    attn_bytes = 2 * T * w.head_dim * (2 * w.n_head + 2 * w.n_kv_head)
+    a_ms = float(t_attn.mean())
+    tflops = att_flops / (a_ms * 1e-3) / 1e12
+
+    def kstat(t):
+        return {"mean_ms": float(t.mean()), "median_ms": float(np.median(t)),
+                "p10_ms": float(np.percentile(t, 10)), "p90_ms": float(np.percentile(t, 90))}
+
+    kernels = {
+        "prefill_attention": dict(kstat(t_attn), tflops=tflops, frac_bf16_peak=tflops / PEAK_BF16_TFLOPS,
+                                  flop=att_flops, algorithmic_bytes=attn_bytes),
+        "qkv_proj": dict(kstat(t_gemm), tflops=gemm_flops / (t_gemm.mean() * 1e-3) / 1e12,
+                         frac_bf16_peak=gemm_flops / (t_gemm.mean() * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                         flop=gemm_flops),
+        "kv_cache_write": dict(kstat(t_kv), algorithmic_bytes=kv_bytes,
+                               gbs_in_step=kv_bytes / (t_kv.mean() * 1e-3) / 1e9,
+                               cold_mean_ms=float(t_kv_cold.mean()),
+                               cold_median_ms=float(np.median(t_kv_cold)),
+                               gbs_cold=kv_bytes / (np.median(t_kv_cold) * 1e-3) / 1e9,
+                               frac_hbm_cold=kv_bytes / (np.median(t_kv_cold) * 1e-3) / 1e9 / PEAK_HBM_GBS),
+    }
+    traffic = measured_traffic(w.name)
+    roofline = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": tflops / PEAK_BF16_TFLOPS, "traffic": traffic, "kernel": "attn_fwd_kernel<128,2>",
+                "flop_per_launch": att_flops, "avg_launch_ms": a_ms}
+    out = {
+        "metric": METRIC,
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,1/h) weights, bf16)",
+        "config": {"workload": w.name, "seq_lens": list(w.seqlens) if w.num_seqs <= 16 else w.num_seqs,
+                   "total_tokens": T, "h": w.h, "n_head": w.n_head, "n_kv_head": w.n_kv_head,
+                   "head_dim": w.head_dim, "page_size": 16, "kv_cache": w.cache,
+                   "block_table": w.block_table},
+        "roofline": roofline,
+        "kernels": kernels,
+        "path_tflops": (att_flops + gemm_flops) / (ms_step * 1e-3) / 1e12,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

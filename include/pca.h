@@ -1,0 +1,179 @@
+/*
+ * pca.h -- C ABI of libpca, the prefill attention-unit path on MI355X (gfx950).
+ *
+ * The path is the prefill forward of one decoder layer's attention unit as the
+ * "Prefill decoder-layer attention data flow" article (hncyxsy.com/news/270449)
+ * lays it out: one fused QKV projection GEMM (§1.2, §2.1, §4.1), the head
+ * split by stride (§2.2), causal attention with online softmax and GQA head
+ * sharing (§2.3, §3.1-§3.4, §4.3), the heads flattened back to (s, h) (§3.3),
+ * and the write of K/V into a paged KV cache (§4.2; the paging follows
+ * "Prefill vs decode tuning notes" (hncyxsy.com/news/227904) §3.4, its fp8
+ * storage §3.3, and the 16-token block size of "Decoding LLM inference
+ * latency: prefill bottlenecks" (lnwmold.com/news/496245) §3.3).
+ *
+ * Conventions shared by every call:
+ *  - Pointers marked "device" are HIP device addresses; the caller allocates
+ *    and owns every buffer.  The library allocates nothing and keeps no state
+ *    besides a thread-local error message.
+ *  - Compute calls are asynchronous: they validate their arguments on the
+ *    host, enqueue kernels on `stream` (a hipStream_t; NULL = the null
+ *    stream) and return.  Validation happens before any enqueue, so a call
+ *    that returns an error has not touched device memory.
+ *  - bf16 values travel as their 16-bit storage pattern (pca_bf16).
+ *  - Device pointers must be 16-byte aligned; leading dimensions (row
+ *    strides, in elements) must be multiples of 8 and at least the row width.
+ *  - Errors: PCA_ERR_INVALID_ARG for a null or misaligned pointer, a size
+ *    out of range or an inconsistent shape; PCA_ERR_UNSUPPORTED for a
+ *    head_dim, page size or dtype the kernels are not built for;
+ *    PCA_ERR_HIP when the launch itself fails.  pca_last_error() describes
+ *    the last failure on the calling thread.
+ */
+#ifndef PCA_H
+#define PCA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t pca_bf16;
+
+typedef enum pca_status {
+    PCA_OK = 0,
+    PCA_ERR_INVALID_ARG = 1,
+    PCA_ERR_UNSUPPORTED = 2,
+    PCA_ERR_HIP = 3
+} pca_status;
+
+typedef enum pca_dtype {
+    PCA_DTYPE_BF16 = 0,      /* 2 bytes per element                              */
+    PCA_DTYPE_FP8_E4M3 = 1   /* OCP E4M3 (max 448, no inf), 1 byte per element   */
+} pca_dtype;
+
+/* Offsets and strides of the head split and of the page pools.  All strides
+ * and offsets are in elements; the *_bytes fields are bytes. */
+typedef struct pca_kv_layout_t {
+    int64_t qkv_ld;             /* row width of the fused projection output: (n_head + 2 n_kv) hd */
+    int64_t q_off;              /* first column of Q in that row: 0                                */
+    int64_t k_off;              /* first column of K: n_head * hd                                  */
+    int64_t v_off;              /* first column of V: (n_head + n_kv) * hd                         */
+    int64_t head_stride;        /* columns between consecutive heads: hd                           */
+    int64_t page_size;          /* token slots per page                                            */
+    int64_t pool_page_stride;   /* elements per page: page_size * n_kv * hd                        */
+    int64_t pool_slot_stride;   /* elements per slot: n_kv * hd                                    */
+    int64_t pool_head_stride;   /* elements per kv head within a slot: hd                          */
+    int64_t scale_page_stride;  /* fp8 only: scales per page, page_size * n_kv (else 0)            */
+    int64_t scale_slot_stride;  /* fp8 only: scales per slot, n_kv (else 0)                        */
+    int64_t elem_bytes;         /* 2 for bf16, 1 for fp8                                           */
+    int64_t kv_bytes_per_token_layer;    /* 2 * n_kv * hd * elem_bytes (K and V)                  */
+    int64_t scale_bytes_per_token_layer; /* fp8: 2 * n_kv * 4 (K and V scales), else 0            */
+    int64_t page_bytes;         /* bytes of one page of one pool                                   */
+} pca_kv_layout_t;
+
+/*
+ * pca_kv_layout -- pure host arithmetic, no device work.
+ *   Byte accounting follows the data-flow article §3.4 (K and V, per kv head,
+ *   per token: 16 KB for 32 kv heads and 4 KB for 8 at head_dim 128, 2-byte
+ *   elements) and the tuning notes §3.1 (2 x layers x heads x head_dim x
+ *   tokens x bytes).  The column offsets are the head split of the article's
+ *   §2.2: the fused row is [Q | K | V], each head a run of head_dim columns.
+ *   n_head % n_kv_head must be 0.  `out` is a host pointer owned by the
+ *   caller.  Returns PCA_ERR_INVALID_ARG for non-positive or inconsistent
+ *   sizes and on int64 overflow, PCA_ERR_UNSUPPORTED for an unknown dtype.
+ */
+pca_status pca_kv_layout(int n_head, int n_kv_head, int head_dim, int page_size,
+                         pca_dtype cache_dtype, pca_kv_layout_t* out);
+
+/*
+ * pca_qkv_proj -- y[M, N] = x[M, K] * w_t[N, K]^T, bf16 in, fp32
+ *   accumulation, one round-to-nearest-even to bf16 out.
+ *   This is the single fused QKV GEMM of the data-flow article (§2.1, §4.1):
+ *   the three projections in one (h, 3h) -- for GQA (h, (n_head+2 n_kv) hd)
+ *   -- weight, so the activation is read from HBM once.  The weight is passed
+ *   pre-transposed, (N, K) row-major, as the article's §5.1 advises doing
+ *   once at load time so the GEMM reads both operands along K.
+ *   x:   device, M rows of K elements, row stride ldx (>= K).
+ *   w_t: device, N rows of K elements, row stride ldw (>= K).
+ *   y:   device, M rows of N elements, row stride ldy (>= N); must not
+ *        overlap x or w_t.
+ *   M, N >= 1 (any value); K >= 8 and a multiple of 8.
+ */
+pca_status pca_qkv_proj(const pca_bf16* x, int64_t ldx, const pca_bf16* w_t, int64_t ldw,
+                        pca_bf16* y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                        void* stream);
+
+/*
+ * pca_prefill_attention -- causal GQA attention over packed sequences.
+ *   For sequence b, query head i (kv head g = i / (n_head / n_kv_head)) and
+ *   position r:  o[r, i] = sum_{c <= r} softmax_c(q[r, i] . k[c, g] * scale) v[c, g]
+ *   (data-flow article §2.3, §3.1, §3.2; GQA sharing §3.4).  The kernel is
+ *   the fused blockwise form (§3.2, §4.3): scores and probabilities live only
+ *   in registers, the softmax runs online per kv tile, and the causal mask is
+ *   control flow -- kv tiles after a query tile are never visited.
+ *   q, k, v: device, token-major rows; head h of token t starts at
+ *        q + t*ldq + h*head_dim (likewise k, v with kv heads).  They may be
+ *        strided views into one fused projection output (use the offsets
+ *        from pca_kv_layout).
+ *   cu_seqlens: device int32[num_seqs + 1], cu[0] = 0, non-decreasing,
+ *        cu[num_seqs] = total_tokens; sequence b is tokens [cu[b], cu[b+1]).
+ *        NULL means one sequence of total_tokens (num_seqs must be 1).
+ *        Entries are clamped to [0, total_tokens] on the device, so a bad
+ *        table cannot cause out-of-bounds access (it gives wrong output).
+ *   max_seqlen: >= the longest sequence; rows of longer sequences past
+ *        max_seqlen are not written.
+ *   head_dim: 32, 64 or 128 (else PCA_ERR_UNSUPPORTED).  causal must be 1.
+ *   o:   device, bf16, (total_tokens, n_head*head_dim) with row stride ldo;
+ *        head i of token t at o + t*ldo + i*head_dim (heads flattened back
+ *        to (s, h), §3.3).  Must not overlap q, k, v.
+ *   total_tokens == 0 (with num_seqs >= 1) is a no-op and accepts NULL buffers.
+ */
+pca_status pca_prefill_attention(const pca_bf16* q, const pca_bf16* k, const pca_bf16* v,
+                                 int64_t ldq, int64_t ldk, int64_t ldv,
+                                 const int32_t* cu_seqlens, int num_seqs, int max_seqlen,
+                                 int64_t total_tokens, int n_head, int n_kv_head, int head_dim,
+                                 float scale, int causal, pca_bf16* o, int64_t ldo,
+                                 void* stream);
+
+/*
+ * pca_kv_cache_write -- scatter each token's K and V into its page slot.
+ *   Token position p of sequence b goes to page block_table[b*max_pages_per_seq
+ *   + p / page_size], slot p % page_size (data-flow article §4.2,
+ *   "per-block contiguous"; tuning notes §3.4).  Pools are
+ *   [num_pages][page_size][n_kv_head][head_dim]; slots no token maps to are
+ *   left untouched.
+ *   k, v: device bf16, token-major rows (row strides ldk, ldv); kv head j of
+ *        token t at k + t*ldk + j*head_dim.
+ *   cu_seqlens: as for pca_prefill_attention (NULL = one sequence).
+ *   block_table: device int32[num_seqs][max_pages_per_seq].  Entries outside
+ *        [0, num_pages) and positions past max_pages_per_seq*page_size are
+ *        skipped on the device (never written out of bounds).
+ *   page_size: 16 (else PCA_ERR_UNSUPPORTED).  head_dim: 32, 64 or 128.
+ *   cache_dtype PCA_DTYPE_BF16: k_cache, v_cache are bf16 pools, a bit copy;
+ *        k_scale and v_scale must be NULL.
+ *   cache_dtype PCA_DTYPE_FP8_E4M3 (tuning notes §3.3): k_cache, v_cache are
+ *        uint8 pools of E4M3 codes and k_scale, v_scale are device fp32 pools
+ *        [num_pages][page_size][n_kv_head].  For each (token, kv head) row x
+ *        of K (and of V): amax = max|x|, scale = amax / 448,
+ *        code = E4M3_RNE_saturate(x * (448 / amax)), every step in binary32
+ *        round-to-nearest; amax == 0 gives scale 0 and codes of +-0.
+ *   total_tokens == 0 (with num_seqs >= 1) is a no-op and accepts NULL buffers.
+ */
+pca_status pca_kv_cache_write(const pca_bf16* k, const pca_bf16* v, int64_t ldk, int64_t ldv,
+                              const int32_t* cu_seqlens, int num_seqs, int64_t total_tokens,
+                              const int32_t* block_table, int max_pages_per_seq,
+                              int n_kv_head, int head_dim, int page_size, pca_dtype cache_dtype,
+                              void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                              int64_t num_pages, void* stream);
+
+/* Message for the last non-OK status returned on the calling thread ("" if none). */
+const char* pca_last_error(void);
+
+/* Library version string, e.g. "pca 0.1.0 gfx950". */
+const char* pca_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PCA_H */

@@ -1,0 +1,155 @@
+"""ctypes binding of libpca (argument marshalling only).
+
+Every step of the path runs in the HIP kernels of libpca.so; this module only
+turns torch tensors into device pointers, strides and the current HIP stream.
+There is no fallback: if the library is missing or fails to load, every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libpca.so")
+
+PCA_OK, PCA_ERR_INVALID_ARG, PCA_ERR_UNSUPPORTED, PCA_ERR_HIP = 0, 1, 2, 3
+DTYPES = {"bf16": 0, "fp8_e4m3": 1}
+
+EXPORTED = ("pca_kv_layout", "pca_qkv_proj", "pca_prefill_attention", "pca_kv_cache_write",
+            "pca_last_error", "pca_version")
+
+
+class PcaError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed (status {status}): {msg}")
+        self.status = status
+
+
+class KvLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "qkv_ld", "q_off", "k_off", "v_off", "head_stride", "page_size", "pool_page_stride",
+        "pool_slot_stride", "pool_head_stride", "scale_page_stride", "scale_slot_stride",
+        "elem_bytes", "kv_bytes_per_token_layer", "scale_bytes_per_token_layer", "page_bytes")]
+
+    def as_dict(self) -> dict:
+        return {n: int(getattr(self, n)) for n, _ in self._fields_}
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libpca.so (built in-tree by __graft_entry__.build()); raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise FileNotFoundError(f"{path} is not built: run __graft_entry__.build() (hipcc for gfx950)")
+    lib = ctypes.CDLL(path)
+    i64, i32, vp, f32 = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_float
+    lib.pca_kv_layout.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(KvLayout)]
+    lib.pca_qkv_proj.argtypes = [vp, i64, vp, i64, vp, i64, i64, i64, i64, vp]
+    lib.pca_prefill_attention.argtypes = [vp, vp, vp, i64, i64, i64, vp, i32, i32, i64, i32, i32, i32,
+                                          f32, i32, vp, i64, vp]
+    lib.pca_kv_cache_write.argtypes = [vp, vp, i64, i64, vp, i32, i64, vp, i32, i32, i32, i32, i32,
+                                       vp, vp, vp, vp, i64, vp]
+    for fn in ("pca_kv_layout", "pca_qkv_proj", "pca_prefill_attention", "pca_kv_cache_write"):
+        getattr(lib, fn).restype = ctypes.c_int
+    lib.pca_last_error.restype = ctypes.c_char_p
+    lib.pca_last_error.argtypes = []
+    lib.pca_version.restype = ctypes.c_char_p
+    lib.pca_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != PCA_OK:
+        raise PcaError(fn, status, load().pca_last_error().decode())
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return int(stream)
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _rows(t, name: str):
+    """(pointer, row stride) of a 2-D row-major view with unit column stride."""
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D view with unit column stride")
+    return t.data_ptr(), t.stride(0)
+
+
+def version() -> str:
+    return load().pca_version().decode()
+
+
+def kv_layout(n_head: int, n_kv_head: int, head_dim: int, page_size: int = 16,
+              cache_dtype: str = "bf16") -> dict:
+    out = KvLayout()
+    _check("pca_kv_layout", load().pca_kv_layout(n_head, n_kv_head, head_dim, page_size,
+                                                 DTYPES[cache_dtype], ctypes.byref(out)))
+    return out.as_dict()
+
+
+def qkv_proj(x, w_t, y, stream=None):
+    """y[M, N] = x[M, K] @ w_t[N, K]^T on the GPU (bf16 tensors, 2-D views)."""
+    px, ldx = _rows(x, "x")
+    pw, ldw = _rows(w_t, "w_t")
+    py, ldy = _rows(y, "y")
+    M, K = x.shape
+    N = w_t.shape[0]
+    if w_t.shape[1] != K or tuple(y.shape) != (M, N):
+        raise ValueError(f"shape mismatch: x {tuple(x.shape)}, w_t {tuple(w_t.shape)}, y {tuple(y.shape)}")
+    _check("pca_qkv_proj", load().pca_qkv_proj(px, ldx, pw, ldw, py, ldy, M, N, K, _stream(stream)))
+    return y
+
+
+def prefill_attention(q, k, v, o, n_head: int, n_kv_head: int, head_dim: int,
+                      cu_seqlens=None, max_seqlen: Optional[int] = None, scale: Optional[float] = None,
+                      total_tokens: Optional[int] = None, stream=None):
+    """Causal GQA attention.  q, k, v, o: 2-D token-major views (T, >= heads*hd)
+    with unit column stride (e.g. column slices of the fused projection output).
+    cu_seqlens: int32 device tensor [num_seqs + 1] or None (one sequence)."""
+    pq, ldq = _rows(q, "q")
+    pk, ldk = _rows(k, "k")
+    pv, ldv = _rows(v, "v")
+    po, ldo = _rows(o, "o")
+    T = q.shape[0] if total_tokens is None else int(total_tokens)
+    num_seqs = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
+    if max_seqlen is None:
+        max_seqlen = T
+    if scale is None:
+        scale = head_dim ** -0.5
+    _check("pca_prefill_attention", load().pca_prefill_attention(
+        pq, pk, pv, ldq, ldk, ldv, _ptr(cu_seqlens), num_seqs, int(max_seqlen), T,
+        n_head, n_kv_head, head_dim, float(scale), 1, po, ldo, _stream(stream)))
+    return o
+
+
+def kv_cache_write(k, v, block_table, k_cache, v_cache, n_kv_head: int, head_dim: int,
+                   cu_seqlens=None, cache_dtype: str = "bf16", k_scale=None, v_scale=None,
+                   page_size: int = 16, total_tokens: Optional[int] = None, stream=None):
+    """Scatter K/V rows into the page pools through the block table (int32 device
+    tensor [num_seqs, max_pages_per_seq]).  Pools are device tensors of
+    num_pages * page_size * n_kv_head * head_dim elements (bf16 or uint8)."""
+    pk, ldk = _rows(k, "k")
+    pv, ldv = _rows(v, "v")
+    T = k.shape[0] if total_tokens is None else int(total_tokens)
+    num_seqs = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be 2-D [num_seqs, max_pages_per_seq]")
+    elem = 2 if cache_dtype == "bf16" else 1
+    num_pages = k_cache.numel() * k_cache.element_size() // (page_size * n_kv_head * head_dim * elem)
+    _check("pca_kv_cache_write", load().pca_kv_cache_write(
+        pk, pv, ldk, ldv, _ptr(cu_seqlens), num_seqs, T, block_table.data_ptr(), block_table.shape[1],
+        n_kv_head, head_dim, page_size, DTYPES[cache_dtype], k_cache.data_ptr(), v_cache.data_ptr(),
+        _ptr(k_scale), _ptr(v_scale), num_pages, _stream(stream)))

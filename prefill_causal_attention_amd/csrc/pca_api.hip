@@ -1,0 +1,200 @@
+// C ABI of libpca: host-side validation, then kernel launch on the caller's stream.
+// Every check runs before any enqueue, so a call that fails leaves device
+// memory untouched.  See include/pca.h for the contract of each call.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "pca.h"
+#include "pca_internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+pca_status fail(pca_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+pca_status ok() {
+    g_err[0] = '\0';
+    return PCA_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool supported_head_dim(int hd) { return hd == 32 || hd == 64 || hd == 128; }
+
+constexpr int64_t kMaxBufferBytes = int64_t(1) << 31;   // buffer-resource offsets stay below 2^31
+
+pca_status hip_status(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(PCA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+// sizes of one packed-sequence batch: cu_seqlens may be null only for one sequence
+pca_status check_batch(const int32_t* cu, int num_seqs, int64_t total_tokens) {
+    if (num_seqs < 1) return fail(PCA_ERR_INVALID_ARG, "num_seqs must be >= 1 (got %d)", num_seqs);
+    if (cu == nullptr && num_seqs != 1)
+        return fail(PCA_ERR_INVALID_ARG, "cu_seqlens is NULL but num_seqs = %d (must be 1)", num_seqs);
+    if (total_tokens < 0) return fail(PCA_ERR_INVALID_ARG, "total_tokens must be >= 0");
+    if (cu != nullptr && ((uintptr_t)cu & 3u))
+        return fail(PCA_ERR_INVALID_ARG, "cu_seqlens must be 4-byte aligned");
+    return PCA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pca_last_error(void) { return g_err; }
+
+const char* pca_version(void) { return "pca 0.1.0 gfx950"; }
+
+pca_status pca_kv_layout(int n_head, int n_kv_head, int head_dim, int page_size,
+                         pca_dtype cache_dtype, pca_kv_layout_t* out) {
+    if (out == nullptr) return fail(PCA_ERR_INVALID_ARG, "out is NULL");
+    if (n_head <= 0 || n_kv_head <= 0 || head_dim <= 0 || page_size <= 0)
+        return fail(PCA_ERR_INVALID_ARG, "sizes must be positive (n_head=%d n_kv_head=%d head_dim=%d page_size=%d)",
+                    n_head, n_kv_head, head_dim, page_size);
+    if (n_head % n_kv_head != 0)
+        return fail(PCA_ERR_INVALID_ARG, "n_head (%d) must be a multiple of n_kv_head (%d)", n_head, n_kv_head);
+    int64_t eb;
+    if (cache_dtype == PCA_DTYPE_BF16) eb = 2;
+    else if (cache_dtype == PCA_DTYPE_FP8_E4M3) eb = 1;
+    else return fail(PCA_ERR_UNSUPPORTED, "unknown cache dtype %d", (int)cache_dtype);
+    const int64_t hd = head_dim, nq = n_head, nk = n_kv_head, ps = page_size;
+    // all products below stay far from int64 overflow for int inputs: (2^31)^3 < 2^94 is not,
+    // so bound the largest one explicitly
+    if ((nq + 2 * nk) > (int64_t(1) << 40) / hd || ps * nk > (int64_t(1) << 40) / hd)
+        return fail(PCA_ERR_INVALID_ARG, "layout sizes overflow");
+    memset(out, 0, sizeof(*out));
+    out->qkv_ld = (nq + 2 * nk) * hd;
+    out->q_off = 0;
+    out->k_off = nq * hd;
+    out->v_off = (nq + nk) * hd;
+    out->head_stride = hd;
+    out->page_size = ps;
+    out->pool_page_stride = ps * nk * hd;
+    out->pool_slot_stride = nk * hd;
+    out->pool_head_stride = hd;
+    out->scale_page_stride = eb == 1 ? ps * nk : 0;
+    out->scale_slot_stride = eb == 1 ? nk : 0;
+    out->elem_bytes = eb;
+    out->kv_bytes_per_token_layer = 2 * nk * hd * eb;
+    out->scale_bytes_per_token_layer = eb == 1 ? 2 * nk * 4 : 0;
+    out->page_bytes = ps * nk * hd * eb;
+    return ok();
+}
+
+pca_status pca_qkv_proj(const pca_bf16* x, int64_t ldx, const pca_bf16* w_t, int64_t ldw,
+                        pca_bf16* y, int64_t ldy, int64_t M, int64_t N, int64_t K, void* stream) {
+    if (!x || !w_t || !y) return fail(PCA_ERR_INVALID_ARG, "null pointer (x=%p w_t=%p y=%p)", x, w_t, y);
+    if (!aligned16(x) || !aligned16(w_t) || !aligned16(y))
+        return fail(PCA_ERR_INVALID_ARG, "x, w_t and y must be 16-byte aligned");
+    if (M < 1 || N < 1 || K < 8 || K % 8 != 0)
+        return fail(PCA_ERR_INVALID_ARG, "need M >= 1, N >= 1, K >= 8 and K %% 8 == 0 (M=%lld N=%lld K=%lld)",
+                    (long long)M, (long long)N, (long long)K);
+    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX)
+        return fail(PCA_ERR_INVALID_ARG, "M, N, K must fit in int32");
+    if (ldx < K || ldw < K || ldy < N || ldx % 8 || ldw % 8 || ldy % 8)
+        return fail(PCA_ERR_INVALID_ARG, "leading dimensions must be >= the row width and multiples of 8 "
+                    "(ldx=%lld ldw=%lld ldy=%lld)", (long long)ldx, (long long)ldw, (long long)ldy);
+    if (256 * ldx * 2 >= kMaxBufferBytes || 256 * ldw * 2 >= kMaxBufferBytes)
+        return fail(PCA_ERR_UNSUPPORTED, "row stride too large for a 256-row tile view");
+    pca::GemmArgs a;
+    a.x = x; a.ldx = ldx; a.w = w_t; a.ldw = ldw; a.y = y; a.ldy = ldy;
+    a.M = (int)M; a.N = (int)N; a.K = (int)K;
+    return hip_status(pca::launch_qkv_gemm(a, (hipStream_t)stream), "qkv_proj launch");
+}
+
+pca_status pca_prefill_attention(const pca_bf16* q, const pca_bf16* k, const pca_bf16* v,
+                                 int64_t ldq, int64_t ldk, int64_t ldv,
+                                 const int32_t* cu_seqlens, int num_seqs, int max_seqlen,
+                                 int64_t total_tokens, int n_head, int n_kv_head, int head_dim,
+                                 float scale, int causal, pca_bf16* o, int64_t ldo, void* stream) {
+    if (total_tokens == 0 && num_seqs >= 1 && causal == 1) return ok();   // empty batch: nothing to read or write
+    if (!q || !k || !v || !o) return fail(PCA_ERR_INVALID_ARG, "null q, k, v or o");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+        return fail(PCA_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
+    if (causal != 1) return fail(PCA_ERR_INVALID_ARG, "only causal attention (causal = 1) is provided");
+    if (n_head <= 0 || n_kv_head <= 0 || n_head % n_kv_head != 0)
+        return fail(PCA_ERR_INVALID_ARG, "need n_head, n_kv_head > 0 and n_head %% n_kv_head == 0 (%d, %d)",
+                    n_head, n_kv_head);
+    if (!supported_head_dim(head_dim))
+        return fail(PCA_ERR_UNSUPPORTED, "head_dim %d not supported (32, 64 or 128)", head_dim);
+    pca_status st = check_batch(cu_seqlens, num_seqs, total_tokens);
+    if (st != PCA_OK) return st;
+    if (!(scale > 0.0f) || scale != scale || scale > 1e30f) return fail(PCA_ERR_INVALID_ARG, "scale must be finite and > 0");
+    if (ldq < (int64_t)n_head * head_dim || ldk < (int64_t)n_kv_head * head_dim ||
+        ldv < (int64_t)n_kv_head * head_dim || ldo < (int64_t)n_head * head_dim ||
+        ldq % 8 || ldk % 8 || ldv % 8 || ldo % 8)
+        return fail(PCA_ERR_INVALID_ARG, "row strides must cover the heads and be multiples of 8 "
+                    "(ldq=%lld ldk=%lld ldv=%lld ldo=%lld)", (long long)ldq, (long long)ldk, (long long)ldv, (long long)ldo);
+    if (total_tokens == 0) return ok();
+    if (max_seqlen < 1 || (cu_seqlens == nullptr && max_seqlen < total_tokens))
+        return fail(PCA_ERR_INVALID_ARG, "max_seqlen must be >= 1 and cover the sequence (got %d)", max_seqlen);
+    // each sequence is read through its own buffer view, which must stay below 2 GiB
+    const int64_t longest = cu_seqlens ? (max_seqlen < total_tokens ? max_seqlen : total_tokens) : total_tokens;
+    if (longest * ldq * 2 >= kMaxBufferBytes || longest * ldk * 2 >= kMaxBufferBytes ||
+        longest * ldv * 2 >= kMaxBufferBytes)
+        return fail(PCA_ERR_UNSUPPORTED, "per-sequence q/k/v views beyond 2 GiB are not supported");
+    pca::AttnArgs a;
+    a.q = q; a.k = k; a.v = v; a.ldq = ldq; a.ldk = ldk; a.ldv = ldv;
+    a.cu_seqlens = cu_seqlens; a.num_seqs = num_seqs; a.max_seqlen = max_seqlen;
+    a.total_tokens = total_tokens; a.n_head = n_head; a.n_kv_head = n_kv_head; a.head_dim = head_dim;
+    a.scale = scale; a.o = o; a.ldo = ldo;
+    return hip_status(pca::launch_attention(a, (hipStream_t)stream), "prefill_attention launch");
+}
+
+pca_status pca_kv_cache_write(const pca_bf16* k, const pca_bf16* v, int64_t ldk, int64_t ldv,
+                              const int32_t* cu_seqlens, int num_seqs, int64_t total_tokens,
+                              const int32_t* block_table, int max_pages_per_seq,
+                              int n_kv_head, int head_dim, int page_size, pca_dtype cache_dtype,
+                              void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                              int64_t num_pages, void* stream) {
+    if (total_tokens == 0 && num_seqs >= 1) return ok();   // empty batch: nothing to read or write
+    if (!k || !v || !block_table || !k_cache || !v_cache)
+        return fail(PCA_ERR_INVALID_ARG, "null k, v, block_table, k_cache or v_cache");
+    if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
+        return fail(PCA_ERR_INVALID_ARG, "k, v, k_cache and v_cache must be 16-byte aligned");
+    if ((uintptr_t)block_table & 3u) return fail(PCA_ERR_INVALID_ARG, "block_table must be 4-byte aligned");
+    if (n_kv_head <= 0) return fail(PCA_ERR_INVALID_ARG, "n_kv_head must be > 0");
+    if (!supported_head_dim(head_dim))
+        return fail(PCA_ERR_UNSUPPORTED, "head_dim %d not supported (32, 64 or 128)", head_dim);
+    if (page_size != 16) return fail(PCA_ERR_UNSUPPORTED, "page_size must be 16 (got %d)", page_size);
+    pca_status st = check_batch(cu_seqlens, num_seqs, total_tokens);
+    if (st != PCA_OK) return st;
+    if (max_pages_per_seq < 1 || num_pages < 1)
+        return fail(PCA_ERR_INVALID_ARG, "max_pages_per_seq and num_pages must be >= 1");
+    if (ldk < (int64_t)n_kv_head * head_dim || ldv < (int64_t)n_kv_head * head_dim || ldk % 8 || ldv % 8)
+        return fail(PCA_ERR_INVALID_ARG, "ldk/ldv must cover n_kv_head*head_dim and be multiples of 8");
+    if (cache_dtype == PCA_DTYPE_BF16) {
+        if (k_scale || v_scale) return fail(PCA_ERR_INVALID_ARG, "k_scale/v_scale must be NULL for a bf16 cache");
+    } else if (cache_dtype == PCA_DTYPE_FP8_E4M3) {
+        if (!k_scale || !v_scale) return fail(PCA_ERR_INVALID_ARG, "fp8 cache needs k_scale and v_scale");
+        if (((uintptr_t)k_scale & 3u) || ((uintptr_t)v_scale & 3u))
+            return fail(PCA_ERR_INVALID_ARG, "k_scale/v_scale must be 4-byte aligned");
+    } else {
+        return fail(PCA_ERR_UNSUPPORTED, "unknown cache dtype %d", (int)cache_dtype);
+    }
+    if (total_tokens * 2 * ((int64_t)n_kv_head * head_dim / 8) >= (int64_t(1) << 31))
+        return fail(PCA_ERR_UNSUPPORTED, "batch too large (total_tokens * n_kv_head * head_dim)");
+    if (total_tokens == 0) return ok();
+    pca::KvWriteArgs a;
+    a.k = k; a.v = v; a.ldk = ldk; a.ldv = ldv;
+    a.cu_seqlens = cu_seqlens; a.num_seqs = num_seqs; a.total_tokens = total_tokens;
+    a.block_table = block_table; a.max_pages_per_seq = max_pages_per_seq;
+    a.n_kv_head = n_kv_head; a.head_dim = head_dim; a.page_size = page_size;
+    a.k_cache = k_cache; a.v_cache = v_cache; a.k_scale = k_scale; a.v_scale = v_scale;
+    a.num_pages = num_pages;
+    hipError_t e = cache_dtype == PCA_DTYPE_BF16 ? pca::launch_kv_write_bf16(a, (hipStream_t)stream)
+                                                 : pca::launch_kv_write_fp8(a, (hipStream_t)stream);
+    return hip_status(e, "kv_cache_write launch");
+}
+
+}  // extern "C"

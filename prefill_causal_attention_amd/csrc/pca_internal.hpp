@@ -1,0 +1,59 @@
+// Internal launch entry points of libpca (host side).  Arguments have been
+// validated by the C ABI layer (pca_api.hip) before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pca {
+
+struct KvWriteArgs {
+    const uint16_t* k;
+    const uint16_t* v;
+    int64_t ldk, ldv;
+    const int32_t* cu_seqlens;   // may be null: one sequence
+    int num_seqs;
+    int64_t total_tokens;
+    const int32_t* block_table;
+    int max_pages_per_seq;
+    int n_kv_head, head_dim, page_size;
+    void* k_cache;
+    void* v_cache;
+    float* k_scale;
+    float* v_scale;
+    int64_t num_pages;
+};
+
+hipError_t launch_kv_write_bf16(const KvWriteArgs& a, hipStream_t s);
+hipError_t launch_kv_write_fp8(const KvWriteArgs& a, hipStream_t s);
+
+struct GemmArgs {
+    const uint16_t* x;
+    int64_t ldx;
+    const uint16_t* w;   // (N, K) row-major
+    int64_t ldw;
+    uint16_t* y;
+    int64_t ldy;
+    int M, N, K;
+};
+
+hipError_t launch_qkv_gemm(const GemmArgs& a, hipStream_t s);
+
+struct AttnArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    int64_t ldq, ldk, ldv;
+    const int32_t* cu_seqlens;   // may be null: one sequence
+    int num_seqs;
+    int max_seqlen;
+    int64_t total_tokens;
+    int n_head, n_kv_head, head_dim;
+    float scale;
+    uint16_t* o;
+    int64_t ldo;
+};
+
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+
+}  // namespace pca

@@ -1,0 +1,80 @@
+"""GPU parity of pca_qkv_proj against the fp64 oracle projection."""
+import numpy as np
+import pytest
+import torch
+
+import prefill_causal_attention_amd as pca
+import workloads
+from oracle import bf16 as obf16
+from oracle import projection as P
+
+from _gpu_helpers import assert_close, bits, dev, require_gpu, sample_rows, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_proj(x, wq, y_pad=0):
+    """x (M, K) bf16, wq (K, N) bf16 as drawn; the weight is transposed once
+    (untimed, a storage choice) before the call."""
+    M, K = x.shape
+    N = wq.shape[1]
+    dx = dev(x)
+    dwt = dev(wq.t().contiguous())
+    y = torch.full((M, N + y_pad), float("nan"), dtype=torch.bfloat16, device="cuda")
+    pca.qkv_proj(dx, dwt, y[:, :N])
+    torch.cuda.synchronize()
+    return y
+
+
+def test_integer_inputs_exact():
+    """|x|, |w| <= 4 integers and K = 4096: every fp32 partial sum is an exact
+    integer below 2^24, so y must equal RNE_bf16(exact product) bitwise."""
+    require_gpu()
+    rng = np.random.default_rng(51)
+    M, K, N = 300, 4096, 520
+    xi = rng.integers(-4, 5, (M, K))
+    wi = rng.integers(-4, 5, (K, N))
+    x = torch.from_numpy(xi.astype(np.float32)).to(torch.bfloat16)
+    wq = torch.from_numpy(wi.astype(np.float32)).to(torch.bfloat16)
+    say(f"qkv_proj integer pin M={M} N={N} K={K}")
+    y = _gpu_proj(x, wq)
+    exact = xi.astype(np.int64) @ wi.astype(np.int64)
+    want = obf16.from_f64(exact.astype(np.float64))
+    got = bits(y)
+    assert np.array_equal(got, want), f"{np.sum(got != want)} mismatches"
+
+
+def test_one_hot_columns_copy_x():
+    require_gpu()
+    rng = np.random.default_rng(52)
+    M, K, N = 257, 520, 72
+    x = workloads.normal_bf16(53, (M, K))
+    picks = rng.integers(0, K, N)
+    w = np.zeros((K, N), dtype=np.float32)
+    w[picks, np.arange(N)] = 1.0
+    y = _gpu_proj(x, torch.from_numpy(w).to(torch.bfloat16))
+    assert np.array_equal(bits(y), bits(x)[:, picks])
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 8, 8), (100, 200, 64), (257, 384, 4096), (513, 1000, 1032), (2048, 6144, 4096)])
+def test_normal_inputs_tolerance(M, N, K):
+    require_gpu()
+    x = workloads.normal_bf16(54, (M, K))
+    wq = workloads.normal_bf16(55, (K, N), std=float(1 / np.sqrt(K)))
+    say(f"qkv_proj N(0,1) M={M} N={N} K={K}")
+    y = _gpu_proj(x, wq, y_pad=8)
+    want = P.qkv_projection(bits(x), bits(wq))
+    assert_close(y[:, :N].float().cpu().numpy(), want, f"gemm {M}x{N}x{K}")
+    assert torch.isnan(y[:, N:].float()).all(), "wrote past N"
+
+
+@pytest.mark.parametrize("idx", [2, 3, 4, 5])
+def test_full_size_sampled(idx):
+    require_gpu()
+    w = workloads.WORKLOADS[idx - 1]
+    x, wq = workloads.projection_inputs(w)
+    say(f"qkv_proj {w.name} M={w.total_tokens} N={w.n_qkv} K={w.h} seeds={w.seed(1)},{w.seed(2)}")
+    y = _gpu_proj(x, wq)
+    rows = sample_rows(w.total_tokens, 64, 200 + idx, must=(0, 255, 256, w.total_tokens - 1))
+    want = P.projection_rows(bits(x), bits(wq), rows)
+    assert_close(y[rows].float().cpu().numpy(), want, f"{w.name} projection rows")
