@@ -11,7 +11,7 @@
 // (§3.3).  Scores never leave registers.
 //
 // gfx950 mapping.
-//  * A wave owns 32*NQB query rows of one head; a workgroup is 4 waves that
+//  * A wave owns 32*NQB query rows of one head (NQB = 1 for every head_dim); a workgroup is 4 waves that
 //    share one kv head and the same kv tiles, loaded once into LDS per
 //    workgroup: for G >= 4 the 4 waves are 4 query heads at the same
 //    positions, for smaller G consecutive query blocks.
@@ -29,7 +29,11 @@
 //    tiles transposed, both double-buffered: tile j+1 is fetched into
 //    registers while tile j is on the matrix cores.
 //  * exp is exp2 with scale*log2(e) folded into one FMA; m, l, P in fp32,
-//    P rounded to bf16 only as the MFMA operand.
+//    P rounded to bf16 only as the MFMA operand.  The reference max of a row
+//    moves only when the row's scores exceed it by 2^8 (see below), so the
+//    rescale of the O accumulators is nearly always skipped.
+//  * One wave per 32 query rows and two waves per SIMD (221 VGPRs): the
+//    softmax of one wave overlaps the matrix-core work of the other.
 //  * The causal rule: a wave skips kv tiles that start after its last query,
 //    and masks per element only on tiles that reach past its first query.
 //    Workgroups are ordered heaviest-first and all workgroups of one
@@ -45,6 +49,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int BK = 64;   // keys per kv tile
+constexpr float kRescaleLog2 = 8.0f;   // lazy max update threshold (p stays <= 256)
 
 template <int HD, int NQB>
 struct Cfg {
@@ -78,7 +83,7 @@ struct Params {
 };
 
 template <int HD, int NQB>
-__global__ __launch_bounds__(kThreads)
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3 - NQB, 3 - NQB)))
 void attn_fwd_kernel(Params p) {
     using C = Cfg<HD, NQB>;
     extern __shared__ __align__(16) uint16_t smem[];
@@ -244,7 +249,12 @@ void attn_fwd_kernel(Params p) {
                             if (key > qry) s[kb][qb][e] = -__builtin_inff();
                         }
             }
-            // online softmax (one query per lane; its 32 keys split with lane ^ 32)
+            // online softmax (one query per lane; its 32 keys split with lane ^ 32).
+            // The running max is only moved when a row's tile max exceeds it by
+            // more than kRescaleLog2 (in log2 units): the result is the same for
+            // any reference value (it cancels in O / l), and the skipped moves keep
+            // p <= 2^kRescaleLog2.  So the rescale of O -- the only VALU work on
+            // the accumulators -- runs on the first tile and then only rarely.
             bf16x8_t pb[NQB][2][2];
 #pragma unroll
             for (int qb = 0; qb < NQB; ++qb) {
@@ -254,10 +264,20 @@ void attn_fwd_kernel(Params p) {
 #pragma unroll
                     for (int e = 0; e < 16; ++e) mx = __builtin_fmaxf(mx, s[kb][qb][e]);
                 mx = __builtin_fmaxf(mx, swap_halves(mx));
-                const float m_new = __builtin_fmaxf(m_run[qb], mx);
-                const float alpha = fast_exp2((m_run[qb] - m_new) * c);
-                m_run[qb] = m_new;
-                const float mc = m_new * c;
+                const bool move = (mx - m_run[qb]) * c > kRescaleLog2;
+                if (__builtin_amdgcn_ballot_w64(move) != 0) {
+                    // only rows past the threshold move, so every row's arithmetic
+                    // depends on its own scores alone (alpha = 1 is exact elsewhere)
+                    const float m_new = move ? mx : m_run[qb];
+                    const float alpha = move ? fast_exp2((m_run[qb] - m_new) * c) : 1.0f;
+                    m_run[qb] = m_new;
+                    l_run[qb] *= alpha;
+#pragma unroll
+                    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) oacc[qb][db][e] *= alpha;
+                }
+                const float mc = m_run[qb] * c;
                 float rs = 0.0f;
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
@@ -267,11 +287,7 @@ void attn_fwd_kernel(Params p) {
                         s[kb][qb][e] = pe;
                         rs += pe;
                     }
-                l_run[qb] = l_run[qb] * alpha + rs;
-#pragma unroll
-                for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) oacc[qb][db][e] *= alpha;
+                l_run[qb] += rs;
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -352,8 +368,8 @@ hipError_t launch_cfg(const AttnArgs& a, hipStream_t s) {
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     switch (a.head_dim) {
         case 32: return launch_cfg<32, 1>(a, s);
-        case 64: return launch_cfg<64, 2>(a, s);
-        case 128: return launch_cfg<128, 2>(a, s);
+        case 64: return launch_cfg<64, 1>(a, s);
+        case 128: return launch_cfg<128, 1>(a, s);
         default: return hipErrorInvalidValue;
     }
 }
