@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU oracle sample time")
     ap.add_argument("--kv-cold-reps", type=int, default=20)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (to scale HBM byte counters)")
     return ap.parse_args()
 
 
@@ -112,6 +114,14 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     pca.load()
+    if args.copy_calibration:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": 1 << 30, "copy_bytes_written": 1 << 30, "reps": 5}), flush=True)
+        return
     w = workloads.BY_NAME[args.workload]
     dev = torch.device("cuda:0")
     T, nk = w.total_tokens, w.n_kv_head * w.head_dim
@@ -212,7 +222,7 @@ def main():
     }
     traffic = measured_traffic(w.name)
     roofline = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": tflops / PEAK_BF16_TFLOPS, "traffic": traffic, "kernel": "attn_fwd_kernel<128,2>",
+                "frac": tflops / PEAK_BF16_TFLOPS, "traffic": traffic, "kernel": f"attn_fwd_kernel<{w.head_dim},1>",
                 "flop_per_launch": att_flops, "avg_launch_ms": a_ms}
     out = {
         "metric": METRIC,

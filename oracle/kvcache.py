@@ -47,8 +47,9 @@ def layout(n_head: int, n_kv_head: int, head_dim: int, page_size: int, elem_byte
         "pool_page_stride": page_size * n_kv_head * head_dim,
         "pool_slot_stride": n_kv_head * head_dim,
         "pool_head_stride": head_dim,
-        "scale_page_stride": page_size * n_kv_head,
-        "scale_slot_stride": n_kv_head,
+        # scale pools exist only for the 1-byte (fp8) cache
+        "scale_page_stride": page_size * n_kv_head if elem_bytes == 1 else 0,
+        "scale_slot_stride": n_kv_head if elem_bytes == 1 else 0,
         "kv_bytes_per_token_layer": 2 * n_kv_head * head_dim * elem_bytes,
         "scale_bytes_per_token_layer": (2 * n_kv_head * 4) if elem_bytes == 1 else 0,
         "page_bytes": page_size * n_kv_head * head_dim * elem_bytes,

@@ -11,29 +11,33 @@
 // (§3.3).  Scores never leave registers.
 //
 // gfx950 mapping.
-//  * A wave owns 32*NQB query rows of one head (NQB = 1 for every head_dim); a workgroup is 4 waves that
-//    share one kv head and the same kv tiles, loaded once into LDS per
-//    workgroup: for G >= 4 the 4 waves are 4 query heads at the same
-//    positions, for smaller G consecutive query blocks.
+//  * A wave owns 32 query rows of one head; a workgroup is 4 waves (one per
+//    SIMD) that share one kv head and therefore the kv tiles in LDS: for
+//    G >= 4 the 4 waves are 4 query heads at the same positions, for smaller
+//    G consecutive query blocks.  Two workgroups per CU (2 waves per SIMD):
+//    the softmax of one wave overlaps the matrix-core work of the other.
 //  * Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16: the 32x32 accumulator then holds, in each
 //    lane, 16 keys of ONE query (the lane's column).  Row max and row sum are
 //    lane-local plus one exchange with lane ^ 32, and the accumulator is
 //    already the B operand of the second product O^T = V^T P^T once
-//    converted to bf16 -- no cross-lane shuffle of P.  The contraction index
-//    of that product pairs (lane half, element) in both operands, so V^T is
-//    laid out in LDS with the same key order the accumulator has (within
-//    each 16 keys: 0-3, 8-11 | 4-7, 12-15).
+//    converted to bf16 -- no cross-lane shuffle of P.
+//  * K and V tiles (64 keys) go from HBM/L2 straight into LDS with
+//    buffer_load ... lds (no register staging), double-buffered: tile j+1 is
+//    in flight while tile j is on the matrix cores.  Both are stored
+//    row-major (key rows of head_dim) with the 16-byte chunks of each row
+//    XOR-swizzled by the row index, so that the K operand reads (ds_read_b128,
+//    16 rows per 16 lanes) and the V operand reads hit all 64 banks once.
+//    V^T comes out of LDS with the gfx950 transpose read ds_read_b64_tr_b16:
+//    each 16-lane group returns, for 16 consecutive d, 4 keys per lane -- the
+//    A-operand layout of O^T = V^T P^T, in the same key order the S^T
+//    accumulator hands to the B operand (within 16 keys: 0-3, 8-11 | 4-7, 12-15).
 //  * Q stays in registers (B operand of S^T) for the whole kv loop; the O^T
-//    accumulator (fp32) likewise; K tiles are stored row-major in LDS and V
-//    tiles transposed, both double-buffered: tile j+1 is fetched into
-//    registers while tile j is on the matrix cores.
+//    accumulator (fp32) likewise.
 //  * exp is exp2 with scale*log2(e) folded into one FMA; m, l, P in fp32,
 //    P rounded to bf16 only as the MFMA operand.  The reference max of a row
 //    moves only when the row's scores exceed it by 2^8 (see below), so the
 //    rescale of the O accumulators is nearly always skipped.
-//  * One wave per 32 query rows and two waves per SIMD (221 VGPRs): the
-//    softmax of one wave overlaps the matrix-core work of the other.
 //  * The causal rule: a wave skips kv tiles that start after its last query,
 //    and masks per element only on tiles that reach past its first query.
 //    Workgroups are ordered heaviest-first and all workgroups of one
@@ -46,25 +50,39 @@ namespace pca {
 
 namespace {
 
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
+
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
-constexpr int BK = 64;   // keys per kv tile
-constexpr float kRescaleLog2 = 8.0f;   // lazy max update threshold (p stays <= 256)
+constexpr int BQ = 32;                  // query rows per wave
+constexpr int BK = 64;                  // keys per kv tile
+constexpr float kRescaleLog2 = 8.0f;    // lazy max update threshold (p stays <= 256)
+constexpr int kVmcnt0 = 0x0F70;         // s_waitcnt vmcnt(0), other counters unconstrained
 
-template <int HD, int NQB>
+template <int HD>
 struct Cfg {
-    static constexpr int BQW = 32 * NQB;          // query rows per wave
-    static constexpr int KROW = HD + 8;           // K tile row stride (elements), 16-byte pad
-    static constexpr int VROW = BK + 8;           // V^T tile row stride (elements), 16-byte pad
-    static constexpr int K_ELEMS = BK * KROW;
-    static constexpr int V_ELEMS = HD * VROW;
-    static constexpr int STAGE = K_ELEMS + V_ELEMS;
-    static constexpr int LDS_BYTES = 2 * STAGE * 2;
-    static constexpr int DCH = HD / 16;            // k16 steps over head_dim
-    static constexpr int DB = HD / 32;             // 32-row blocks of O^T
-    static constexpr int K_LOADS = BK * HD / 8 / kThreads;     // 16-byte chunks per thread
-    static constexpr int V_BLOCKS = (BK / 8) * (HD / 4);       // 8-key x 4-d blocks per tile
+    static constexpr int NC = HD / 8;                    // 16-byte chunks per key row
+    static constexpr int ROWB = HD * 2;                  // bytes per key row
+    static constexpr int TILE = BK * ROWB;               // bytes of the K (or V) tile
+    static constexpr int STAGE = 2 * TILE;               // K tile then V tile
+    static constexpr int LDS_BYTES = 2 * STAGE;          // two stages
+    static constexpr int RPI = 1024 / ROWB;              // rows per 1 KiB wave DMA instruction
+    static constexpr int DMA_PER_WAVE = TILE / 1024 / kWaves;
+    static constexpr int DCH = HD / 16;                  // k16 steps over head_dim
+    static constexpr int DB = HD / 32;                   // 32-row blocks of O^T
+    static_assert(DMA_PER_WAVE >= 1, "tile too small for the DMA split");
 };
+
+// Physical 16-byte chunk of logical chunk c in key row r is c ^ swz(r): the
+// keys of 16 consecutive rows are all distinct (K reads), and so are the
+// physical chunks of 4 consecutive rows x 4 consecutive chunks (V transpose
+// reads), for head_dim 128.
+template <int HD>
+__device__ inline int swz(int r) { return ((r & 3) * 4 + ((r >> 2) & 3)) & (Cfg<HD>::NC - 1); }
 
 struct Params {
     const uint16_t* q;
@@ -82,14 +100,33 @@ struct Params {
     int units;          // num_seqs * n_kv
 };
 
-template <int HD, int NQB>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3 - NQB, 3 - NQB)))
+// Issue the DMA of one kv tile (keys [kbase, kbase + BK)) into one LDS stage:
+// buffer views that start at the tile, so keys at or past the sequence end read 0.
+template <int HD>
+__device__ __forceinline__ void dma_tile(const Params& p, int64_t s0, int Lb, int g, int wave, int kbase,
+                                         lds_char_t* base, const uint32_t* dma_k, const uint32_t* dma_v) {
+    using C = Cfg<HD>;
+    const __amdgpu_buffer_rsrc_t rk =
+        make_rsrc(p.k + (s0 + kbase) * p.ldk, (uint32_t)((int64_t)(Lb - kbase) * p.ldk * 2));
+    const __amdgpu_buffer_rsrc_t rv =
+        make_rsrc(p.v + (s0 + kbase) * p.ldv, (uint32_t)((int64_t)(Lb - kbase) * p.ldv * 2));
+#pragma unroll
+    for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
+        const int blk = wave * C::DMA_PER_WAVE + i;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(base + blk * 1024), 16, dma_k[i], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(base + C::TILE + blk * 1024), 16, dma_v[i], 0, 0, 0);
+    }
+}
+
+template <int HD>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(Params p) {
-    using C = Cfg<HD, NQB>;
+    using C = Cfg<HD>;
     extern __shared__ __align__(16) uint16_t smem[];
+    lds_char_t* lds = (lds_char_t*)smem;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r32 = lane & 31, half = lane >> 5;
 
     // ---- workgroup -> (unit = (sequence, kv head), task group), heaviest first
@@ -115,7 +152,7 @@ void attn_fwd_kernel(Params p) {
     }
     const int Lb = (int)(s1 - s0);
     const int G = p.group;
-    const int nqb = (Lb + C::BQW - 1) / C::BQW;
+    const int nqb = (Lb + BQ - 1) / BQ;
     const int ntasks = G * nqb;
     const int ntg_b = (ntasks + kWaves - 1) / kWaves;
     const int tg = p.ntg - 1 - rank;
@@ -125,222 +162,195 @@ void attn_fwd_kernel(Params p) {
     const bool active = task < ntasks;
     const int qblk = active ? task / G : 0;
     const int head = g * G + (active ? task % G : 0);
-    const int q0 = qblk * C::BQW;                              // first query row (in sequence)
+    const int q0 = qblk * BQ;                                  // first query row (in sequence)
     const int last_task = min(tg * kWaves + kWaves - 1, ntasks - 1);
-    const int kv_end = min(Lb, (last_task / G + 1) * C::BQW);
+    const int kv_end = min(Lb, (last_task / G + 1) * BQ);
     const int ntiles = (kv_end + BK - 1) / BK;
-    const int wave_last_q = min(q0 + C::BQW, Lb) - 1;
+    const int wave_last_q = min(q0 + BQ, Lb) - 1;
     const int wave_ntiles = active ? wave_last_q / BK + 1 : 0;
 
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + s0 * p.ldq, (uint32_t)((int64_t)Lb * p.ldq * 2));
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + s0 * p.ldk, (uint32_t)((int64_t)Lb * p.ldk * 2));
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + s0 * p.ldv, (uint32_t)((int64_t)Lb * p.ldv * 2));
-
     // ---- Q tile in registers: B operand of S^T = K Q^T (column = query r32)
-    bf16x8_t qreg[NQB][C::DCH];
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb)
+    bf16x8_t qreg[C::DCH];
+    {
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + s0 * p.ldq, (uint32_t)((int64_t)Lb * p.ldq * 2));
 #pragma unroll
         for (int dc = 0; dc < C::DCH; ++dc) {
-            const uint32_t off = (uint32_t)(((int64_t)(q0 + qb * 32 + r32) * p.ldq + head * HD + dc * 16 + half * 8) * 2);
-            qreg[qb][dc] = as_bf16x8(buf_load16(rq, off));
+            const uint32_t off = (uint32_t)(((int64_t)(q0 + r32) * p.ldq + head * HD + dc * 16 + half * 8) * 2);
+            qreg[dc] = as_bf16x8(buf_load16(rq, off));
         }
+    }
 
-    // ---- K/V tile staging (all 256 threads)
-    u32x4_t kst[C::K_LOADS];
-    u32x2_t vst[8];
-    const int v_kg = tid / (HD / 4), v_dq = tid % (HD / 4);   // V block: 8 keys x 4 d
-    const int v_key0 = (v_kg >> 1) * 16 + (v_kg & 1) * 4;
-    const bool v_loader = tid < C::V_BLOCKS;
-    auto global_load = [&](int kbase) {
+    // ---- DMA of one kv tile: wave w fills the 1 KiB blocks [w*DMA_PER_WAVE, ...) of the
+    // K and V tiles.  Lane l writes bytes [16 l, 16 l + 16) of a block: row l / NC,
+    // physical chunk l % NC, so it fetches the logical chunk the swizzle puts there.
+    uint32_t dma_k[C::DMA_PER_WAVE], dma_v[C::DMA_PER_WAVE];
 #pragma unroll
-        for (int i = 0; i < C::K_LOADS; ++i) {
-            const int id = i * kThreads + tid;
-            const int key = id / (HD / 8), ch = id % (HD / 8);
-            const uint32_t off = (uint32_t)(((int64_t)(kbase + key) * p.ldk + g * HD + ch * 8) * 2);
-            kst[i] = buf_load16(rk, off);
-        }
-        if (v_loader) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int key = kbase + v_key0 + (j & 3) + (j >> 2) * 8;
-                const uint32_t off = (uint32_t)(((int64_t)key * p.ldv + g * HD + v_dq * 4) * 2);
-                vst[j] = buf_load8(rv, off);
-            }
-        }
-    };
-    auto lds_store = [&](int st) {
-        uint16_t* ks = smem + st * C::STAGE;
-        uint16_t* vt = ks + C::K_ELEMS;
-#pragma unroll
-        for (int i = 0; i < C::K_LOADS; ++i) {
-            const int id = i * kThreads + tid;
-            const int key = id / (HD / 8), ch = id % (HD / 8);
-            *reinterpret_cast<u32x4_t*>(ks + key * C::KROW + ch * 8) = kst[i];
-        }
-        if (v_loader) {
-            // transpose 8 keys x 4 d into 4 rows (d) of 8 keys each
-#pragma unroll
-            for (int dd = 0; dd < 4; ++dd) {
-                u32x4_t w;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint32_t a0 = vst[2 * j][dd >> 1], a1 = vst[2 * j + 1][dd >> 1];
-                    w[j] = (dd & 1) ? ((a0 >> 16) | (a1 & 0xFFFF0000u)) : ((a0 & 0xFFFFu) | (a1 << 16));
-                }
-                *reinterpret_cast<u32x4_t*>(vt + (v_dq * 4 + dd) * C::VROW + (v_kg >> 1) * 16 + (v_kg & 1) * 8) = w;
-            }
-        }
+    for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
+        const int row = (wave * C::DMA_PER_WAVE + i) * C::RPI + lane / C::NC;
+        const int lch = (lane % C::NC) ^ swz<HD>(row);
+        dma_k[i] = (uint32_t)(((int64_t)row * p.ldk + g * HD + lch * 8) * 2);
+        dma_v[i] = (uint32_t)(((int64_t)row * p.ldv + g * HD + lch * 8) * 2);
+    }
+    auto issue_tile = [&](int kbase, int stage) {
+        dma_tile<HD>(p, s0, Lb, g, wave, kbase, lds + stage * C::STAGE, dma_k, dma_v);
     };
 
-    f32x16_t oacc[NQB][C::DB];
-    float m_run[NQB], l_run[NQB];
+    // ---- per-lane LDS read offsets (bytes within a stage)
+    // K operand (A of S^T): row = kb*32 + r32, logical chunk dc*2 + half
+    uint32_t koff[C::DCH];
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-        m_run[qb] = -1.0e30f;
-        l_run[qb] = 0.0f;
+    for (int dc = 0; dc < C::DCH; ++dc)
+        koff[dc] = r32 * C::ROWB + (((dc * 2 + half) ^ swz<HD>(r32)) * 16);
+    // V operand (A of O^T) through the transpose read: 16-lane group (u, dh), lane i = 4 kk + qq
+    // reads key row 4u + 8jb + kk (+ kb*32 + h*16), d = db*32 + 16dh + 4qq .. +3.
+    uint32_t voff[C::DB][2];
+    {
+        const int grp = lane >> 4, i = lane & 15;
+        const int u = grp >> 1, dh = grp & 1, kk = i >> 2, qq = i & 3;
 #pragma unroll
         for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) oacc[qb][db][e] = 0.0f;
+            for (int jb = 0; jb < 2; ++jb) {
+                const int row = u * 4 + jb * 8 + kk;
+                const int lch = (db * 32 + dh * 16 + qq * 4) / 8;
+                voff[db][jb] = C::TILE + row * C::ROWB + ((lch ^ swz<HD>(row)) * 16) + (qq & 1) * 8;
+            }
     }
+
+    f32x16_t oacc[C::DB];
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[db][e] = 0.0f;
+    float m_run = -1.0e30f, l_run = 0.0f;
     const float c = p.c;
 
-    global_load(0);
-    lds_store(0);
-    __syncthreads();
-
-    for (int j = 0; j < ntiles; ++j) {
-        const int st = j & 1;
-        const int kbase = j * BK;
-        if (j + 1 < ntiles) global_load(kbase + BK);
-
-        if (j < wave_ntiles) {
-            const uint16_t* ks = smem + st * C::STAGE;
-            const uint16_t* vt = ks + C::K_ELEMS;
-            // S^T = K Q^T: 2 blocks of 32 keys x NQB blocks of 32 queries
-            f32x16_t s[2][NQB];
+    auto compute_tile = [&](int kbase, int stage) {
+        const lds_char_t* base = lds + stage * C::STAGE;
+        // S^T = K Q^T: 2 blocks of 32 keys
+        f32x16_t s[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) s[kb][e] = 0.0f;
+#pragma unroll
+        for (int dc = 0; dc < C::DCH; ++dc) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const bf16x8_t ka = as_bf16x8(*(const lds_u32x4_t*)(base + kb * 32 * C::ROWB + koff[dc]));
+                s[kb] = mfma32x32x16(ka, qreg[dc], s[kb]);
+            }
+        }
+        // causal mask per element on tiles that reach past the first query
+        if (kbase + BK - 1 > q0) {
+            const int qry = q0 + r32;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) s[kb][qb][e] = 0.0f;
-#pragma unroll
-            for (int dc = 0; dc < C::DCH; ++dc) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const bf16x8_t ka = as_bf16x8(*reinterpret_cast<const u32x4_t*>(
-                        ks + (kb * 32 + r32) * C::KROW + dc * 16 + half * 8));
-#pragma unroll
-                    for (int qb = 0; qb < NQB; ++qb) s[kb][qb] = mfma32x32x16(ka, qreg[qb][dc], s[kb][qb]);
+                for (int e = 0; e < 16; ++e) {
+                    const int key = kbase + kb * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
+                    if (key > qry) s[kb][e] = -__builtin_inff();
                 }
-            }
-            // causal mask per element on tiles that reach past the first query
-            if (kbase + BK - 1 > q0) {
+        }
+        // online softmax, one query per lane (its 32 keys split with lane ^ 32).
+        // A row's reference max only moves when the row's tile max exceeds it by
+        // more than kRescaleLog2 (log2 units): the result does not depend on the
+        // reference (it cancels in O / l) and p stays <= 2^kRescaleLog2.  So the
+        // rescale of O -- the only VALU work on the accumulators -- runs on the
+        // first tile and then rarely.  Only rows past the threshold move, so a
+        // row's arithmetic depends on its own scores alone.
+        float mx = s[0][0];
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                    for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-                        for (int e = 0; e < 16; ++e) {
-                            const int key = kbase + kb * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
-                            const int qry = q0 + qb * 32 + r32;
-                            if (key > qry) s[kb][qb][e] = -__builtin_inff();
-                        }
-            }
-            // online softmax (one query per lane; its 32 keys split with lane ^ 32).
-            // The running max is only moved when a row's tile max exceeds it by
-            // more than kRescaleLog2 (in log2 units): the result is the same for
-            // any reference value (it cancels in O / l), and the skipped moves keep
-            // p <= 2^kRescaleLog2.  So the rescale of O -- the only VALU work on
-            // the accumulators -- runs on the first tile and then only rarely.
-            bf16x8_t pb[NQB][2][2];
-#pragma unroll
-            for (int qb = 0; qb < NQB; ++qb) {
-                float mx = s[0][qb][0];
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) mx = __builtin_fmaxf(mx, s[kb][qb][e]);
-                mx = __builtin_fmaxf(mx, swap_halves(mx));
-                const bool move = (mx - m_run[qb]) * c > kRescaleLog2;
-                if (__builtin_amdgcn_ballot_w64(move) != 0) {
-                    // only rows past the threshold move, so every row's arithmetic
-                    // depends on its own scores alone (alpha = 1 is exact elsewhere)
-                    const float m_new = move ? mx : m_run[qb];
-                    const float alpha = move ? fast_exp2((m_run[qb] - m_new) * c) : 1.0f;
-                    m_run[qb] = m_new;
-                    l_run[qb] *= alpha;
-#pragma unroll
-                    for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-                        for (int e = 0; e < 16; ++e) oacc[qb][db][e] *= alpha;
-                }
-                const float mc = m_run[qb] * c;
-                float rs = 0.0f;
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const float pe = fast_exp2(__builtin_fmaf(s[kb][qb][e], c, -mc));
-                        s[kb][qb][e] = pe;
-                        rs += pe;
-                    }
-                l_run[qb] += rs;
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        u32x4_t w;
-#pragma unroll
-                        for (int t = 0; t < 4; ++t)
-                            w[t] = pack_bf16x2(s[kb][qb][h * 8 + 2 * t], s[kb][qb][h * 8 + 2 * t + 1]);
-                        pb[qb][kb][h] = as_bf16x8(w);
-                    }
-            }
-            // O^T += V^T P^T
+            for (int e = 0; e < 16; ++e) mx = __builtin_fmaxf(mx, s[kb][e]);
+        mx = __builtin_fmaxf(mx, swap_halves(mx));
+        const bool move = (mx - m_run) * c > kRescaleLog2;
+        if (__builtin_amdgcn_ballot_w64(move) != 0) {
+            const float m_new = move ? mx : m_run;
+            const float alpha = move ? fast_exp2((m_run - m_new) * c) : 1.0f;
+            m_run = m_new;
+            l_run *= alpha;
 #pragma unroll
             for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const bf16x8_t va = as_bf16x8(*reinterpret_cast<const u32x4_t*>(
-                            vt + (db * 32 + r32) * C::VROW + (kb * 2 + h) * 16 + half * 8));
-#pragma unroll
-                        for (int qb = 0; qb < NQB; ++qb) oacc[qb][db] = mfma32x32x16(va, pb[qb][kb][h], oacc[qb][db]);
-                    }
+                for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
         }
-        if (j + 1 < ntiles) lds_store(st ^ 1);
+        const float mc = m_run * c;
+        float rs = 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const float pe = fast_exp2(__builtin_fmaf(s[kb][e], c, -mc));
+                s[kb][e] = pe;
+                rs += pe;
+            }
+        l_run += rs;
+        bf16x8_t pb[2][2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                u32x4_t w;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) w[t] = pack_bf16x2(s[kb][h * 8 + 2 * t], s[kb][h * 8 + 2 * t + 1]);
+                pb[kb][h] = as_bf16x8(w);
+            }
+        // O^T += V^T P^T
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int roff = (kb * 32 + h * 16) * C::ROWB;
+                    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(base + roff + voff[db][0]));
+                    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(base + roff + voff[db][1]));
+                    const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
+                    const u32x4_t w = {l2[0], l2[1], h2[0], h2[1]};
+                    oacc[db] = mfma32x32x16(as_bf16x8(w), pb[kb][h], oacc[db]);
+                }
+    };
+
+    issue_tile(0, 0);
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    __syncthreads();
+    // two tiles per trip so each stage's LDS offsets are compile-time constants
+    for (int j = 0; j < ntiles; j += 2) {
+        if (j + 1 < ntiles) issue_tile((j + 1) * BK, 1);
+        if (j < wave_ntiles) compute_tile(j * BK, 0);
+        __builtin_amdgcn_s_waitcnt(kVmcnt0);
+        __syncthreads();
+        if (j + 1 >= ntiles) break;
+        if (j + 2 < ntiles) issue_tile((j + 2) * BK, 0);
+        if (j + 1 < wave_ntiles) compute_tile((j + 1) * BK, 1);
+        __builtin_amdgcn_s_waitcnt(kVmcnt0);
         __syncthreads();
     }
 
     if (!active) return;
     // ---- epilogue: O / l, bf16 RNE, 4 consecutive d per store
+    const float l_tot = l_run + swap_halves(l_run);
+    const float inv = 1.0f / l_tot;
+    const int row = q0 + r32;
+    if (row >= Lb) return;
+    uint16_t* dst = p.o + (s0 + row) * p.ldo + head * HD;
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-        const float l_tot = l_run[qb] + swap_halves(l_run[qb]);
-        const float inv = 1.0f / l_tot;
-        const int row = q0 + qb * 32 + r32;
-        if (row >= Lb) continue;
-        uint16_t* dst = p.o + (s0 + row) * p.ldo + head * HD;
+    for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                const int d = db * 32 + gq * 8 + half * 4;
-                u32x2_t w2 = {pack_bf16x2(oacc[qb][db][gq * 4 + 0] * inv, oacc[qb][db][gq * 4 + 1] * inv),
-                              pack_bf16x2(oacc[qb][db][gq * 4 + 2] * inv, oacc[qb][db][gq * 4 + 3] * inv)};
-                *reinterpret_cast<u32x2_t*>(dst + d) = w2;
-            }
-    }
+        for (int gq = 0; gq < 4; ++gq) {
+            const int d = db * 32 + gq * 8 + half * 4;
+            u32x2_t w2 = {pack_bf16x2(oacc[db][gq * 4 + 0] * inv, oacc[db][gq * 4 + 1] * inv),
+                          pack_bf16x2(oacc[db][gq * 4 + 2] * inv, oacc[db][gq * 4 + 3] * inv)};
+            *reinterpret_cast<u32x2_t*>(dst + d) = w2;
+        }
 }
 
-template <int HD, int NQB>
+template <int HD>
 hipError_t launch_cfg(const AttnArgs& a, hipStream_t s) {
-    using C = Cfg<HD, NQB>;
-    static const hipError_t attr = hipFuncSetAttribute((const void*)attn_fwd_kernel<HD, NQB>,
+    using C = Cfg<HD>;
+    static const hipError_t attr = hipFuncSetAttribute((const void*)attn_fwd_kernel<HD>,
                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                                        C::LDS_BYTES);
     if (attr != hipSuccess) return attr;
@@ -355,11 +365,11 @@ hipError_t launch_cfg(const AttnArgs& a, hipStream_t s) {
     p.c = a.scale * 1.4426950408889634f;
     p.o = a.o;
     p.ldo = a.ldo;
-    const int nqb = (a.max_seqlen + C::BQW - 1) / C::BQW;
+    const int nqb = (a.max_seqlen + BQ - 1) / BQ;
     p.ntg = (p.group * nqb + kWaves - 1) / kWaves;
     p.units = a.num_seqs * a.n_kv_head;
     const int64_t grid = (int64_t)p.ntg * p.units;
-    hipLaunchKernelGGL((attn_fwd_kernel<HD, NQB>), dim3((uint32_t)grid), dim3(kThreads), C::LDS_BYTES, s, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<HD>), dim3((uint32_t)grid), dim3(kThreads), C::LDS_BYTES, s, p);
     return hipGetLastError();
 }
 
@@ -367,9 +377,9 @@ hipError_t launch_cfg(const AttnArgs& a, hipStream_t s) {
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     switch (a.head_dim) {
-        case 32: return launch_cfg<32, 1>(a, s);
-        case 64: return launch_cfg<64, 1>(a, s);
-        case 128: return launch_cfg<128, 1>(a, s);
+        case 32: return launch_cfg<32>(a, s);
+        case 64: return launch_cfg<64>(a, s);
+        case 128: return launch_cfg<128>(a, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -1,0 +1,120 @@
+"""Host-only checks of libpca: it loads, exports every call include/pca.h
+declares, kv_layout matches the oracle's accounting, and every compute call
+rejects bad arguments before touching the device.  No GPU needed: the
+argument checks run before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import prefill_causal_attention_amd as pca
+from oracle import kvcache
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pca.h")
+
+FAKE = 0x10000          # an aligned "device" address; never dereferenced by these calls
+MISALIGNED = 0x10008
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:pca_status|const char\*)\s+(pca_\w+)\s*\(", text, re.M)))
+
+
+def test_library_loads_and_exports_header_symbols():
+    lib = pca.load()
+    names = _declared()
+    assert set(names) >= {"pca_kv_layout", "pca_qkv_proj", "pca_prefill_attention", "pca_kv_cache_write",
+                          "pca_last_error", "pca_version"}
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in pca.h but not exported"
+    assert set(names) == set(pca.EXPORTED)
+    assert pca.version().startswith("pca ")
+
+
+@pytest.mark.parametrize("nh,nkv,hd,dtype", [(32, 32, 128, "bf16"), (32, 8, 128, "bf16"), (40, 8, 128, "fp8_e4m3"),
+                                             (2, 2, 32, "bf16"), (8, 1, 64, "fp8_e4m3")])
+def test_kv_layout_matches_oracle(nh, nkv, hd, dtype):
+    got = pca.kv_layout(nh, nkv, hd, 16, dtype)
+    want = kvcache.layout(nh, nkv, hd, 16, 1 if dtype == "fp8_e4m3" else 2)
+    for k, v in want.items():
+        assert got[k] == v, k
+    assert got["page_size"] == 16 and got["elem_bytes"] == want["kv_bytes_per_token_layer"] // (2 * nkv * hd)
+
+
+def test_kv_layout_page_figures(golden):
+    for name, n_kv, hd, eb, layers, tokens, expected, _ in golden("kv_bytes_pages.txt"):
+        if int(layers) == 1 and int(tokens) == 1:
+            lay = pca.kv_layout(int(n_kv), int(n_kv), int(hd), 16, "bf16")
+            assert lay["kv_bytes_per_token_layer"] == int(expected), name
+
+
+@pytest.mark.parametrize("args", [(32, 7, 128), (0, 1, 128), (4, 0, 128), (4, 2, 0)])
+def test_kv_layout_rejects(args):
+    with pytest.raises(pca.PcaError) as e:
+        pca.kv_layout(*args)
+    assert e.value.status == 1
+
+
+def _status(fn, *a):
+    lib = pca.load()
+    st = getattr(lib, fn)(*a)
+    return st, lib.pca_last_error().decode()
+
+
+def test_qkv_proj_validation():
+    cases = [
+        (0, 64, FAKE, 64, FAKE, 64, 4, 4, 64),            # null x
+        (MISALIGNED, 64, FAKE, 64, FAKE, 64, 4, 4, 64),   # misaligned x
+        (FAKE, 64, FAKE, 64, FAKE, 64, 0, 4, 64),         # M = 0
+        (FAKE, 64, FAKE, 64, FAKE, 64, 4, 4, 60),         # K % 8
+        (FAKE, 32, FAKE, 64, FAKE, 64, 4, 4, 64),         # ldx < K
+        (FAKE, 64, FAKE, 64, FAKE, 2, 4, 4, 64),          # ldy < N
+    ]
+    for c in cases:
+        st, msg = _status("pca_qkv_proj", *c, None)
+        assert st == 1 and msg, c
+
+
+def test_attention_validation():
+    base = dict(q=FAKE, k=FAKE, v=FAKE, ldq=4096, ldk=1024, ldv=1024, cu=None, ns=1, mx=64, T=64,
+                nh=32, nkv=8, hd=128, scale=0.088, causal=1, o=FAKE, ldo=4096)
+    bad = [dict(nkv=7), dict(hd=96), dict(hd=256), dict(causal=0), dict(q=0), dict(o=MISALIGNED),
+           dict(ldq=4000), dict(ldo=100), dict(ns=2), dict(scale=0.0), dict(scale=float("nan")),
+           dict(mx=10), dict(T=-1)]
+    want = {"hd": 2}
+    for b in bad:
+        a = dict(base, **b)
+        st, msg = _status("pca_prefill_attention", a["q"], a["k"], a["v"], a["ldq"], a["ldk"], a["ldv"], a["cu"],
+                          a["ns"], a["mx"], a["T"], a["nh"], a["nkv"], a["hd"], ctypes.c_float(a["scale"]),
+                          a["causal"], a["o"], a["ldo"], None)
+        exp = want.get(next(iter(b)), 1)
+        assert st == exp and msg, (b, st, msg)
+
+
+def test_attention_empty_batch_is_ok_without_buffers():
+    st, _ = _status("pca_prefill_attention", None, None, None, 4096, 1024, 1024, None, 1, 0, 0, 32, 8, 128,
+                    ctypes.c_float(0.088), 1, None, 4096, None)
+    assert st == 0
+
+
+def test_kv_write_validation():
+    base = dict(k=FAKE, v=FAKE, ldk=1024, ldv=1024, cu=None, ns=1, T=64, bt=FAKE, mp=4, nkv=8, hd=128, ps=16,
+                dt=0, kc=FAKE, vc=FAKE, ks=None, vs=None, np_=4)
+    bad = {("ps", 32): 2, ("hd", 48): 2, ("dt", 5): 2, ("dt", 1): 1, ("ks", FAKE): 1, ("bt", 0): 1,
+           ("kc", MISALIGNED): 1, ("ldk", 1000): 1, ("mp", 0): 1, ("np_", 0): 1, ("ns", 3): 1, ("nkv", 0): 1}
+    for (key, val), exp in bad.items():
+        a = dict(base, **{key: val})
+        st, msg = _status("pca_kv_cache_write", a["k"], a["v"], a["ldk"], a["ldv"], a["cu"], a["ns"], a["T"], a["bt"],
+                          a["mp"], a["nkv"], a["hd"], a["ps"], a["dt"], a["kc"], a["vc"], a["ks"], a["vs"],
+                          a["np_"], None)
+        assert st == exp and msg, (key, val, st, msg)
+
+
+def test_error_message_is_thread_local_and_cleared():
+    st, msg = _status("pca_kv_cache_write", 0, 0, 0, 0, None, 1, 5, 0, 1, 1, 128, 16, 0, 0, 0, None, None, 1, None)
+    assert st == 1 and "null" in msg
+    pca.kv_layout(4, 2, 64)
+    assert pca.load().pca_last_error().decode() == ""
