@@ -11,31 +11,38 @@
 // (§3.3).  Scores never leave registers.
 //
 // gfx950 mapping.
-//  * A wave owns 32 query rows of one head; a workgroup is 4 waves (one per
-//    SIMD) that share one kv head and therefore the kv tiles in LDS: for
-//    G >= 4 the 4 waves are 4 query heads at the same positions, for smaller
-//    G consecutive query blocks.  Two workgroups per CU (2 waves per SIMD).
+//  * A wave owns 32 query rows of one head.  A workgroup is 8 waves that
+//    share one kv head (and so every K/V tile in LDS), one workgroup per CU:
+//    two waves per SIMD, waves w and w + 4 on the same SIMD.  For G = 4 the
+//    workgroup is 4 query heads x 64 consecutive rows.
+//  * Ping-pong between the two waves of a SIMD.  Waves 0-3 (group A) and
+//    4-7 (group B) alternate two phases per kv tile, switching at a
+//    workgroup barrier: the matrix phase (O += P V for this tile, then the
+//    scores of the next tile) and the softmax phase (max, exponentials, sums,
+//    packing of P).  While one wave of a SIMD is in its matrix phase the
+//    other is in its softmax, so the MFMA pipe and the VALU work at the same
+//    time; the matrix-phase wave runs at raised priority so its MFMAs issue
+//    as soon as the pipe frees.  (Within one wave, transcendental VALU work
+//    overlaps poorly with that wave's own MFMAs; across two waves it
+//    overlaps almost completely.)
 //  * Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16: the 32x32 accumulator then holds, in each
 //    lane, 16 keys of ONE query (the lane's column).  Row max and row sum are
-//    lane-local plus one exchange with lane ^ 32, and the accumulator is
+//    lane-local plus one exchange between the wave's two 32-lane halves
+//    (v_permlane32_swap, no LDS traffic), and the accumulator is
 //    already the B operand of the second product O^T = V^T P^T once
 //    converted to bf16 -- no cross-lane shuffle of P.
-//  * Software pipeline inside a wave: while the softmax of kv tile j runs on
-//    the VALU, the scores of tile j + 1 are already on the matrix cores, so a
-//    wave keeps its MFMA pipe busy through its own softmax; the other wave on
-//    the SIMD fills the VALU while this one runs P V.  K therefore runs one
-//    tile ahead of V: K and V have separate double buffers, and iteration j
-//    reads K_{j+1} and V_j while K_{j+2} and V_{j+1} arrive.
-//  * K and V tiles (64 keys) go from HBM/L2 straight into LDS with
-//    buffer_load ... lds (no register staging).  Rows are stored key-major
-//    with the 16-byte chunks of each row XOR-swizzled by the row index, so
-//    that the K operand reads (ds_read_b128, 16 rows per 16 lanes) and the V
-//    operand reads hit all 64 banks once.  V^T comes out of LDS with the
-//    gfx950 transpose read ds_read_b64_tr_b16: each 16-lane group returns,
-//    for 16 consecutive d, 4 keys per lane -- the A-operand layout of
-//    O^T = V^T P^T, in the same key order the S^T accumulator hands to the B
-//    operand (within 16 keys: 0-3, 8-11 | 4-7, 12-15).
+//  * K runs one tile ahead of V (the matrix phase of tile j needs K_{j+1}
+//    and V_j): K and V have separate LDS double buffers, and the tiles
+//    K_{j+2}, V_{j+1} are in flight during tile j.  They go from HBM/L2
+//    straight into LDS with buffer_load ... lds (no register staging).  Rows
+//    are stored key-major with the 16-byte chunks of each row XOR-swizzled
+//    by the row index, so that the K operand reads (ds_read_b128, 16 rows per
+//    16 lanes) and the V operand reads hit all 64 banks once.  V^T comes out
+//    of LDS with the gfx950 transpose read ds_read_b64_tr_b16: each 16-lane
+//    group returns, for 16 consecutive d, 4 keys per lane -- the A-operand
+//    layout of O^T = V^T P^T, in the same key order the S^T accumulator hands
+//    to the B operand (within 16 keys: 0-3, 8-11 | 4-7, 12-15).
 //  * Q stays in registers (B operand of S^T) for the whole kv loop; the O^T
 //    accumulator (fp32) likewise.
 //  * exp is exp2 with scale*log2(e) folded into one FMA; m, l, P in fp32,
@@ -43,13 +50,13 @@
 //    moves only when the row's scores exceed it by 2^8 (see below); the new
 //    reference is a per-lane select, so the exponentials need no branch, and
 //    only the rescale of O and l sits behind one -- taken on the first tile
-//    and rarely after.  The common path is one straight block the scheduler
-//    can interleave with the matrix-core work.
+//    and rarely after.
 //  * The causal rule: a wave skips kv tiles that start after its last query,
 //    and masks per element only on tiles that reach past its first query.
-//    Workgroups are ordered heaviest-first and all workgroups of one
-//    (sequence, kv head) are placed on one XCD (ids go round-robin over the
-//    8 XCDs), so its K/V stays in that XCD's L2.
+//    Workgroups are ordered heaviest-first, and units (sequence, kv head) go
+//    round-robin over the 8 XCDs (workgroup ids are dispatched that way), so
+//    one unit's K/V stays in one XCD's L2 and, with 8 kv heads, every XCD
+//    gets one kv head of every sequence.
 #include "pca_device.hpp"
 #include "pca_internal.hpp"
 
@@ -59,12 +66,11 @@ namespace pca {
 
 namespace {
 
-typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) char lds_char_t;
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;               // per workgroup; waves w and w + 4 share a SIMD
+constexpr int kThreads = kWaves * 64;
 constexpr int BQ = 32;                  // query rows per wave
 constexpr int BK = 64;                  // keys per kv tile
 constexpr float kRescaleLog2 = 8.0f;    // lazy max update threshold (p stays <= 256)
@@ -78,11 +84,11 @@ struct Cfg {
     static constexpr int KBUF0 = 0, KBUF1 = TILE;        // K double buffer
     static constexpr int VBUF0 = 2 * TILE, VBUF1 = 3 * TILE;   // V double buffer
     static constexpr int LDS_BYTES = 4 * TILE;
-    static constexpr int RPI = 1024 / ROWB;              // rows per 1 KiB wave DMA instruction
-    static constexpr int DMA_PER_WAVE = TILE / 1024 / kWaves;
+    static constexpr int RPI = 1024 / ROWB;              // key rows per 1 KiB DMA block
+    static constexpr int NBLK = TILE / 1024;             // 1 KiB DMA blocks per tile
+    static constexpr int DMA_ITERS = (NBLK + kWaves - 1) / kWaves;
     static constexpr int DCH = HD / 16;                  // k16 steps over head_dim
     static constexpr int DB = HD / 32;                   // 32-row blocks of O^T
-    static_assert(DMA_PER_WAVE >= 1, "tile too small for the DMA split");
     static_assert(VBUF1 + 3 * 16 * ROWB < 65536, "V reads use 16-bit DS immediate offsets");
 };
 
@@ -104,10 +110,24 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 __device__ inline uint32_t lds_addr(const lds_char_t* p) { return (uint32_t)(uintptr_t)p; }
 
+// Workgroup barrier with no implied waits.  __syncthreads (and any fence on
+// LDS) makes the compiler wait for every outstanding global load, because the
+// K/V DMA writes LDS; here the DMA must stay in flight across half-steps.  No
+// fence is needed: every LDS read of the kernel is inline asm retired by an
+// explicit lgkmcnt wait before its data is used, and the DMA is retired by an
+// explicit vmcnt wait before the barrier that publishes it.  The memory
+// clobber and the scheduling barriers keep the compiler from moving anything
+// across.
+__device__ __forceinline__ void wg_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // ds_read_b64_tr_b16 as inline asm.  Issued through the builtin, the read
 // carries no alias information, and the compiler then waits for every
 // outstanding global->LDS DMA (the next kv tiles, which target the other
-// buffers) before it; as asm its completion is tracked by lds_wait_block.
+// buffers) before it; as asm its completion is tracked by lds_wait.
 template <int OFF>
 __device__ __forceinline__ u32x2_t lds_read_tr16(uint32_t addr) {
     static_assert(OFF >= 0 && OFF < 65536, "DS offset field is 16 bits");
@@ -116,25 +136,34 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(uint32_t addr) {
     return r;
 }
 
-// The 8 V^T fragments of O^T block DB from the V buffer at byte offset VBUF:
-// for each 16-key group f = (kb, h), the reads of key rows 0-3 and 8-11.
-template <int HD, int VBUF, int DB>
-__device__ __forceinline__ void read_v_block(const uint32_t (&vaddr)[Cfg<HD>::DB][2], u32x2_t (&out)[8]) {
-    static_for<4>([&](auto F) {
-        constexpr int f = decltype(F)::value;
-        constexpr int off = VBUF + f * 16 * Cfg<HD>::ROWB;
-        out[2 * f] = lds_read_tr16<off>(vaddr[DB][0]);
-        out[2 * f + 1] = lds_read_tr16<off>(vaddr[DB][1]);
-    });
+// ds_read_b128 as inline asm, for the same reason: all LDS reads of the
+// matrix phase are issued and retired under explicit control.
+template <int OFF>
+__device__ __forceinline__ u32x4_t lds_read_b128(uint32_t addr) {
+    static_assert(OFF >= 0 && OFF < 65536, "DS offset field is 16 bits");
+    u32x4_t r;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+    return r;
 }
 
 // Wait until at most N LDS operations are outstanding (LDS returns in order);
-// the fragments pass through the asm so their consumers stay after the wait.
+// the fragment passes through the asm so its consumer stays after the wait.
 template <int N>
-__device__ __forceinline__ void lds_wait_block(u32x2_t (&v)[8]) {
-    asm volatile("s_waitcnt lgkmcnt(%8)"
-                 : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7])
-                 : "n"(N));
+__device__ __forceinline__ void lds_wait(u32x4_t& v) {
+    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(v) : "n"(N));
+}
+template <int N>
+__device__ __forceinline__ void lds_wait(u32x2_t& a, u32x2_t& b) {
+    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N));
+}
+
+// LDS reads still in flight after those of MFMA i of a matrix phase, when
+// the reads run LA MFMAs ahead: MFMAs [0, NPV) take two reads, the rest one.
+template <int NPV, int NM, int LA>
+constexpr int reads_after(int i) {
+    int n = 0;
+    for (int m = i + 1; m <= i + LA - 1 && m < NM; ++m) n += (m < NPV) ? 2 : 1;
+    return n;
 }
 
 struct Params {
@@ -155,16 +184,24 @@ struct Params {
 
 // DMA of one K or V tile (keys [kbase, kbase + BK) of one sequence) into the
 // LDS buffer `dst`: the buffer view starts at the tile, so keys at or past the
-// sequence end read 0.  Wave w fills the 1 KiB blocks [w*DMA_PER_WAVE, ...).
+// sequence end read 0.  Wave w fills the 1 KiB blocks w, w + 8, ...
 template <int HD>
 __device__ __forceinline__ void dma_tile(const uint16_t* src, int64_t ld, int64_t s0, int Lb, int wave, int kbase,
                                          lds_char_t* dst, const uint32_t* off) {
     using C = Cfg<HD>;
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(src + (s0 + kbase) * ld, (uint32_t)((int64_t)(Lb - kbase) * ld * 2));
+    // the tile's base and extent are workgroup-uniform; readfirstlane keeps
+    // them in scalar registers (a resource in vector registers would need a
+    // per-lane loop around every DMA)
+    const uint64_t base = (uint64_t)(src + (s0 + kbase) * ld);
+    const uint64_t ubase = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(base >> 32)) << 32) |
+                           (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base);
+    const uint32_t bytes = (uint32_t)__builtin_amdgcn_readfirstlane((int)((int64_t)(Lb - kbase) * ld * 2));
+    const __amdgpu_buffer_rsrc_t r = make_rsrc((const void*)ubase, bytes);
 #pragma unroll
-    for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
-        const int blk = wave * C::DMA_PER_WAVE + i;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(dst + blk * 1024), 16, off[i], 0, 0, 0);
+    for (int i = 0; i < C::DMA_ITERS; ++i) {
+        const int blk = wave + i * kWaves;
+        if (C::NBLK % kWaves == 0 || blk < C::NBLK)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(dst + blk * 1024), 16, off[i], 0, 0, 0);
     }
 }
 
@@ -177,6 +214,7 @@ void attn_fwd_kernel(Params p) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool lead = wave < kWaves / 2;                       // group A: matrix phase first
     const int r32 = lane & 31, half = lane >> 5;
 
     // ---- workgroup -> (unit = (sequence, kv head), task group), heaviest first
@@ -202,7 +240,11 @@ void attn_fwd_kernel(Params p) {
         s0 = min<int64_t>(max<int64_t>(p.cu[b], 0), p.total);
         s1 = min<int64_t>(max<int64_t>(p.cu[b + 1], s0), p.total);
     }
-    const int Lb = (int)(s1 - s0);
+    // sequence bounds are workgroup-uniform: keep them in scalar registers so
+    // the buffer resources built from them need no per-lane handling
+    s0 = ((int64_t)__builtin_amdgcn_readfirstlane((int)(s0 >> 32)) << 32) |
+         (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)s0);
+    const int Lb = __builtin_amdgcn_readfirstlane((int)(s1 - s0));
     const int G = p.group;
     const int nqb = (Lb + BQ - 1) / BQ;
     const int ntasks = G * nqb;
@@ -235,23 +277,23 @@ void attn_fwd_kernel(Params p) {
     // ---- DMA lane offsets: lane l writes bytes [16 l, 16 l + 16) of a 1 KiB block,
     // i.e. row l / NC, physical chunk l % NC, so it fetches the logical chunk the
     // swizzle puts there.
-    uint32_t dma_k[C::DMA_PER_WAVE], dma_v[C::DMA_PER_WAVE];
+    uint32_t dma_k[C::DMA_ITERS], dma_v[C::DMA_ITERS];
 #pragma unroll
-    for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
-        const int row = (wave * C::DMA_PER_WAVE + i) * C::RPI + lane / C::NC;
+    for (int i = 0; i < C::DMA_ITERS; ++i) {
+        const int row = (wave + i * kWaves) * C::RPI + lane / C::NC;
         const int lch = (lane % C::NC) ^ swz<HD>(row);
         dma_k[i] = (uint32_t)(((int64_t)row * p.ldk + g * HD + lch * 8) * 2);
         dma_v[i] = (uint32_t)(((int64_t)row * p.ldv + g * HD + lch * 8) * 2);
     }
-    auto issue_k = [&](int tile, int buf) { dma_tile<HD>(p.k, p.ldk, s0, Lb, wave, tile * BK, lds + buf, dma_k); };
-    auto issue_v = [&](int tile, int buf) { dma_tile<HD>(p.v, p.ldv, s0, Lb, wave, tile * BK, lds + buf, dma_v); };
+    auto issue_k = [&](int tile, int buf) __attribute__((always_inline)) { dma_tile<HD>(p.k, p.ldk, s0, Lb, wave, tile * BK, lds + buf, dma_k); };
+    auto issue_v = [&](int tile, int buf) __attribute__((always_inline)) { dma_tile<HD>(p.v, p.ldv, s0, Lb, wave, tile * BK, lds + buf, dma_v); };
 
     // ---- per-lane LDS read offsets
     // K operand (A of S^T): row = kb*32 + r32, logical chunk dc*2 + half
-    uint32_t koff[C::DCH];
+    uint32_t kaddr[C::DCH];
 #pragma unroll
     for (int dc = 0; dc < C::DCH; ++dc)
-        koff[dc] = r32 * C::ROWB + (((dc * 2 + half) ^ swz<HD>(r32)) * 16);
+        kaddr[dc] = lds_addr(lds) + r32 * C::ROWB + (((dc * 2 + half) ^ swz<HD>(r32)) * 16);
     // V operand (A of O^T) through the transpose read: 16-lane group (u, dh), lane i = 4 kk + qq
     // reads key row 4u + 8jb + kk (+ kb*32 + h*16), d = db*32 + 16dh + 4qq .. +3.
     uint32_t vaddr[C::DB][2];
@@ -275,25 +317,103 @@ void attn_fwd_kernel(Params p) {
         for (int e = 0; e < 16; ++e) oacc[db][e] = 0.0f;
     float m_run = -1.0e30f, l_run = 0.0f;
     const float c = p.c;
+    f32x16_t s[2];          // scores of the tile whose softmax is next
+    bf16x8_t pb[2][2];      // P of the tile whose P V product is next
 
-    // S^T = K Q^T for the tile in K buffer KB: 2 blocks of 32 keys
-    auto scores = [&](auto KBc, f32x16_t (&s)[2]) {
+    // Matrix phase of tile j: O^T += V^T P^T for tile j (V buffer VC), then
+    // S^T = K Q^T for tile j + 1 (K buffer KN), as one sequence of NM MFMAs
+    // whose LDS operands are read LA MFMAs ahead; scheduling barriers pin the
+    // order, so every read has LA MFMAs (~LA * 32 cycles) to land.  P_j is
+    // dead before the score accumulators come alive.  On the wave's last tile
+    // the scores computed here are never used.
+    constexpr int LA = 4;
+    constexpr int NPV = 4 * C::DB;         // (db, kb, h): V^T block x 16-key group
+    constexpr int NS = 2 * C::DCH;         // (dc, kb): head_dim step x 32-key block
+    constexpr int NM = NPV + NS;
+    auto matrix_phase = [&](int j, auto KNc, auto VCc) __attribute__((always_inline)) {
+        if (j >= wave_ntiles) return;
+        constexpr int KB = decltype(KNc)::value, VB = decltype(VCc)::value;
+        u32x2_t vlo[NPV], vhi[NPV];
+        u32x4_t kf[NS];
+        auto issue = [&](auto Ic) __attribute__((always_inline)) {
+            constexpr int i = decltype(Ic)::value;
+            if constexpr (i < NPV) {
+                constexpr int db = i / 4, f = i % 4;
+                constexpr int off = VB + f * 16 * C::ROWB;      // key group f = (kb, h)
+                vlo[i] = lds_read_tr16<off>(vaddr[db][0]);      // key rows 0-3 of the group
+                vhi[i] = lds_read_tr16<off>(vaddr[db][1]);      // key rows 8-11
+            } else {
+                constexpr int m = i - NPV, dc = m / 2, kb = m % 2;
+                kf[m] = lds_read_b128<KB + kb * 32 * C::ROWB>(kaddr[dc]);
+            }
+        };
+        __builtin_amdgcn_s_setprio(1);
+        static_for<LA>([&](auto Ic) { issue(Ic); });
+        static_for<NM>([&](auto Ic) {
+            constexpr int i = decltype(Ic)::value;
+            constexpr int n = reads_after<NPV, NM, LA>(i);
+            if constexpr (i < NPV) {
+                constexpr int db = i / 4, kb = (i % 4) / 2, h = i % 2;
+                lds_wait<n>(vlo[i], vhi[i]);
+                const u32x4_t w = {vlo[i][0], vlo[i][1], vhi[i][0], vhi[i][1]};
+                oacc[db] = mfma32x32x16(as_bf16x8(w), pb[kb][h], oacc[db]);
+            } else {
+                constexpr int m = i - NPV, dc = m / 2, kb = m % 2;
+                lds_wait<n>(kf[m]);
+                // the first head_dim step starts from a zero accumulator
+                s[kb] = mfma32x32x16(as_bf16x8(kf[m]), qreg[dc], dc == 0 ? f32x16_t{} : s[kb]);
+            }
+            if constexpr (i + LA < NM) issue(std::integral_constant<int, i + LA>{});
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        __builtin_amdgcn_s_setprio(0);
+    };
+
+    // S^T = K Q^T for the tile in K buffer KB (prologue only)
+    auto scores = [&](auto KBc) __attribute__((always_inline)) {
         constexpr int KB = decltype(KBc)::value;
+        static_for<NS>([&](auto Mc) {
+            constexpr int m = decltype(Mc)::value, dc = m / 2, kb = m % 2;
+            u32x4_t k = lds_read_b128<KB + kb * 32 * C::ROWB>(kaddr[dc]);
+            lds_wait<0>(k);
+            s[kb] = mfma32x32x16(as_bf16x8(k), qreg[dc], dc == 0 ? f32x16_t{} : s[kb]);
+        });
+    };
+
+    // Softmax phase of tile t (scores in s): P_t into pb, m and l updated.
+    auto softmax_phase = [&](int t) __attribute__((always_inline)) {
+        if (t >= wave_ntiles) return;
+        const int kbase = t * BK;
+        // causal mask per element on tiles that reach past the first query
+        if (kbase + BK - 1 > q0) {
+            const int qry = q0 + r32;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int key = kbase + kb * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
+                    if (key > qry) s[kb][e] = -__builtin_inff();
+                }
+        }
+        // Online softmax, one query per lane (its 64 keys split with lane ^ 32).
+        // A row's reference max only moves when the row's tile max exceeds it by
+        // more than kRescaleLog2 (log2 units): the result does not depend on the
+        // reference (it cancels in O / l) and p stays <= 2^kRescaleLog2.  Only
+        // rows past the threshold move, so a row's arithmetic depends on its own
+        // scores alone.
+        float mx = s[0][0];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) s[kb][e] = 0.0f;
-#pragma unroll
-        for (int dc = 0; dc < C::DCH; ++dc)
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const bf16x8_t ka = as_bf16x8(*(const lds_u32x4_t*)(lds + KB + kb * 32 * C::ROWB + koff[dc]));
-                s[kb] = mfma32x32x16(ka, qreg[dc], s[kb]);
-            }
-    };
-
-    // p = exp2(s*c - mc) in place, row sum, bf16 packing as the B operand of O^T
-    auto exponentiate = [&](f32x16_t (&s)[2], float mc, bf16x8_t (&pb)[2][2]) -> float {
+            for (int e = 0; e < 16; ++e) mx = __builtin_fmaxf(mx, s[kb][e]);
+        {
+            float lo, hi;
+            both_halves(mx, lo, hi);
+            mx = __builtin_fmaxf(lo, hi);
+        }
+        const bool move = (mx - m_run) * c > kRescaleLog2;
+        const float m_ref = move ? mx : m_run;
+        const float mc = m_ref * c;
         float rs = 0.0f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -309,77 +429,9 @@ void attn_fwd_kernel(Params p) {
             for (int h = 0; h < 2; ++h) {
                 u32x4_t w;
 #pragma unroll
-                for (int t = 0; t < 4; ++t) w[t] = pack_bf16x2(s[kb][h * 8 + 2 * t], s[kb][h * 8 + 2 * t + 1]);
+                for (int t2 = 0; t2 < 4; ++t2) w[t2] = pack_bf16x2(s[kb][h * 8 + 2 * t2], s[kb][h * 8 + 2 * t2 + 1]);
                 pb[kb][h] = as_bf16x8(w);
             }
-        return rs;
-    };
-
-    // O^T += V^T P^T from V buffer VB.  The V^T fragments of block db + 1 are in
-    // flight while block db is on the matrix cores (lgkmcnt(8) retires block db).
-    auto pv = [&](auto VBc, const bf16x8_t (&pb)[2][2]) {
-        constexpr int VB = decltype(VBc)::value;
-        u32x2_t vf[2][8];
-        read_v_block<HD, VB, 0>(vaddr, vf[0]);
-        static_for<C::DB>([&](auto DBc) {
-            constexpr int db = decltype(DBc)::value;
-            if constexpr (db + 1 < C::DB) {
-                read_v_block<HD, VB, db + 1>(vaddr, vf[(db + 1) & 1]);
-                lds_wait_block<8>(vf[db & 1]);
-            } else {
-                lds_wait_block<0>(vf[db & 1]);
-            }
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int f = (kb * 2 + h) * 2;
-                    const u32x4_t w = {vf[db & 1][f][0], vf[db & 1][f][1], vf[db & 1][f + 1][0], vf[db & 1][f + 1][1]};
-                    oacc[db] = mfma32x32x16(as_bf16x8(w), pb[kb][h], oacc[db]);
-                }
-        });
-    };
-
-    // score accumulators: tile j in one, tile j + 1 in the other, roles swapping each tile
-    f32x16_t s_a[2], s_b[2];
-
-    // One kv tile j: softmax of S_j (in s_cur) while S_{j+1} goes to the matrix
-    // cores (into s_next), then O += P_j V_j.  KN: K buffer of tile j + 1, VC: V
-    // buffer of tile j.  On a wave's last tile the scores of "tile j + 1" are
-    // computed from whatever the K buffer holds and never used.
-    auto step = [&](int j, auto KNc, auto VCc, f32x16_t (&s_cur)[2], f32x16_t (&s_next)[2]) {
-        const int kbase = j * BK;
-        // causal mask per element on tiles that reach past the first query
-        if (kbase + BK - 1 > q0) {
-            const int qry = q0 + r32;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int key = kbase + kb * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
-                    if (key > qry) s_cur[kb][e] = -__builtin_inff();
-                }
-        }
-        scores(KNc, s_next);
-        // Online softmax, one query per lane (its 64 keys split with lane ^ 32).
-        // A row's reference max only moves when the row's tile max exceeds it by
-        // more than kRescaleLog2 (log2 units): the result does not depend on the
-        // reference (it cancels in O / l) and p stays <= 2^kRescaleLog2.  Only
-        // rows past the threshold move, so a row's arithmetic depends on its own
-        // scores alone.
-        float mx = s_cur[0][0];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) mx = __builtin_fmaxf(mx, s_cur[kb][e]);
-        mx = __builtin_fmaxf(mx, swap_halves(mx));
-        const bool move = (mx - m_run) * c > kRescaleLog2;
-        const float m_ref = move ? mx : m_run;
-        bf16x8_t pb[2][2];
-        const float rs = exponentiate(s_cur, m_ref * c, pb);
-        // keep the exponentials in this block, next to the score MFMAs, instead
-        // of letting them sink past the rare branch
-        asm volatile("" : : "v"(pb[0][0]), "v"(pb[0][1]), "v"(pb[1][0]), "v"(pb[1][1]), "v"(rs));
         if (__builtin_amdgcn_ballot_w64(move) != 0) {
             // rare: rows past the threshold move their reference; rescale their O and l
             const float alpha = fast_exp2((m_run - m_ref) * c);
@@ -391,18 +443,32 @@ void attn_fwd_kernel(Params p) {
                 for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
         }
         l_run += rs;
-        pv(VCc, pb);
     };
 
-    // One loop iteration: DMA of K_{j+2} (into K_j's buffer) and V_{j+1}, then
-    // tile j.  Tile j's K buffer is (j & 1), its V buffer (j & 1).
-    auto iteration = [&](int j, auto KCc, auto KNc, auto VCc, auto VNc, f32x16_t (&s_cur)[2], f32x16_t (&s_next)[2]) {
-        constexpr int KC = decltype(KCc)::value, VN = decltype(VNc)::value;
-        if (j + 2 < ntiles) issue_k(j + 2, KC);
-        if (j + 1 < ntiles) issue_v(j + 1, VN);
-        if (j < wave_ntiles) step(j, KNc, VCc, s_cur, s_next);
-        __builtin_amdgcn_s_waitcnt(kVmcnt0);
-        __syncthreads();
+    // The two groups run the same sequence of phases -- softmax of tile j,
+    // then the matrix phase of tile j -- with group B one half-step behind
+    // group A, so that in every half-step one wave of each SIMD is in its
+    // matrix phase and the other in its softmax.  Half-steps end at workgroup
+    // barriers; B starts with one extra barrier and A ends with one.
+    //
+    // DMA: in half-step 2m + 1 (A's matrix phase of tile m, B's softmax of
+    // tile m) every wave issues its share of K_{m+2} (into K_m's buffer) and
+    // V_{m+1} (into V_{m-1}'s); both were last read in half-step 2m.  They are
+    // waited for at the end of half-step 2m + 2 and first read in 2m + 3.
+    // KC/KN: K buffers of tiles j and j + 1; VC/VN: V buffers of j and j + 1.
+    auto issue_next = [&](int j, auto KCc, auto VNc) __attribute__((always_inline)) {
+        if (j + 2 < ntiles) issue_k(j + 2, decltype(KCc)::value);
+        if (j + 1 < ntiles) issue_v(j + 1, decltype(VNc)::value);
+    };
+    auto tile = [&](int j, auto KCc, auto KNc, auto VCc, auto VNc) __attribute__((always_inline)) {
+        if (!lead) issue_next(j, KCc, VNc);
+        softmax_phase(j);
+        if (lead) __builtin_amdgcn_s_waitcnt(kVmcnt0);
+        wg_barrier();
+        if (lead) issue_next(j, KCc, VNc);
+        matrix_phase(j, KNc, VCc);
+        if (!lead) __builtin_amdgcn_s_waitcnt(kVmcnt0);
+        wg_barrier();
     };
 
     using K0 = std::integral_constant<int, C::KBUF0>;
@@ -410,25 +476,28 @@ void attn_fwd_kernel(Params p) {
     using V0 = std::integral_constant<int, C::VBUF0>;
     using V1 = std::integral_constant<int, C::VBUF1>;
 
-    // prologue: K_0, V_0 and K_1 in flight, scores of tile 0, and a barrier so
-    // that K_0's buffer is free before K_2 lands in it
+    // prologue: K_0, V_0 and K_1 in flight, then every wave computes the
+    // scores of tile 0; group B waits one half-step
     issue_k(0, C::KBUF0);
     issue_v(0, C::VBUF0);
     if (1 < ntiles) issue_k(1, C::KBUF1);
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();
-    if (0 < wave_ntiles) scores(K0{}, s_a);
-    __syncthreads();
+    if (0 < wave_ntiles) scores(K0{});
+    if (!lead) wg_barrier();
     // two tiles per trip so every buffer offset is a compile-time constant
     for (int j = 0; j < ntiles; j += 2) {
-        iteration(j, K0{}, K1{}, V0{}, V1{}, s_a, s_b);
+        tile(j, K0{}, K1{}, V0{}, V1{});
         if (j + 1 >= ntiles) break;
-        iteration(j + 1, K1{}, K0{}, V1{}, V0{}, s_b, s_a);
+        tile(j + 1, K1{}, K0{}, V1{}, V0{});
     }
+    if (lead) wg_barrier();
 
     if (!active) return;
     // ---- epilogue: O / l, bf16 RNE, 4 consecutive d per store
-    const float l_tot = l_run + swap_halves(l_run);
+    float l_lo, l_hi;
+    both_halves(l_run, l_lo, l_hi);
+    const float l_tot = l_lo + l_hi;
     const float inv = 1.0f / l_tot;
     const int row = q0 + r32;
     if (row >= Lb) return;

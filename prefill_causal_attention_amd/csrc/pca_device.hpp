@@ -49,7 +49,16 @@ __device__ inline f32x16_t mfma32x32x16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Value of `v` held by lane (lane ^ 32).
-__device__ inline float swap_halves(float v) { return __shfl_xor(v, 32); }
+// For every lane l: lo = v of lane l % 32, hi = v of lane l % 32 + 32.
+// v_permlane32_swap exchanges the upper 32 lanes of one register with the
+// lower 32 lanes of another in the VALU, so this needs no LDS round trip
+// (a ds_bpermute would queue behind other waves' LDS traffic).  The nops
+// cover the VALU-write -> permlane-read and permlane -> VALU-read hazards.
+__device__ inline void both_halves(float v, float& lo, float& hi) {
+    float a = v, b = v;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+    lo = a;   // [v_lo | v_lo]
+    hi = b;   // [v_hi | v_hi]
+}
 
 }  // namespace pca
