@@ -6,41 +6,96 @@
 // §4.1); the weight arrives pre-transposed to (N, K) so both operands are read
 // along K (§5.1).
 //
-// gfx950 design.  Workgroup tile 256 x 256 (M x N), K step 64, four waves in a
-// 2 x 2 grid, each wave a 128 x 128 sub-tile of 4 x 4 v_mfma_f32_32x32x16_bf16
-// blocks (256 fp32 accumulators per lane).  The wave computes the transposed
-// product (rows = n, columns = m), so each lane's accumulator holds 4
-// consecutive n of one m: the epilogue writes 8-byte runs of a y row.  Tiles
-// are staged in LDS with a 16-byte row pad (rows 144 B apart: 16 consecutive
-// rows start on 16 distinct 4-bank groups, so the 16-byte operand reads do not
-// conflict), double-buffered: the next K step's global loads are in flight in
-// registers while the current step runs on the matrix cores.  Ragged M, N and
-// K tails read zeros through buffer-resource range checks.
-//
-// Tile order: consecutive workgroup ids go round-robin to the 8 XCDs, so the
-// id is first remapped so that each XCD owns one contiguous range of tiles,
-// which is then walked in groups of 8 M-tiles: the tiles resident on one XCD
-// at a time share A rows and B columns in that XCD's L2.
+// gfx950 design.
+//  * Workgroup tile 256 x 256 (M x N), K step 64, four waves (one per SIMD),
+//    each a 128 x 128 sub-tile of 4 x 4 v_mfma_f32_32x32x16_bf16 blocks; the
+//    256 fp32 accumulators per lane live in AGPRs (one wave per SIMD gives
+//    each wave the whole 512-entry register file).  The wave computes the
+//    transposed product (MFMA rows = n, columns = m), so each lane's
+//    accumulator holds 4 consecutive n of one m: the epilogue writes 8-byte
+//    runs of a y row.
+//  * Operand tiles go from HBM/L2 straight into LDS with buffer_load ... lds
+//    (no register staging, no LDS stores), double-buffered: the tiles of K
+//    step kt + 2 are requested as soon as step kt's tiles are no longer read,
+//    so each load has a whole K step of matrix work to land.  Rows of 64
+//    elements (8 chunks of 16 bytes) are stored with chunk c of row r at
+//    c ^ ((r >> 1) & 7): the 16 rows a 16-lane group of a ds_read_b128 touches
+//    then cover all 64 banks once.
+//  * The 64 MFMAs of a K step run as one fixed sequence; the 8 operand reads
+//    of each 16-key step are issued one step ahead as inline asm and retired
+//    by explicit lgkmcnt waits, and scheduling barriers keep the order.
+//  * Ragged M, N read zeros through the buffer-resource range check, a ragged
+//    K tail through an out-of-range offset.
+//  * Tile order: consecutive workgroup ids go round-robin to the 8 XCDs, so
+//    the id is first remapped so that each XCD owns one contiguous range of
+//    tiles, which is then walked in groups of 8 M-tiles: the tiles resident on
+//    one XCD at a time share A rows and B columns in that XCD's L2.
 #include "pca_device.hpp"
 #include "pca_internal.hpp"
+
+#include <utility>
 
 namespace pca {
 
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 64;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
+
+constexpr int BM = 256, BN = 256, BKK = 64;
 constexpr int kThreads = 256;
-constexpr int WTM = 128, WTN = 128;           // wave tile (m, n)
-constexpr int FM = WTM / 32, FN = WTN / 32;   // 32x32 blocks per wave
-constexpr int ROW = BK + 8;                   // LDS row stride in elements (144 B)
-constexpr int A_ELEMS = BM * ROW;
-constexpr int B_ELEMS = BN * ROW;
-constexpr int STAGE = A_ELEMS + B_ELEMS;
-constexpr int CHUNKS_PER_ROW = BK / 8;        // 16-byte chunks per tile row
-constexpr int A_LOADS = BM * CHUNKS_PER_ROW / kThreads;   // 8
-constexpr int B_LOADS = BN * CHUNKS_PER_ROW / kThreads;   // 8
+constexpr int FN = 4, FM = 4;                 // 32x32 blocks per wave (n, m)
+constexpr int ROWB = BKK * 2;                 // 128 bytes per tile row
+constexpr int TILE_B = 256 * ROWB;            // 32 KiB: one operand tile
+constexpr int STAGE_B = 2 * TILE_B;           // W tile, then X tile
+constexpr int LDS_BYTES = 2 * STAGE_B;        // 128 KiB
+constexpr int DMA_PER_TILE = TILE_B / 1024;   // 32 one-KiB DMA blocks per operand tile
+constexpr int DMA_PER_WAVE = DMA_PER_TILE / 4;  // 8 per operand per wave
 constexpr int kGroupM = 8;
 constexpr uint32_t kOob = 0x80000000u;        // an offset past every buffer: loads return 0
+
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+__device__ inline int swz(int row) { return (row >> 1) & 7; }
+
+// s_waitcnt immediate waiting for vmcnt <= n only (gfx9 encoding: vmcnt in
+// bits [15:14] and [3:0]; expcnt 7 and lgkmcnt 15 mean "no wait")
+constexpr int vmcnt_imm(int n) { return ((n & 0x30) << 10) | (n & 0xF) | 0x0F70; }
+static_assert(vmcnt_imm(0) == 0x0F70 && vmcnt_imm(16) == 0x4F70, "s_waitcnt encoding");
+
+template <int OFF>
+__device__ __forceinline__ u32x4_t lds_read_b128(uint32_t addr) {
+    static_assert(OFF >= 0 && OFF < 65536, "DS offset field is 16 bits");
+    u32x4_t r;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+    return r;
+}
+
+// Wait until at most N LDS operations are outstanding (LDS returns in order);
+// the fragments pass through the asm so their consumers stay after the wait.
+template <int N>
+__device__ __forceinline__ void lds_wait8(u32x4_t (&f)[8]) {
+    asm volatile("s_waitcnt lgkmcnt(%8)"
+                 : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(f[4]), "+v"(f[5]), "+v"(f[6]), "+v"(f[7])
+                 : "n"(N));
+}
+
+// Workgroup barrier with no implied waits: the operand DMA of the next K step
+// stays in flight across it.  All LDS reads are inline asm retired by explicit
+// lgkmcnt waits, and the DMA by explicit vmcnt waits, before a barrier that
+// needs them; the memory clobber and scheduling barriers pin the order.
+__device__ __forceinline__ void wg_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
 
 __device__ inline void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
     int total = tiles_m * tiles_n;
@@ -55,58 +110,71 @@ __device__ inline void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
     tn = in_group / gsize;
 }
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const uint16_t* p, int64_t bytes) {
+    const uint64_t b = (uint64_t)p;
+    const uint64_t ub = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(b >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    return make_rsrc((const void*)ub, (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes));
+}
+
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void qkv_gemm_kernel(GemmArgs a) {
     extern __shared__ __align__(16) uint16_t smem[];
+    lds_char_t* lds = (lds_char_t*)smem;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave & 1, wn = wave >> 1;     // wave position in the 2 x 2 grid
+    const int r32 = lane & 31, half = lane >> 5;
 
-    int tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
+    const int tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
     int tm, tn;
     tile_coords(tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
+    const int rows_x = min(BM, a.M - m0), rows_w = min(BN, a.N - n0);
+    const int nk = (a.K + BKK - 1) / BKK;
 
-    // buffer views start at the tile's first row; rows past M (N) read 0
-    const int rows_a = min(BM, a.M - m0), rows_b = min(BN, a.N - n0);
-    __amdgpu_buffer_rsrc_t ra = make_rsrc(a.x + (int64_t)m0 * a.ldx, (uint32_t)((int64_t)(rows_a - 1) * a.ldx * 2 + (int64_t)a.K * 2));
-    __amdgpu_buffer_rsrc_t rb = make_rsrc(a.w + (int64_t)n0 * a.ldw, (uint32_t)((int64_t)(rows_b - 1) * a.ldw * 2 + (int64_t)a.K * 2));
-
-    // per-thread load coordinates: chunk id = i*256 + tid -> (row, chunk)
-    int ld_row[A_LOADS], ld_col[A_LOADS];
+    // DMA lane offsets (bytes from the tile's first row at the current K step):
+    // block b of a wave covers rows 8b .. 8b + 7; lane l writes physical chunk
+    // l % 8 of row 8b + l / 8, i.e. fetches logical chunk (l % 8) ^ swz(row).
+    uint32_t offx[DMA_PER_WAVE], offw[DMA_PER_WAVE];
+    int lchunk[DMA_PER_WAVE];
 #pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) {
-        int id = i * kThreads + tid;
-        ld_row[i] = id / CHUNKS_PER_ROW;
-        ld_col[i] = (id % CHUNKS_PER_ROW) * 8;
+    for (int i = 0; i < DMA_PER_WAVE; ++i) {
+        const int row = (wave * DMA_PER_WAVE + i) * 8 + lane / 8;
+        lchunk[i] = (lane % 8) ^ swz(row);
+        offx[i] = (uint32_t)(((int64_t)row * a.ldx + lchunk[i] * 8) * 2);
+        offw[i] = (uint32_t)(((int64_t)row * a.ldw + lchunk[i] * 8) * 2);
     }
+    auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
+        const int k0 = kt * BKK;
+        const bool tail = k0 + BKK > a.K;        // uniform: last step of a ragged K
+        const __amdgpu_buffer_rsrc_t rw =
+            uniform_rsrc(a.w + (int64_t)n0 * a.ldw + k0, (int64_t)rows_w * a.ldw * 2 - (int64_t)k0 * 2);
+        const __amdgpu_buffer_rsrc_t rx =
+            uniform_rsrc(a.x + (int64_t)m0 * a.ldx + k0, (int64_t)rows_x * a.ldx * 2 - (int64_t)k0 * 2);
+        lds_char_t* dst = lds + stage * STAGE_B;
+#pragma unroll
+        for (int i = 0; i < DMA_PER_WAVE; ++i) {
+            const int blk = wave * DMA_PER_WAVE + i;
+            const bool oob = tail && (k0 + lchunk[i] * 8 >= a.K);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void_t*)(dst + blk * 1024), 16,
+                                                     oob ? kOob : offw[i], 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(dst + TILE_B + blk * 1024), 16,
+                                                     oob ? kOob : offx[i], 0, 0, 0);
+        }
+    };
 
-    u32x4_t stage_a[A_LOADS], stage_b[B_LOADS];
-    auto global_load = [&](int k0) {
+    // operand read addresses: both operands read row (block*32 + r32), logical
+    // chunk ks*2 + half; the swizzle depends only on r32, so one address per
+    // (stage, ks) serves every block through the immediate offset
+    uint32_t waddr[4], xaddr[4];
 #pragma unroll
-        for (int i = 0; i < A_LOADS; ++i) {
-            int kk = k0 + ld_col[i];
-            uint32_t off = (ld_row[i] < rows_a && kk < a.K) ? (uint32_t)(((int64_t)ld_row[i] * a.ldx + kk) * 2) : kOob;
-            stage_a[i] = buf_load16(ra, off);
-        }
-#pragma unroll
-        for (int i = 0; i < B_LOADS; ++i) {
-            int kk = k0 + ld_col[i];
-            uint32_t off = (ld_row[i] < rows_b && kk < a.K) ? (uint32_t)(((int64_t)ld_row[i] * a.ldw + kk) * 2) : kOob;
-            stage_b[i] = buf_load16(rb, off);
-        }
-    };
-    auto lds_store = [&](int st) {
-        uint16_t* sa = smem + st * STAGE;
-        uint16_t* sb = sa + A_ELEMS;
-#pragma unroll
-        for (int i = 0; i < A_LOADS; ++i)
-            *reinterpret_cast<u32x4_t*>(sa + ld_row[i] * ROW + ld_col[i]) = stage_a[i];
-#pragma unroll
-        for (int i = 0; i < B_LOADS; ++i)
-            *reinterpret_cast<u32x4_t*>(sb + ld_row[i] * ROW + ld_col[i]) = stage_b[i];
-    };
+    for (int ks = 0; ks < 4; ++ks) {
+        const uint32_t base = (uint32_t)(uintptr_t)lds + r32 * ROWB + (((ks * 2 + half) ^ swz(r32)) * 16);
+        waddr[ks] = base + wn * 128 * ROWB;
+        xaddr[ks] = base + wm * 128 * ROWB;
+    }
 
     f32x16_t acc[FN][FM];
 #pragma unroll
@@ -116,34 +184,57 @@ void qkv_gemm_kernel(GemmArgs a) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    const int nk = (a.K + BK - 1) / BK;
-    global_load(0);
-    lds_store(0);
-    __syncthreads();
+    // 8 operand fragments of 16-key step ks: W blocks i (rows wn*128 + i*32),
+    // X blocks j (rows wm*128 + j*32)
+    auto read_step = [&](uint32_t soff, auto KSc, u32x4_t (&f)[8]) __attribute__((always_inline)) {
+        constexpr int ks = decltype(KSc)::value;
+        const uint32_t wa = waddr[ks] + soff, xa = xaddr[ks] + soff;
+        static_for<FN>([&](auto Ic) {
+            constexpr int i = decltype(Ic)::value;
+            f[i] = lds_read_b128<i * 32 * ROWB>(wa);
+        });
+        static_for<FM>([&](auto Jc) {
+            constexpr int j = decltype(Jc)::value;
+            f[FN + j] = lds_read_b128<TILE_B + j * 32 * ROWB>(xa);
+        });
+    };
+    auto mfmas = [&](const u32x4_t (&f)[8]) __attribute__((always_inline)) {
+        static_for<FN * FM>([&](auto Ic) {
+            constexpr int i = decltype(Ic)::value / FM, j = decltype(Ic)::value % FM;
+            acc[i][j] = mfma32x32x16(as_bf16x8(f[i]), as_bf16x8(f[FN + j]), acc[i][j]);
+        });
+        __builtin_amdgcn_sched_barrier(0);
+    };
 
-    const int r32 = lane & 31, half = lane >> 5;
+    // Software pipeline over K steps with two LDS stages and one barrier per
+    // step.  The operands of 16-key step ks + 1 are read while ks runs on the
+    // matrix cores.  The barrier of step kt sits after the wave's last LDS read
+    // of stage kt & 1 and before that step's last 16 MFMAs: past it, step
+    // kt + 1's tiles are visible (every wave waited for its own loads first)
+    // and stage kt & 1 is free, so the first operands of step kt + 1 are read
+    // and step kt + 2's tiles requested while those 16 MFMAs run.
+    issue(0, 0);
+    if (1 < nk) issue(1, 1);
+    if (1 < nk) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DMA_PER_WAVE));   // step 0 only
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    wg_barrier();
+    u32x4_t f[2][8];
+    read_step(0u, std::integral_constant<int, 0>{}, f[0]);
     for (int kt = 0; kt < nk; ++kt) {
         const int st = kt & 1;
-        if (kt + 1 < nk) global_load((kt + 1) * BK);
-        const uint16_t* sa = smem + st * STAGE;
-        const uint16_t* sb = sa + A_ELEMS;
-#pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            bf16x8_t fa[FM], fb[FN];
-#pragma unroll
-            for (int j = 0; j < FM; ++j)
-                fa[j] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(sa + (wm * WTM + j * 32 + r32) * ROW + ks * 16 + half * 8));
-#pragma unroll
-            for (int i = 0; i < FN; ++i)
-                fb[i] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(sb + (wn * WTN + i * 32 + r32) * ROW + ks * 16 + half * 8));
-            // transposed product: MFMA rows come from w (n), columns from x (m)
-#pragma unroll
-            for (int i = 0; i < FN; ++i)
-#pragma unroll
-                for (int j = 0; j < FM; ++j) acc[i][j] = mfma32x32x16(fb[i], fa[j], acc[i][j]);
-        }
-        if (kt + 1 < nk) lds_store(st ^ 1);
-        __syncthreads();
+        const uint32_t soff = (uint32_t)(st * STAGE_B);
+        static_for<3>([&](auto KSc) {
+            constexpr int ks = decltype(KSc)::value;
+            read_step(soff, std::integral_constant<int, ks + 1>{}, f[(ks + 1) & 1]);
+            lds_wait8<8>(f[ks & 1]);
+            mfmas(f[ks & 1]);
+        });
+        lds_wait8<0>(f[1]);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // this wave's loads of step kt + 1
+        wg_barrier();
+        if (kt + 1 < nk) read_step(soff ^ (uint32_t)STAGE_B, std::integral_constant<int, 0>{}, f[0]);
+        if (kt + 2 < nk) issue(kt + 2, st);
+        mfmas(f[1]);
     }
 
     // epilogue: lane holds, per block, column m = r32 and rows n = g*8 + half*4 + 0..3
@@ -151,11 +242,11 @@ void qkv_gemm_kernel(GemmArgs a) {
     for (int i = 0; i < FN; ++i) {
 #pragma unroll
         for (int j = 0; j < FM; ++j) {
-            const int m = m0 + wm * WTM + j * 32 + r32;
+            const int m = m0 + wm * 128 + j * 32 + r32;
             if (m >= a.M) continue;
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int n = n0 + wn * WTN + i * 32 + g * 8 + half * 4;
+                const int n = n0 + wn * 128 + i * 32 + g * 8 + half * 4;
                 uint16_t* dst = a.y + (int64_t)m * a.ldy + n;
                 if (n + 3 < a.N) {
                     u32x2_t w2 = {pack_bf16x2(acc[i][j][g * 4 + 0], acc[i][j][g * 4 + 1]),
@@ -174,16 +265,11 @@ void qkv_gemm_kernel(GemmArgs a) {
 }  // namespace
 
 hipError_t launch_qkv_gemm(const GemmArgs& a, hipStream_t s) {
-    static bool configured = false;
-    const size_t lds = 2 * STAGE * sizeof(uint16_t);
-    if (!configured) {
-        hipError_t e = hipFuncSetAttribute((const void*)qkv_gemm_kernel,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        configured = true;
-    }
-    int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-    hipLaunchKernelGGL(qkv_gemm_kernel, dim3(tiles), dim3(kThreads), lds, s, a);
+    static const hipError_t attr = hipFuncSetAttribute((const void*)qkv_gemm_kernel,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+    if (attr != hipSuccess) return attr;
+    const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+    hipLaunchKernelGGL(qkv_gemm_kernel, dim3(tiles), dim3(kThreads), LDS_BYTES, s, a);
     return hipGetLastError();
 }
 
