@@ -45,12 +45,14 @@
 //    to the B operand (within 16 keys: 0-3, 8-11 | 4-7, 12-15).
 //  * Q stays in registers (B operand of S^T) for the whole kv loop; the O^T
 //    accumulator (fp32) likewise.
-//  * exp is exp2 with scale*log2(e) folded into one FMA; m, l, P in fp32,
-//    P rounded to bf16 only as the MFMA operand.  The reference max of a row
-//    moves only when the row's scores exceed it by 2^8 (see below); the new
-//    reference is a per-lane select, so the exponentials need no branch, and
-//    only the rescale of O and l sits behind one -- taken on the first tile
-//    and rarely after.
+//  * scale*log2(e) is folded into Q once (before its bf16 rounding), and
+//    each score chain starts from the accumulator value -R, R the row's
+//    reference max in log2 units: the MFMA hands over s*c - R and the
+//    softmax of a tile is one exp2 and one add per score, plus the packing
+//    of P to bf16 (m, l, P in fp32; P rounded to bf16 only as the MFMA
+//    operand).  A row moves R up to its tile max only on the wave's first
+//    tile and when its tile sum of p passes 2^12; only then are the max, the
+//    rescale of O and l and the -R accumulator refreshed, behind one branch.
 //  * The causal rule: a wave skips kv tiles that start after its last query,
 //    and masks per element only on tiles that reach past its first query.
 //    Workgroups are ordered heaviest-first, and units (sequence, kv head) go
@@ -73,7 +75,7 @@ constexpr int kWaves = 8;               // per workgroup; waves w and w + 4 shar
 constexpr int kThreads = kWaves * 64;
 constexpr int BQ = 32;                  // query rows per wave
 constexpr int BK = 64;                  // keys per kv tile
-constexpr float kRescaleLog2 = 8.0f;    // lazy max update threshold (p stays <= 256)
+constexpr float kSumLimit = 4096.0f;    // a row's reference moves when its tile sum of p exceeds this
 constexpr int kVmcnt0 = 0x0F70;         // s_waitcnt vmcnt(0), other counters unconstrained
 
 template <int HD>
@@ -270,7 +272,13 @@ void attn_fwd_kernel(Params p) {
 #pragma unroll
         for (int dc = 0; dc < C::DCH; ++dc) {
             const uint32_t off = (uint32_t)(((int64_t)(q0 + r32) * p.ldq + head * HD + dc * 16 + half * 8) * 2);
-            qreg[dc] = as_bf16x8(buf_load16(rq, off));
+            // scale * log2(e) folded into Q once (then rounded to bf16), so the
+            // scores come out of the MFMA in log2 units
+            const u32x4_t raw = buf_load16(rq, off);
+            u32x4_t qs;
+#pragma unroll
+            for (int t2 = 0; t2 < 4; ++t2) qs[t2] = pack_bf16x2(bf16_lo(raw[t2]) * p.c, bf16_hi(raw[t2]) * p.c);
+            qreg[dc] = as_bf16x8(qs);
         }
     }
 
@@ -315,8 +323,10 @@ void attn_fwd_kernel(Params p) {
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[db][e] = 0.0f;
-    float m_run = -1.0e30f, l_run = 0.0f;
-    const float c = p.c;
+    // Per row (lane): reference R in log2 units; every score chain starts from
+    // the accumulator sinit = -R, so the MFMA hands over s * c - R directly.
+    float R = 0.0f, l_run = 0.0f;
+    f32x16_t sinit = {};
     f32x16_t s[2];          // scores of the tile whose softmax is next
     bf16x8_t pb[2][2];      // P of the tile whose P V product is next
 
@@ -361,7 +371,7 @@ void attn_fwd_kernel(Params p) {
                 constexpr int m = i - NPV, dc = m / 2, kb = m % 2;
                 lds_wait<n>(kf[m]);
                 // the first head_dim step starts from a zero accumulator
-                s[kb] = mfma32x32x16(as_bf16x8(kf[m]), qreg[dc], dc == 0 ? f32x16_t{} : s[kb]);
+                s[kb] = mfma32x32x16(as_bf16x8(kf[m]), qreg[dc], dc == 0 ? sinit : s[kb]);
             }
             if constexpr (i + LA < NM) issue(std::integral_constant<int, i + LA>{});
             __builtin_amdgcn_sched_barrier(0);
@@ -376,7 +386,7 @@ void attn_fwd_kernel(Params p) {
             constexpr int m = decltype(Mc)::value, dc = m / 2, kb = m % 2;
             u32x4_t k = lds_read_b128<KB + kb * 32 * C::ROWB>(kaddr[dc]);
             lds_wait<0>(k);
-            s[kb] = mfma32x32x16(as_bf16x8(k), qreg[dc], dc == 0 ? f32x16_t{} : s[kb]);
+            s[kb] = mfma32x32x16(as_bf16x8(k), qreg[dc], dc == 0 ? sinit : s[kb]);
         });
     };
 
@@ -396,51 +406,60 @@ void attn_fwd_kernel(Params p) {
                 }
         }
         // Online softmax, one query per lane (its 64 keys split with lane ^ 32).
-        // A row's reference max only moves when the row's tile max exceeds it by
-        // more than kRescaleLog2 (log2 units): the result does not depend on the
-        // reference (it cancels in O / l) and p stays <= 2^kRescaleLog2.  Only
-        // rows past the threshold move, so a row's arithmetic depends on its own
-        // scores alone.
-        float mx = s[0][0];
+        // The scores already hold s * c - R, so the common case is one exp2 and
+        // one add per score (p in fp32 for the row sum, rounded to bf16 for
+        // the MFMA).  A row moves its reference R up to its tile max on the
+        // wave's first tile and when its tile sum of p exceeds kSumLimit; the
+        // fast path stays only while every lane's half-row sum is at most
+        // kSumLimit / 2, which bounds every p by kSumLimit.  The result does
+        // not depend on R (it cancels in O / l), and a row's arithmetic depends
+        // on its own scores alone.
+        float rs;
+        auto exps = [&](float d) __attribute__((always_inline)) {
+            rs = 0.0f;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) mx = __builtin_fmaxf(mx, s[kb][e]);
-        {
+                for (int h = 0; h < 2; ++h) {
+                    u32x4_t w;
+#pragma unroll
+                    for (int t2 = 0; t2 < 4; ++t2) {
+                        const float e0 = fast_exp2(s[kb][h * 8 + 2 * t2] - d);
+                        const float e1 = fast_exp2(s[kb][h * 8 + 2 * t2 + 1] - d);
+                        w[t2] = pack_bf16x2(e0, e1);
+                        rs += e0;
+                        rs += e1;
+                    }
+                    pb[kb][h] = as_bf16x8(w);
+                }
+        };
+        exps(0.0f);
+        if (t == 0 || __builtin_amdgcn_ballot_w64(rs > 0.5f * kSumLimit) != 0) {
+            float rlo, rhi;
+            both_halves(rs, rlo, rhi);
+            const bool move = t == 0 || rlo + rhi > kSumLimit;
+            // rare: moving rows take their tile max as the new reference,
+            // recompute p and rescale O and l (non-moving rows: d = 0, alpha = 1,
+            // the same p as above)
+            float mx = s[0][0];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) mx = __builtin_fmaxf(mx, s[kb][e]);
             float lo, hi;
             both_halves(mx, lo, hi);
-            mx = __builtin_fmaxf(lo, hi);
-        }
-        const bool move = (mx - m_run) * c > kRescaleLog2;
-        const float m_ref = move ? mx : m_run;
-        const float mc = m_ref * c;
-        float rs = 0.0f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const float pe = fast_exp2(__builtin_fmaf(s[kb][e], c, -mc));
-                s[kb][e] = pe;
-                rs += pe;
-            }
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                u32x4_t w;
-#pragma unroll
-                for (int t2 = 0; t2 < 4; ++t2) w[t2] = pack_bf16x2(s[kb][h * 8 + 2 * t2], s[kb][h * 8 + 2 * t2 + 1]);
-                pb[kb][h] = as_bf16x8(w);
-            }
-        if (__builtin_amdgcn_ballot_w64(move) != 0) {
-            // rare: rows past the threshold move their reference; rescale their O and l
-            const float alpha = fast_exp2((m_run - m_ref) * c);
-            m_run = m_ref;
+            const float d = move ? __builtin_fmaxf(lo, hi) : 0.0f;
+            exps(d);
+            // d > 0 for a row past the limit; on the first tile O and l are 0
+            const float alpha = __builtin_fminf(fast_exp2(-d), 1.0f);
             l_run *= alpha;
 #pragma unroll
             for (int db = 0; db < C::DB; ++db)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+            R += d;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) sinit[e] = -R;
         }
         l_run += rs;
     };
