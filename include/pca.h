@@ -104,6 +104,35 @@ pca_status pca_qkv_proj(const pca_bf16* x, int64_t ldx, const pca_bf16* w_t, int
                         void* stream);
 
 /*
+ * pca_qkv_proj_kv_write -- pca_qkv_proj with the KV-cache write done by the
+ *   GEMM's epilogue.  The data-flow article's §4.2 notes that the projection
+ *   output can be scattered into its cache blocks by the kernel that produces
+ *   it, and that a separate copy pass is waste: here the GEMM tiles that
+ *   produce K and V columns also store them into their page slots, so the
+ *   separate pass (which re-reads K and V from y) disappears.
+ *   Result: y as from pca_qkv_proj (bit for bit), with
+ *        N = (n_head + 2 n_kv_head) * head_dim and the [Q | K | V] column
+ *        order of pca_kv_layout; and the pools (and fp8 scales) exactly as
+ *        pca_kv_cache_write would leave them for k = y + k_off, v = y + v_off
+ *        (row stride ldy), total_tokens = M.
+ *   x, w_t, y, M, K: as for pca_qkv_proj.
+ *   cu_seqlens, num_seqs, block_table, max_pages_per_seq, page_size,
+ *   cache_dtype, k_cache, v_cache, k_scale, v_scale, num_pages: as for
+ *        pca_kv_cache_write (tokens are the M rows of y).
+ *   n_head, n_kv_head: > 0, n_head a multiple of n_kv_head; head_dim 32, 64
+ *        or 128.  For an fp8 cache, n_head*head_dim and n_kv_head*head_dim
+ *        must be multiples of 128 (else PCA_ERR_UNSUPPORTED): each 128-column
+ *        slab of a GEMM tile then holds whole heads of one of K or V.
+ */
+pca_status pca_qkv_proj_kv_write(const pca_bf16* x, int64_t ldx, const pca_bf16* w_t, int64_t ldw,
+                                 pca_bf16* y, int64_t ldy, int64_t M, int64_t K,
+                                 int n_head, int n_kv_head, int head_dim,
+                                 const int32_t* cu_seqlens, int num_seqs,
+                                 const int32_t* block_table, int max_pages_per_seq, int page_size,
+                                 pca_dtype cache_dtype, void* k_cache, void* v_cache,
+                                 float* k_scale, float* v_scale, int64_t num_pages, void* stream);
+
+/*
  * pca_prefill_attention -- causal GQA attention over packed sequences.
  *   For sequence b, query head i (kv head g = i / (n_head / n_kv_head)) and
  *   position r:  o[r, i] = sum_{c <= r} softmax_c(q[r, i] . k[c, g] * scale) v[c, g]

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(PKG, "libpca.so")
 PCA_OK, PCA_ERR_INVALID_ARG, PCA_ERR_UNSUPPORTED, PCA_ERR_HIP = 0, 1, 2, 3
 DTYPES = {"bf16": 0, "fp8_e4m3": 1}
 
-EXPORTED = ("pca_kv_layout", "pca_qkv_proj", "pca_prefill_attention", "pca_kv_cache_write",
+EXPORTED = ("pca_kv_layout", "pca_qkv_proj", "pca_qkv_proj_kv_write", "pca_prefill_attention", "pca_kv_cache_write",
             "pca_last_error", "pca_version")
 
 
@@ -55,7 +55,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                           f32, i32, vp, i64, vp]
     lib.pca_kv_cache_write.argtypes = [vp, vp, i64, i64, vp, i32, i64, vp, i32, i32, i32, i32, i32,
                                        vp, vp, vp, vp, i64, vp]
-    for fn in ("pca_kv_layout", "pca_qkv_proj", "pca_prefill_attention", "pca_kv_cache_write"):
+    lib.pca_qkv_proj_kv_write.argtypes = [vp, i64, vp, i64, vp, i64, i64, i64, i32, i32, i32, vp, i32,
+                                          vp, i32, i32, i32, vp, vp, vp, vp, i64, vp]
+    for fn in ("pca_kv_layout", "pca_qkv_proj", "pca_prefill_attention", "pca_kv_cache_write",
+               "pca_qkv_proj_kv_write"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.pca_last_error.restype = ctypes.c_char_p
     lib.pca_last_error.argtypes = []
@@ -110,6 +113,30 @@ def qkv_proj(x, w_t, y, stream=None):
     if w_t.shape[1] != K or tuple(y.shape) != (M, N):
         raise ValueError(f"shape mismatch: x {tuple(x.shape)}, w_t {tuple(w_t.shape)}, y {tuple(y.shape)}")
     _check("pca_qkv_proj", load().pca_qkv_proj(px, ldx, pw, ldw, py, ldy, M, N, K, _stream(stream)))
+    return y
+
+
+def qkv_proj_kv_write(x, w_t, y, block_table, k_cache, v_cache, n_head: int, n_kv_head: int, head_dim: int,
+                      cu_seqlens=None, cache_dtype: str = "bf16", k_scale=None, v_scale=None,
+                      page_size: int = 16, stream=None):
+    """qkv_proj with the KV-cache write in the GEMM epilogue: y as from
+    qkv_proj, pools as from kv_cache_write of y's K and V columns."""
+    px, ldx = _rows(x, "x")
+    pw, ldw = _rows(w_t, "w_t")
+    py, ldy = _rows(y, "y")
+    M, K = x.shape
+    N = (n_head + 2 * n_kv_head) * head_dim
+    if tuple(w_t.shape) != (N, K) or tuple(y.shape) != (M, N):
+        raise ValueError(f"shape mismatch: x {tuple(x.shape)}, w_t {tuple(w_t.shape)}, y {tuple(y.shape)}, N={N}")
+    num_seqs = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be 2-D [num_seqs, max_pages_per_seq]")
+    elem = 2 if cache_dtype == "bf16" else 1
+    num_pages = k_cache.numel() * k_cache.element_size() // (page_size * n_kv_head * head_dim * elem)
+    _check("pca_qkv_proj_kv_write", load().pca_qkv_proj_kv_write(
+        px, ldx, pw, ldw, py, ldy, M, K, n_head, n_kv_head, head_dim, _ptr(cu_seqlens), num_seqs,
+        block_table.data_ptr(), block_table.shape[1], page_size, DTYPES[cache_dtype],
+        k_cache.data_ptr(), v_cache.data_ptr(), _ptr(k_scale), _ptr(v_scale), num_pages, _stream(stream)))
     return y
 
 

@@ -16,8 +16,7 @@
 // loads first, resolves the page slot of the few tokens it touches into LDS
 // while they are in flight, then stores.  Loads and stores are non-temporal:
 // the data is touched once.
-#include "pca_device.hpp"
-#include "pca_internal.hpp"
+#include "kv_common.hpp"
 
 namespace pca {
 
@@ -26,36 +25,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kItems = 4;
 constexpr int kChunksPerBlock = kThreads * kItems;
-
-// Largest b with cu[b] <= t (cu = null: single sequence).
-__device__ inline int find_seq(const int32_t* cu, int num_seqs, int64_t t) {
-    int lo = 0, hi = num_seqs - 1;
-    while (lo < hi) {
-        int mid = (lo + hi + 1) >> 1;
-        if ((int64_t)cu[mid] <= t) lo = mid; else hi = mid - 1;
-    }
-    return lo;
-}
-
-// Slot index (page * page_size + slot) of token t, or -1 if the token maps to
-// no valid slot (outside every sequence, past the block table, or a page
-// number outside [0, num_pages)).
-__device__ inline int64_t token_slot(const KvWriteArgs& a, int64_t t) {
-    int b = 0;
-    int64_t start = 0, end = a.total_tokens;
-    if (a.cu_seqlens != nullptr) {
-        b = find_seq(a.cu_seqlens, a.num_seqs, t);
-        start = a.cu_seqlens[b];
-        end = a.cu_seqlens[b + 1];
-    }
-    if (t < start || t >= end) return -1;
-    int64_t pos = t - start;
-    int64_t pidx = pos / a.page_size;
-    if (pidx >= a.max_pages_per_seq) return -1;
-    int32_t page = a.block_table[(int64_t)b * a.max_pages_per_seq + pidx];
-    if (page < 0 || (int64_t)page >= a.num_pages) return -1;
-    return (int64_t)page * a.page_size + (pos % a.page_size);
-}
 
 // Resolve the slots of tokens [first, first + ntok) into LDS.
 __device__ inline void resolve_slots(const KvWriteArgs& a, int64_t first, int ntok, int64_t* slots) {
@@ -103,37 +72,6 @@ __global__ __launch_bounds__(kThreads) void kv_write_bf16_kernel(KvWriteArgs a) 
         uint16_t* pool = isv[i] ? (uint16_t*)a.v_cache : (uint16_t*)a.k_cache;
         __builtin_nontemporal_store(val[i], reinterpret_cast<u32x4_t*>(pool + (slot * (int64_t)C + cc[i]) * 8));
     }
-}
-
-// OCP E4M3 encoding of a binary32 value, round to nearest even, finite
-// overflow saturating to +-448; the sign bit is copied from y.  Branch-free:
-// below 2^-6 the code is the subnormal count rint(|y| * 2^9) (exact scaling,
-// ties to even); from there the 3 kept mantissa bits are rounded to nearest
-// even in the integer domain and the exponent rebiased from 127 to 7.
-__device__ inline uint32_t e4m3_rne_sat(float y) {
-    const uint32_t u = __builtin_bit_cast(uint32_t, y);
-    const uint32_t sign = (u >> 24) & 0x80u;
-    const float a = __builtin_fabsf(y);
-    const uint32_t ua = u & 0x7FFFFFFFu;
-    const uint32_t sub = (uint32_t)__builtin_rintf(a * 512.0f);
-    const uint32_t nrm = ((ua + 0x7FFFFu + ((ua >> 20) & 1u)) >> 20) - (120u << 3);
-    uint32_t code = a < 0.015625f ? sub : nrm;
-    code = (a >= 448.0f || code > 0x7Eu) ? 0x7Eu : code;
-    return sign | code;
-}
-
-// max over the R-lane group (R = 4, 8 or 16, aligned) holding one (token, kv
-// head) row, with DPP lane permutes inside 16-lane rows: swap neighbours, swap
-// pairs, mirror halves of 8, mirror the 16
-template <int R>
-__device__ inline float group_max(float v) {
-    v = __builtin_fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
-    v = __builtin_fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));
-    if constexpr (R >= 8)
-        v = __builtin_fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false)));
-    if constexpr (R >= 16)
-        v = __builtin_fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false)));
-    return v;
 }
 
 template <int R>

@@ -47,6 +47,58 @@ pca_status check_batch(const int32_t* cu, int num_seqs, int64_t total_tokens) {
     return PCA_OK;
 }
 
+// Shape checks of a GEMM call; fills the GEMM part of `a` (no fused write).
+pca_status check_gemm(const pca_bf16* x, int64_t ldx, const pca_bf16* w_t, int64_t ldw, pca_bf16* y, int64_t ldy,
+                      int64_t M, int64_t N, int64_t K, pca::GemmArgs& a) {
+    if (!x || !w_t || !y) return fail(PCA_ERR_INVALID_ARG, "null pointer (x=%p w_t=%p y=%p)", x, w_t, y);
+    if (!aligned16(x) || !aligned16(w_t) || !aligned16(y))
+        return fail(PCA_ERR_INVALID_ARG, "x, w_t and y must be 16-byte aligned");
+    if (M < 1 || N < 1 || K < 8 || K % 8 != 0)
+        return fail(PCA_ERR_INVALID_ARG, "need M >= 1, N >= 1, K >= 8 and K %% 8 == 0 (M=%lld N=%lld K=%lld)",
+                    (long long)M, (long long)N, (long long)K);
+    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX)
+        return fail(PCA_ERR_INVALID_ARG, "M, N, K must fit in int32");
+    if (ldx < K || ldw < K || ldy < N || ldx % 8 || ldw % 8 || ldy % 8)
+        return fail(PCA_ERR_INVALID_ARG, "leading dimensions must be >= the row width and multiples of 8 "
+                    "(ldx=%lld ldw=%lld ldy=%lld)", (long long)ldx, (long long)ldw, (long long)ldy);
+    if (256 * ldx * 2 >= kMaxBufferBytes || 256 * ldw * 2 >= kMaxBufferBytes)
+        return fail(PCA_ERR_UNSUPPORTED, "row stride too large for a 256-row tile view");
+    memset(&a, 0, sizeof(a));
+    a.x = x; a.ldx = ldx; a.w = w_t; a.ldw = ldw; a.y = y; a.ldy = ldy;
+    a.M = (int)M; a.N = (int)N; a.K = (int)K;
+    a.kv_mode = 0;
+    return PCA_OK;
+}
+
+// Checks of the page-pool side of a KV-cache write (shared by the separate
+// and the fused write).
+pca_status check_kv_cache(const int32_t* cu_seqlens, int num_seqs, int64_t total_tokens,
+                          const int32_t* block_table, int max_pages_per_seq, int n_kv_head, int head_dim,
+                          int page_size, pca_dtype cache_dtype, void* k_cache, void* v_cache,
+                          float* k_scale, float* v_scale, int64_t num_pages) {
+    if (!block_table || !k_cache || !v_cache) return fail(PCA_ERR_INVALID_ARG, "null block_table, k_cache or v_cache");
+    if (!aligned16(k_cache) || !aligned16(v_cache))
+        return fail(PCA_ERR_INVALID_ARG, "k_cache and v_cache must be 16-byte aligned");
+    if ((uintptr_t)block_table & 3u) return fail(PCA_ERR_INVALID_ARG, "block_table must be 4-byte aligned");
+    if (page_size != 16) return fail(PCA_ERR_UNSUPPORTED, "page_size must be 16 (got %d)", page_size);
+    pca_status st = check_batch(cu_seqlens, num_seqs, total_tokens);
+    if (st != PCA_OK) return st;
+    if (max_pages_per_seq < 1 || num_pages < 1)
+        return fail(PCA_ERR_INVALID_ARG, "max_pages_per_seq and num_pages must be >= 1");
+    if (cache_dtype == PCA_DTYPE_BF16) {
+        if (k_scale || v_scale) return fail(PCA_ERR_INVALID_ARG, "k_scale/v_scale must be NULL for a bf16 cache");
+    } else if (cache_dtype == PCA_DTYPE_FP8_E4M3) {
+        if (!k_scale || !v_scale) return fail(PCA_ERR_INVALID_ARG, "fp8 cache needs k_scale and v_scale");
+        if (((uintptr_t)k_scale & 3u) || ((uintptr_t)v_scale & 3u))
+            return fail(PCA_ERR_INVALID_ARG, "k_scale/v_scale must be 4-byte aligned");
+    } else {
+        return fail(PCA_ERR_UNSUPPORTED, "unknown cache dtype %d", (int)cache_dtype);
+    }
+    if (total_tokens * 2 * ((int64_t)n_kv_head * head_dim / 8) >= (int64_t(1) << 31))
+        return fail(PCA_ERR_UNSUPPORTED, "batch too large (total_tokens * n_kv_head * head_dim)");
+    return PCA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -93,23 +145,45 @@ pca_status pca_kv_layout(int n_head, int n_kv_head, int head_dim, int page_size,
 
 pca_status pca_qkv_proj(const pca_bf16* x, int64_t ldx, const pca_bf16* w_t, int64_t ldw,
                         pca_bf16* y, int64_t ldy, int64_t M, int64_t N, int64_t K, void* stream) {
-    if (!x || !w_t || !y) return fail(PCA_ERR_INVALID_ARG, "null pointer (x=%p w_t=%p y=%p)", x, w_t, y);
-    if (!aligned16(x) || !aligned16(w_t) || !aligned16(y))
-        return fail(PCA_ERR_INVALID_ARG, "x, w_t and y must be 16-byte aligned");
-    if (M < 1 || N < 1 || K < 8 || K % 8 != 0)
-        return fail(PCA_ERR_INVALID_ARG, "need M >= 1, N >= 1, K >= 8 and K %% 8 == 0 (M=%lld N=%lld K=%lld)",
-                    (long long)M, (long long)N, (long long)K);
-    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX)
-        return fail(PCA_ERR_INVALID_ARG, "M, N, K must fit in int32");
-    if (ldx < K || ldw < K || ldy < N || ldx % 8 || ldw % 8 || ldy % 8)
-        return fail(PCA_ERR_INVALID_ARG, "leading dimensions must be >= the row width and multiples of 8 "
-                    "(ldx=%lld ldw=%lld ldy=%lld)", (long long)ldx, (long long)ldw, (long long)ldy);
-    if (256 * ldx * 2 >= kMaxBufferBytes || 256 * ldw * 2 >= kMaxBufferBytes)
-        return fail(PCA_ERR_UNSUPPORTED, "row stride too large for a 256-row tile view");
     pca::GemmArgs a;
-    a.x = x; a.ldx = ldx; a.w = w_t; a.ldw = ldw; a.y = y; a.ldy = ldy;
-    a.M = (int)M; a.N = (int)N; a.K = (int)K;
+    pca_status st = check_gemm(x, ldx, w_t, ldw, y, ldy, M, N, K, a);
+    if (st != PCA_OK) return st;
     return hip_status(pca::launch_qkv_gemm(a, (hipStream_t)stream), "qkv_proj launch");
+}
+
+pca_status pca_qkv_proj_kv_write(const pca_bf16* x, int64_t ldx, const pca_bf16* w_t, int64_t ldw,
+                                 pca_bf16* y, int64_t ldy, int64_t M, int64_t K,
+                                 int n_head, int n_kv_head, int head_dim,
+                                 const int32_t* cu_seqlens, int num_seqs,
+                                 const int32_t* block_table, int max_pages_per_seq, int page_size,
+                                 pca_dtype cache_dtype, void* k_cache, void* v_cache,
+                                 float* k_scale, float* v_scale, int64_t num_pages, void* stream) {
+    if (n_head <= 0 || n_kv_head <= 0 || n_head % n_kv_head != 0)
+        return fail(PCA_ERR_INVALID_ARG, "need n_head, n_kv_head > 0 and n_head %% n_kv_head == 0 (%d, %d)",
+                    n_head, n_kv_head);
+    if (!supported_head_dim(head_dim))
+        return fail(PCA_ERR_UNSUPPORTED, "head_dim %d not supported (32, 64 or 128)", head_dim);
+    const int64_t N = ((int64_t)n_head + 2 * (int64_t)n_kv_head) * head_dim;
+    pca::GemmArgs a;
+    pca_status st = check_gemm(x, ldx, w_t, ldw, y, ldy, M, N, K, a);
+    if (st != PCA_OK) return st;
+    st = check_kv_cache(cu_seqlens, num_seqs, M, block_table, max_pages_per_seq, n_kv_head, head_dim,
+                        page_size, cache_dtype, k_cache, v_cache, k_scale, v_scale, num_pages);
+    if (st != PCA_OK) return st;
+    const int64_t nkc = (int64_t)n_kv_head * head_dim;
+    if (cache_dtype == PCA_DTYPE_FP8_E4M3 && (((int64_t)n_head * head_dim) % 128 != 0 || nkc % 128 != 0))
+        return fail(PCA_ERR_UNSUPPORTED, "fused fp8 write needs n_head*head_dim and n_kv_head*head_dim to be "
+                    "multiples of 128 (got %d*%d, %d*%d)", n_head, head_dim, n_kv_head, head_dim);
+    a.kv_mode = cache_dtype == PCA_DTYPE_BF16 ? 1 : 2;
+    a.k_col0 = n_head * head_dim;
+    a.v_col0 = (int)(a.k_col0 + nkc);
+    a.kv.k = nullptr; a.kv.v = nullptr; a.kv.ldk = 0; a.kv.ldv = 0;
+    a.kv.cu_seqlens = cu_seqlens; a.kv.num_seqs = num_seqs; a.kv.total_tokens = M;
+    a.kv.block_table = block_table; a.kv.max_pages_per_seq = max_pages_per_seq;
+    a.kv.n_kv_head = n_kv_head; a.kv.head_dim = head_dim; a.kv.page_size = page_size;
+    a.kv.k_cache = k_cache; a.kv.v_cache = v_cache; a.kv.k_scale = k_scale; a.kv.v_scale = v_scale;
+    a.kv.num_pages = num_pages;
+    return hip_status(pca::launch_qkv_gemm(a, (hipStream_t)stream), "qkv_proj_kv_write launch");
 }
 
 pca_status pca_prefill_attention(const pca_bf16* q, const pca_bf16* k, const pca_bf16* v,
@@ -158,32 +232,16 @@ pca_status pca_kv_cache_write(const pca_bf16* k, const pca_bf16* v, int64_t ldk,
                               void* k_cache, void* v_cache, float* k_scale, float* v_scale,
                               int64_t num_pages, void* stream) {
     if (total_tokens == 0 && num_seqs >= 1) return ok();   // empty batch: nothing to read or write
-    if (!k || !v || !block_table || !k_cache || !v_cache)
-        return fail(PCA_ERR_INVALID_ARG, "null k, v, block_table, k_cache or v_cache");
-    if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
-        return fail(PCA_ERR_INVALID_ARG, "k, v, k_cache and v_cache must be 16-byte aligned");
-    if ((uintptr_t)block_table & 3u) return fail(PCA_ERR_INVALID_ARG, "block_table must be 4-byte aligned");
+    if (!k || !v) return fail(PCA_ERR_INVALID_ARG, "null k or v");
+    if (!aligned16(k) || !aligned16(v)) return fail(PCA_ERR_INVALID_ARG, "k and v must be 16-byte aligned");
     if (n_kv_head <= 0) return fail(PCA_ERR_INVALID_ARG, "n_kv_head must be > 0");
     if (!supported_head_dim(head_dim))
         return fail(PCA_ERR_UNSUPPORTED, "head_dim %d not supported (32, 64 or 128)", head_dim);
-    if (page_size != 16) return fail(PCA_ERR_UNSUPPORTED, "page_size must be 16 (got %d)", page_size);
-    pca_status st = check_batch(cu_seqlens, num_seqs, total_tokens);
-    if (st != PCA_OK) return st;
-    if (max_pages_per_seq < 1 || num_pages < 1)
-        return fail(PCA_ERR_INVALID_ARG, "max_pages_per_seq and num_pages must be >= 1");
     if (ldk < (int64_t)n_kv_head * head_dim || ldv < (int64_t)n_kv_head * head_dim || ldk % 8 || ldv % 8)
         return fail(PCA_ERR_INVALID_ARG, "ldk/ldv must cover n_kv_head*head_dim and be multiples of 8");
-    if (cache_dtype == PCA_DTYPE_BF16) {
-        if (k_scale || v_scale) return fail(PCA_ERR_INVALID_ARG, "k_scale/v_scale must be NULL for a bf16 cache");
-    } else if (cache_dtype == PCA_DTYPE_FP8_E4M3) {
-        if (!k_scale || !v_scale) return fail(PCA_ERR_INVALID_ARG, "fp8 cache needs k_scale and v_scale");
-        if (((uintptr_t)k_scale & 3u) || ((uintptr_t)v_scale & 3u))
-            return fail(PCA_ERR_INVALID_ARG, "k_scale/v_scale must be 4-byte aligned");
-    } else {
-        return fail(PCA_ERR_UNSUPPORTED, "unknown cache dtype %d", (int)cache_dtype);
-    }
-    if (total_tokens * 2 * ((int64_t)n_kv_head * head_dim / 8) >= (int64_t(1) << 31))
-        return fail(PCA_ERR_UNSUPPORTED, "batch too large (total_tokens * n_kv_head * head_dim)");
+    pca_status st = check_kv_cache(cu_seqlens, num_seqs, total_tokens, block_table, max_pages_per_seq, n_kv_head,
+                                   head_dim, page_size, cache_dtype, k_cache, v_cache, k_scale, v_scale, num_pages);
+    if (st != PCA_OK) return st;
     if (total_tokens == 0) return ok();
     pca::KvWriteArgs a;
     a.k = k; a.v = v; a.ldk = ldk; a.ldv = ldv;

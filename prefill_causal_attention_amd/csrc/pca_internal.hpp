@@ -35,6 +35,10 @@ struct GemmArgs {
     uint16_t* y;
     int64_t ldy;
     int M, N, K;
+    // optional KV-cache write of y's K and V columns from the epilogue
+    int kv_mode;          // 0: none, 1: bf16 cache, 2: fp8 E4M3 cache
+    int k_col0, v_col0;   // first K / V column of y; each range is n_kv_head * head_dim wide
+    KvWriteArgs kv;       // cache side (kv.k, kv.v, kv.ldk, kv.ldv unused; tokens are y's rows)
 };
 
 hipError_t launch_qkv_gemm(const GemmArgs& a, hipStream_t s);

@@ -30,8 +30,7 @@
 //    the id is first remapped so that each XCD owns one contiguous range of
 //    tiles, which is then walked in groups of 8 M-tiles: the tiles resident on
 //    one XCD at a time share A rows and B columns in that XCD's L2.
-#include "pca_device.hpp"
-#include "pca_internal.hpp"
+#include "kv_common.hpp"
 
 #include <utility>
 
@@ -117,6 +116,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const uint16_t* p
     return make_rsrc((const void*)ub, (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes));
 }
 
+// KV = 0: plain GEMM; 1 / 2: the epilogue also writes y's K and V columns
+// into the bf16 / fp8 page pools (see kv_epilogue).
+template <int KV>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void qkv_gemm_kernel(GemmArgs a) {
     extern __shared__ __align__(16) uint16_t smem[];
@@ -237,25 +239,107 @@ void qkv_gemm_kernel(GemmArgs a) {
         mfmas(f[1]);
     }
 
-    // epilogue: lane holds, per block, column m = r32 and rows n = g*8 + half*4 + 0..3
+    // Epilogue.  The accumulators hold, per block (i, j), column m = r32 and
+    // rows n = g*8 + half*4 + 0..3 -- 8-byte runs spread over 32 rows of y per
+    // store instruction.  Each wave instead stages its 128 x 128 bf16 tile in
+    // LDS (token-major, 16-byte chunks XOR-swizzled by row so neither the
+    // 32-row writes nor the row reads collide on banks) and writes it back as
+    // full rows: 16 lanes x 16 bytes = one 256-byte run of a y row per lane
+    // group, four rows per store instruction.
+    wg_barrier();                                        // every wave is done with the operand stages
+    lds_char_t* stg = lds + wave * (128 * 256);          // this wave's 32 KiB
 #pragma unroll
-    for (int i = 0; i < FN; ++i) {
+    for (int i = 0; i < FN; ++i)
 #pragma unroll
-        for (int j = 0; j < FM; ++j) {
-            const int m = m0 + wm * 128 + j * 32 + r32;
-            if (m >= a.M) continue;
+        for (int j = 0; j < FM; ++j)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int n = n0 + wn * 128 + i * 32 + g * 8 + half * 4;
-                uint16_t* dst = a.y + (int64_t)m * a.ldy + n;
-                if (n + 3 < a.N) {
-                    u32x2_t w2 = {pack_bf16x2(acc[i][j][g * 4 + 0], acc[i][j][g * 4 + 1]),
-                                  pack_bf16x2(acc[i][j][g * 4 + 2], acc[i][j][g * 4 + 3])};
-                    *reinterpret_cast<u32x2_t*>(dst) = w2;
-                } else {
+                const int ml = j * 32 + r32, c = i * 4 + g;
+                const u32x2_t w2 = {pack_bf16x2(acc[i][j][g * 4 + 0], acc[i][j][g * 4 + 1]),
+                                    pack_bf16x2(acc[i][j][g * 4 + 2], acc[i][j][g * 4 + 3])};
+                *reinterpret_cast<__attribute__((address_space(3))) u32x2_t*>(
+                    stg + ml * 256 + ((c ^ (ml & 15)) * 16) + half * 8) = w2;
+            }
+    const int c = lane & 15;                             // the lane's 16-byte chunk of a row: columns c*8 .. c*8+7
+    const int n = n0 + wn * 128 + c * 8;
+    const int m_lo = m0 + wm * 128;
+
+    // fused KV-cache write: where the lane's 8 columns go (the data-flow
+    // article's §4.2 point -- the projection output goes straight into its
+    // page slot, no second pass over K and V).  The cache receives exactly
+    // the bf16 values stored to y, so it equals a separate pca_kv_cache_write
+    // of y.
+    [[maybe_unused]] const KvWriteArgs& kv = a.kv;
+    [[maybe_unused]] int kv_sel = -1, kvh = 0, dcol = 0;   // 0: K, 1: V; kv head and first d of the chunk
+    [[maybe_unused]] int slot_lo = -1, slot_hi = -1;       // page slots of tokens m_lo + lane, m_lo + 64 + lane
+    if constexpr (KV != 0) {
+        const int hd = kv.head_dim, nkc = kv.n_kv_head * hd;
+        int col = -1;
+        if (n >= a.k_col0 && n < a.k_col0 + nkc) { kv_sel = 0; col = n - a.k_col0; }
+        else if (n >= a.v_col0 && n < a.v_col0 + nkc) { kv_sel = 1; col = n - a.v_col0; }
+        if (col >= 0) { kvh = col / hd; dcol = col - kvh * hd; }
+        // only waves whose columns touch K or V look up page slots
+        const int nw0 = n0 + wn * 128, nw1 = min(nw0 + 128, a.N);
+        if ((nw0 < a.k_col0 + nkc && nw1 > a.k_col0) || (nw0 < a.v_col0 + nkc && nw1 > a.v_col0)) {
+            if (m_lo + lane < a.M) slot_lo = (int)token_slot(kv, m_lo + lane);
+            if (m_lo + 64 + lane < a.M) slot_hi = (int)token_slot(kv, m_lo + 64 + lane);
+        }
+    }
+
+#pragma unroll 4
+    for (int r = 0; r < 32; ++r) {
+        const int ml = r * 4 + (lane >> 4);
+        const u32x4_t v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(
+            stg + ml * 256 + ((c ^ (ml & 15)) * 16));
+        const int m = m_lo + ml;
+        [[maybe_unused]] int slot = -1;
+        if constexpr (KV != 0)   // the slot of row ml sits in lane ml % 64 of slot_lo / slot_hi
+            slot = __builtin_amdgcn_ds_bpermute((ml & 63) * 4, r < 16 ? slot_lo : slot_hi);
+        if (m >= a.M) continue;
+        uint16_t* dst = a.y + (int64_t)m * a.ldy + n;
+        if (n + 7 < a.N) {
+            *reinterpret_cast<u32x4_t*>(dst) = v;
+        } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (n + e < a.N) dst[e] = (uint16_t)(pack_bf16x2(acc[i][j][g * 4 + e], 0.0f) & 0xFFFFu);
+            for (int e = 0; e < 8; ++e)
+                if (n + e < a.N) dst[e] = (uint16_t)((v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+        }
+        if constexpr (KV == 1) {
+            if (kv_sel >= 0 && slot >= 0) {
+                uint16_t* pool = kv_sel == 0 ? (uint16_t*)kv.k_cache : (uint16_t*)kv.v_cache;
+                *reinterpret_cast<u32x4_t*>(pool + ((int64_t)slot * kv.n_kv_head + kvh) * kv.head_dim + dcol) = v;
+            }
+        } else if constexpr (KV == 2) {
+            // fp8: the wave's 128 columns are whole heads of K or of V (the
+            // host checks that both ranges start on a multiple of 128 and span
+            // a multiple of 128), so kv_sel is uniform over the wave and a
+            // (token, kv head) row is hd / 8 consecutive lanes of a 16-lane
+            // row group.  Codes come from the bf16 values, as for a separate
+            // write from y.
+            if (kv_sel >= 0) {
+                float x[8];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    x[2 * t] = bf16_lo(v[t]);
+                    x[2 * t + 1] = bf16_hi(v[t]);
+                }
+                float amax = 0.0f;
+#pragma unroll
+                for (int t = 0; t < 8; ++t) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[t]));
+                const int hd = kv.head_dim;
+                amax = hd == 128 ? group_max<16>(amax) : hd == 64 ? group_max<8>(amax) : group_max<4>(amax);
+                if (slot >= 0) {
+                    // binary32 round-to-nearest division (no fast-math): scale = amax / 448, inv = 448 / amax
+                    const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
+                    uint32_t lo = 0, hi = 0;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) lo |= e4m3_rne_sat(x[t] * inv) << (8 * t);
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) hi |= e4m3_rne_sat(x[4 + t] * inv) << (8 * t);
+                    const int64_t row = (int64_t)slot * kv.n_kv_head + kvh;
+                    uint8_t* pool = kv_sel == 0 ? (uint8_t*)kv.k_cache : (uint8_t*)kv.v_cache;
+                    *reinterpret_cast<u32x2_t*>(pool + row * hd + dcol) = u32x2_t{lo, hi};
+                    if (dcol == 0) (kv_sel == 0 ? kv.k_scale : kv.v_scale)[row] = amax / 448.0f;
                 }
             }
         }
@@ -264,13 +348,27 @@ void qkv_gemm_kernel(GemmArgs a) {
 
 }  // namespace
 
-hipError_t launch_qkv_gemm(const GemmArgs& a, hipStream_t s) {
-    static const hipError_t attr = hipFuncSetAttribute((const void*)qkv_gemm_kernel,
+namespace {
+
+template <int KV>
+hipError_t launch_kv(const GemmArgs& a, hipStream_t s) {
+    static const hipError_t attr = hipFuncSetAttribute((const void*)qkv_gemm_kernel<KV>,
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
     if (attr != hipSuccess) return attr;
     const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-    hipLaunchKernelGGL(qkv_gemm_kernel, dim3(tiles), dim3(kThreads), LDS_BYTES, s, a);
+    hipLaunchKernelGGL(qkv_gemm_kernel<KV>, dim3(tiles), dim3(kThreads), LDS_BYTES, s, a);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_qkv_gemm(const GemmArgs& a, hipStream_t s) {
+    switch (a.kv_mode) {
+        case 0: return launch_kv<0>(a, s);
+        case 1: return launch_kv<1>(a, s);
+        case 2: return launch_kv<2>(a, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace pca

@@ -118,3 +118,24 @@ def test_error_message_is_thread_local_and_cleared():
     assert st == 1 and "null" in msg
     pca.kv_layout(4, 2, 64)
     assert pca.load().pca_last_error().decode() == ""
+
+
+def test_fused_kv_write_validation():
+    # x, ldx, w_t, ldw, y, ldy, M, K, nh, nkv, hd, cu, ns, bt, mp, ps, dt, kc, vc, ks, vs, num_pages
+    base = dict(x=FAKE, ldx=64, w=FAKE, ldw=64, y=FAKE, ldy=1536, M=64, K=64, nh=8, nkv=2, hd=128, cu=None, ns=1,
+                bt=FAKE, mp=4, ps=16, dt=0, kc=FAKE, vc=FAKE, ks=None, vs=None, np_=4)
+    bad = {("x", 0): 1, ("y", MISALIGNED): 1, ("K", 60): 1, ("ldy", 1000): 1, ("nkv", 3): 1, ("hd", 96): 2,
+           ("ps", 8): 2, ("bt", 0): 1, ("kc", 0): 1, ("dt", 1): 1, ("ks", FAKE): 1, ("ns", 2): 1, ("np_", 0): 1,
+           ("dt", 7): 2}
+    for (key, val), exp in bad.items():
+        a = dict(base, **{key: val})
+        st, msg = _status("pca_qkv_proj_kv_write", a["x"], a["ldx"], a["w"], a["ldw"], a["y"], a["ldy"], a["M"],
+                          a["K"], a["nh"], a["nkv"], a["hd"], a["cu"], a["ns"], a["bt"], a["mp"], a["ps"], a["dt"],
+                          a["kc"], a["vc"], a["ks"], a["vs"], a["np_"], None)
+        assert st == exp and msg, (key, val, st, msg)
+    # fp8 needs K and V column blocks that start and span multiples of 128 columns
+    a = dict(base, nh=3, nkv=1, hd=64, ldy=320, dt=1, ks=FAKE, vs=FAKE)
+    st, msg = _status("pca_qkv_proj_kv_write", a["x"], a["ldx"], a["w"], a["ldw"], a["y"], a["ldy"], a["M"],
+                      a["K"], a["nh"], a["nkv"], a["hd"], a["cu"], a["ns"], a["bt"], a["mp"], a["ps"], a["dt"],
+                      a["kc"], a["vc"], a["ks"], a["vs"], a["np_"], None)
+    assert st == 2 and "128" in msg, (st, msg)
