@@ -1,0 +1,110 @@
+"""Pins for oracle.prefix (a chunk attending over a cached prefix): brute
+force with the shifted causal rule, the chunking invariant against the plain
+causal attention, the prefix-0 special case, the paged read-back, and the fp8
+decode.  CPU only."""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import attention as A
+from oracle import fp8, kvcache
+from oracle import prefix as PX
+
+
+def _rand(seed, *shape):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def brute_force_prefix(q, k, v, P, scale):
+    """Pure-Python loops: chunk row r (position P + r) weighs keys 0 .. P + r
+    with math.exp, normalised by their sum."""
+    Lq, H, D = len(q), len(q[0]), len(q[0][0])
+    G = H // len(k[0])
+    out = [[0.0] * (H * D) for _ in range(Lq)]
+    for i in range(H):
+        g = i // G
+        for r in range(Lq):
+            sc = [sum(q[r][i][d] * k[c][g][d] for d in range(D)) * scale for c in range(P + r + 1)]
+            mx = max(sc)
+            w = [math.exp(x - mx) for x in sc]
+            tot = sum(w)
+            for d in range(D):
+                out[r][i * D + d] = sum(w[c] * v[c][g][d] for c in range(P + r + 1)) / tot
+    return np.array(out)
+
+
+@pytest.mark.parametrize("P,Lq,H,Hk,D", [(0, 5, 2, 2, 3), (3, 4, 4, 2, 3), (9, 6, 4, 1, 4), (1, 1, 2, 1, 2)])
+def test_brute_force(P, Lq, H, Hk, D):
+    q, k, v = _rand(1, Lq, H, D), _rand(2, P + Lq, Hk, D), _rand(3, P + Lq, Hk, D)
+    ref = brute_force_prefix(q.tolist(), k.tolist(), v.tolist(), P, 1 / math.sqrt(D))
+    got = PX.prefix_causal_attention(q, k, v, P)
+    assert np.max(np.abs(got - ref)) < 1e-12
+
+
+@pytest.mark.parametrize("L,P", [(40, 0), (40, 17), (40, 39), (33, 32)])
+def test_chunk_rows_equal_whole_sequence_rows(L, P):
+    """Processing positions P .. L-1 as a chunk over the cached prefix gives
+    exactly the rows P .. L-1 of attention over the whole sequence."""
+    q, k, v = _rand(4, L, 4, 8), _rand(5, L, 2, 8), _rand(6, L, 2, 8)
+    whole = A.causal_attention(q, k, v)
+    chunk = PX.prefix_causal_attention(q[P:], k, v, P)
+    assert np.max(np.abs(chunk - whole[P:])) < 1e-12
+
+
+def test_first_chunk_row_with_long_prefix_sees_whole_prefix():
+    # one key dominating the prefix: row 0 of the chunk returns (almost) its value
+    P, D = 20, 4
+    q = np.zeros((1, 1, D)); q[0, 0, 0] = 40.0
+    k = np.zeros((P + 1, 1, D)); k[7, 0, 0] = 1.0
+    v = _rand(7, P + 1, 1, D)
+    got = PX.prefix_causal_attention(q, k, v, P, scale=1.0)
+    assert np.max(np.abs(got[0] - v[7, 0])) < 1e-12
+
+
+def _pools(seed, lens, ctxs, Hk, D, pages, fp8_cache=False):
+    """Write each sequence's ctx keys through a permuted block table."""
+    rng = np.random.default_rng(seed)
+    mp = max((c + 15) // 16 for c in ctxs)
+    order = rng.permutation(pages)
+    bt = np.full((len(ctxs), mp), -1, dtype=np.int64)
+    at = 0
+    for b, c in enumerate(ctxs):
+        n = (c + 15) // 16
+        bt[b, :n] = order[at:at + n]
+        at += n
+    cu_k = np.concatenate([[0], np.cumsum(ctxs)])
+    kk = _rand(seed + 1, int(cu_k[-1]), Hk, D).astype(np.float32)
+    vv = _rand(seed + 2, int(cu_k[-1]), Hk, D).astype(np.float32)
+    from oracle import bf16
+    kb, vb = bf16.from_f64(kk.astype(np.float64)), bf16.from_f64(vv.astype(np.float64))
+    if fp8_cache:
+        kc, vc, ks, vs = kvcache.paged_write_fp8(kb, vb, cu_k, bt, pages)
+        return kb, vb, cu_k, bt, kc, vc, ks, vs
+    kc, vc = kvcache.paged_write_bf16(kb, vb, cu_k, bt, pages)
+    return kb, vb, cu_k, bt, kc, vc, None, None
+
+
+def test_paged_read_back_bf16():
+    lens, ctxs = [5, 9], [21, 9]
+    kb, vb, cu_k, bt, kc, vc, _, _ = _pools(31, lens, ctxs, 2, 8, 6)
+    cu_q = np.concatenate([[0], np.cumsum(lens)])
+    q = _rand(32, int(cu_q[-1]), 4, 8)
+    got = PX.paged_prefix_attention(q, cu_q, ctxs, kc, vc, bt)
+    for b in range(2):
+        k = kb[cu_k[b]:cu_k[b + 1]]
+        v = vb[cu_k[b]:cu_k[b + 1]]
+        want = PX.prefix_causal_attention(q[cu_q[b]:cu_q[b + 1]], k, v, ctxs[b] - lens[b])
+        assert np.array_equal(got[cu_q[b]:cu_q[b + 1]], want)
+
+
+def test_paged_read_back_fp8_decodes_with_scales():
+    lens, ctxs = [4], [37]
+    kb, vb, cu_k, bt, kc, vc, ks, vs = _pools(41, lens, ctxs, 2, 16, 4, fp8_cache=True)
+    k, v = PX.cached_keys(kc, vc, bt, 0, 37, ks, vs)
+    # decoded values match the stored codes times scales, and sit within the E4M3 step of the bf16 input
+    kf = A._as_f64(kb)
+    assert np.max(np.abs(k - kf) / np.maximum(np.abs(kf).max(axis=2, keepdims=True), 1e-30)) <= 2.0 ** -4
+    page, slot = bt[0, 2], 3          # position 35: page 2, slot 3
+    pos = 2 * 16 + slot
+    assert np.array_equal(k[pos], fp8.decode(kc[page, slot]) * ks[page, slot][:, None])
