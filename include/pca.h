@@ -165,6 +165,41 @@ pca_status pca_prefill_attention(const pca_bf16* q, const pca_bf16* k, const pca
                                  void* stream);
 
 /*
+ * pca_prefill_attention_paged -- causal GQA attention of a prefill chunk over
+ *   its sequence's cached prefix.  Chunked prefill ("Prefill vs decode tuning
+ *   notes" (hncyxsy.com/news/227904) §2.1; "Decoding LLM inference latency"
+ *   (lnwmold.com/news/496245) §3.3 runs it with 512-token chunks over 16-token
+ *   blocks) processes a long prompt a chunk at a time, keeping the earlier
+ *   chunks' K/V in the paged cache.  The chunk's own K/V must already be in
+ *   the cache (pca_kv_cache_write or pca_qkv_proj_kv_write): all keys are read
+ *   from the pools through the block table.
+ *   For sequence b, chunk rows are q rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1
+ *   (Lq of them) and its keys are cache positions 0 .. ctx_lens[b]-1, so row r
+ *   sits at position P + r with P = ctx_lens[b] - Lq and sees keys c <= P + r:
+ *        o[r, i] = sum_{c <= P + r} softmax_c(q[r, i] . k[c, g] * scale) v[c, g].
+ *   q, o: as for pca_prefill_attention (token-major, row strides ldq, ldo).
+ *   cu_seqlens_q: device int32[num_seqs + 1] over the chunk rows (NULL = one
+ *        sequence of total_q rows); max_seqlen_q >= the longest chunk.
+ *   ctx_lens: device int32[num_seqs], keys per sequence (prefix + chunk);
+ *        clamped on the device to [Lq, max_pages_per_seq * 16].
+ *        max_ctx_len >= every ctx_lens[b] (sizes the staged block-table row).
+ *   block_table, max_pages_per_seq, page_size (16), k_cache, v_cache,
+ *        num_pages: the pools of pca_kv_cache_write.  Only a bf16 cache is read
+ *        (cache_dtype PCA_DTYPE_FP8_E4M3 gives PCA_ERR_UNSUPPORTED; k_scale and
+ *        v_scale must be NULL).  Each pool must be smaller than 2 GiB.
+ *        Block-table entries outside [0, num_pages) give unspecified output,
+ *        never an access outside the pools.
+ *   head_dim 32, 64 or 128; causal must be 1.
+ */
+pca_status pca_prefill_attention_paged(const pca_bf16* q, int64_t ldq, const int32_t* cu_seqlens_q, int num_seqs,
+                                       int max_seqlen_q, int64_t total_q, const int32_t* ctx_lens, int max_ctx_len,
+                                       const int32_t* block_table, int max_pages_per_seq, int page_size,
+                                       pca_dtype cache_dtype, const void* k_cache, const void* v_cache,
+                                       const float* k_scale, const float* v_scale, int64_t num_pages,
+                                       int n_head, int n_kv_head, int head_dim, float scale, int causal,
+                                       pca_bf16* o, int64_t ldo, void* stream);
+
+/*
  * pca_kv_cache_write -- scatter each token's K and V into its page slot.
  *   Token position p of sequence b goes to page block_table[b*max_pages_per_seq
  *   + p / page_size], slot p % page_size (data-flow article §4.2,

@@ -17,8 +17,8 @@ LIB_PATH = os.path.join(PKG, "libpca.so")
 PCA_OK, PCA_ERR_INVALID_ARG, PCA_ERR_UNSUPPORTED, PCA_ERR_HIP = 0, 1, 2, 3
 DTYPES = {"bf16": 0, "fp8_e4m3": 1}
 
-EXPORTED = ("pca_kv_layout", "pca_qkv_proj", "pca_qkv_proj_kv_write", "pca_prefill_attention", "pca_kv_cache_write",
-            "pca_last_error", "pca_version")
+EXPORTED = ("pca_kv_layout", "pca_qkv_proj", "pca_qkv_proj_kv_write", "pca_prefill_attention",
+            "pca_prefill_attention_paged", "pca_kv_cache_write", "pca_last_error", "pca_version")
 
 
 class PcaError(RuntimeError):
@@ -57,8 +57,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                        vp, vp, vp, vp, i64, vp]
     lib.pca_qkv_proj_kv_write.argtypes = [vp, i64, vp, i64, vp, i64, i64, i64, i32, i32, i32, vp, i32,
                                           vp, i32, i32, i32, vp, vp, vp, vp, i64, vp]
+    lib.pca_prefill_attention_paged.argtypes = [vp, i64, vp, i32, i32, i64, vp, i32, vp, i32, i32, i32, vp, vp,
+                                                vp, vp, i64, i32, i32, i32, f32, i32, vp, i64, vp]
     for fn in ("pca_kv_layout", "pca_qkv_proj", "pca_prefill_attention", "pca_kv_cache_write",
-               "pca_qkv_proj_kv_write"):
+               "pca_qkv_proj_kv_write", "pca_prefill_attention_paged"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.pca_last_error.restype = ctypes.c_char_p
     lib.pca_last_error.argtypes = []
@@ -159,6 +161,36 @@ def prefill_attention(q, k, v, o, n_head: int, n_kv_head: int, head_dim: int,
     _check("pca_prefill_attention", load().pca_prefill_attention(
         pq, pk, pv, ldq, ldk, ldv, _ptr(cu_seqlens), num_seqs, int(max_seqlen), T,
         n_head, n_kv_head, head_dim, float(scale), 1, po, ldo, _stream(stream)))
+    return o
+
+
+def prefill_attention_paged(q, o, k_cache, v_cache, block_table, ctx_lens, n_head: int, n_kv_head: int,
+                            head_dim: int, cu_seqlens=None, max_seqlen: Optional[int] = None,
+                            max_ctx: Optional[int] = None, scale: Optional[float] = None,
+                            cache_dtype: str = "bf16", k_scale=None, v_scale=None, page_size: int = 16,
+                            total_tokens: Optional[int] = None, stream=None):
+    """Causal GQA attention of chunk rows q over the cached keys of their
+    sequences (prefix then the chunk itself) read through the block table.
+    ctx_lens: int32 device tensor [num_seqs], keys per sequence."""
+    pq, ldq = _rows(q, "q")
+    po, ldo = _rows(o, "o")
+    T = q.shape[0] if total_tokens is None else int(total_tokens)
+    num_seqs = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
+    if max_seqlen is None:
+        max_seqlen = T
+    if max_ctx is None:
+        max_ctx = int(ctx_lens.max().item()) if ctx_lens.numel() else 0
+    if scale is None:
+        scale = head_dim ** -0.5
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be 2-D [num_seqs, max_pages_per_seq]")
+    elem = 2 if cache_dtype == "bf16" else 1
+    num_pages = k_cache.numel() * k_cache.element_size() // (page_size * n_kv_head * head_dim * elem)
+    _check("pca_prefill_attention_paged", load().pca_prefill_attention_paged(
+        pq, ldq, _ptr(cu_seqlens), num_seqs, int(max_seqlen), T, ctx_lens.data_ptr(), int(max_ctx),
+        block_table.data_ptr(), block_table.shape[1], page_size, DTYPES[cache_dtype], k_cache.data_ptr(),
+        v_cache.data_ptr(), _ptr(k_scale), _ptr(v_scale), num_pages, n_head, n_kv_head, head_dim, float(scale), 1,
+        po, ldo, _stream(stream)))
     return o
 
 

@@ -182,7 +182,18 @@ struct Params {
     int64_t ldo;
     int ntg;            // task groups per (sequence, kv head) in the grid
     int units;          // num_seqs * n_kv
+    // paged K/V (chunk over a cached prefix): k, v are the page pools
+    // [page][slot][n_kv][hd]; key c of sequence b sits in page bt[b][c / 16],
+    // slot c % 16; the sequence has ctx[b] keys, the last cu[b+1] - cu[b] of
+    // them being the chunk's own
+    const int32_t* bt;
+    int mp;             // block-table row length
+    const int32_t* ctx;
+    uint32_t pool_bytes;
 };
+
+constexpr uint32_t kOob = 0x80000000u;  // a buffer offset past every pool: loads return 0
+constexpr int kBtPerThread = 4;         // block-table entries per thread loaded ahead of the Q tile
 
 // DMA of one K or V tile (keys [kbase, kbase + BK) of one sequence) into the
 // LDS buffer `dst`: the buffer view starts at the tile, so keys at or past the
@@ -207,7 +218,33 @@ __device__ __forceinline__ void dma_tile(const uint16_t* src, int64_t ld, int64_
     }
 }
 
+// DMA of one K or V tile from a page pool: key c = kbase + row of the tile
+// comes from page bt[c / 16] (the sequence's block-table row, staged in LDS),
+// slot c % 16, kv head g; keys at or past Lk read 0 through an out-of-range
+// offset.  Same lane -> (row, swizzled chunk) map as dma_tile.
 template <int HD>
+__device__ __forceinline__ void dma_tile_paged(__amdgpu_buffer_rsrc_t r, int wave, int lane, int kbase, int Lk,
+                                               int n_kv, int g, lds_char_t* dst,
+                                               const __attribute__((address_space(3))) int32_t* lbt) {
+    using C = Cfg<HD>;
+#pragma unroll
+    for (int i = 0; i < C::DMA_ITERS; ++i) {
+        const int blk = wave + i * kWaves;
+        if (C::NBLK % kWaves == 0 || blk < C::NBLK) {
+            const int row = blk * C::RPI + lane / C::NC;
+            const int lch = (lane % C::NC) ^ swz<HD>(row);
+            const int c = kbase + row;
+            uint32_t off = kOob;
+            if (c < Lk) {
+                const int64_t slot = (int64_t)lbt[c >> 4] * 16 + (c & 15);
+                off = (uint32_t)(((slot * n_kv + g) * HD + lch * 8) * 2);
+            }
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(dst + blk * 1024), 16, off, 0, 0, 0);
+        }
+    }
+}
+
+template <int HD, bool PAGED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(Params p) {
     using C = Cfg<HD>;
@@ -246,7 +283,12 @@ void attn_fwd_kernel(Params p) {
     // the buffer resources built from them need no per-lane handling
     s0 = ((int64_t)__builtin_amdgcn_readfirstlane((int)(s0 >> 32)) << 32) |
          (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)s0);
-    const int Lb = __builtin_amdgcn_readfirstlane((int)(s1 - s0));
+    const int Lb = __builtin_amdgcn_readfirstlane((int)(s1 - s0));   // query rows (the chunk)
+    // keys: the chunk itself, or the cached prefix followed by the chunk; the
+    // chunk's row r sits at key position pos0 + r
+    int Lk = Lb;
+    if constexpr (PAGED) Lk = __builtin_amdgcn_readfirstlane(min(max(p.ctx[b], Lb), p.mp * 16));
+    const int pos0 = Lk - Lb;
     const int G = p.group;
     const int nqb = (Lb + BQ - 1) / BQ;
     const int ntasks = G * nqb;
@@ -260,10 +302,19 @@ void attn_fwd_kernel(Params p) {
     const int head = g * G + (active ? task % G : 0);
     const int q0 = qblk * BQ;                                  // first query row (in sequence)
     const int last_task = min(tg * kWaves + kWaves - 1, ntasks - 1);
-    const int kv_end = min(Lb, (last_task / G + 1) * BQ);
+    const int kv_end = pos0 + min(Lb, (last_task / G + 1) * BQ);
     const int ntiles = (kv_end + BK - 1) / BK;                 // tiles the workgroup visits
-    const int wave_last_q = min(q0 + BQ, Lb) - 1;
+    const int wave_last_q = pos0 + min(q0 + BQ, Lb) - 1;       // key position of the wave's last query
     const int wave_ntiles = active ? wave_last_q / BK + 1 : 0; // tiles this wave computes
+
+    // paged: first part of the sequence's block-table row (staged in LDS below)
+    [[maybe_unused]] const int npg = (Lk + 15) >> 4;
+    [[maybe_unused]] int32_t btv[kBtPerThread];
+    if constexpr (PAGED) {
+#pragma unroll
+        for (int u = 0; u < kBtPerThread; ++u)
+            btv[u] = u * kThreads + tid < npg ? p.bt[(int64_t)b * p.mp + u * kThreads + tid] : 0;
+    }
 
     // ---- Q tile in registers: B operand of S^T = K Q^T (column = query r32)
     bf16x8_t qreg[C::DCH];
@@ -293,8 +344,29 @@ void attn_fwd_kernel(Params p) {
         dma_k[i] = (uint32_t)(((int64_t)row * p.ldk + g * HD + lch * 8) * 2);
         dma_v[i] = (uint32_t)(((int64_t)row * p.ldv + g * HD + lch * 8) * 2);
     }
-    auto issue_k = [&](int tile, int buf) __attribute__((always_inline)) { dma_tile<HD>(p.k, p.ldk, s0, Lb, wave, tile * BK, lds + buf, dma_k); };
-    auto issue_v = [&](int tile, int buf) __attribute__((always_inline)) { dma_tile<HD>(p.v, p.ldv, s0, Lb, wave, tile * BK, lds + buf, dma_v); };
+    // paged: the sequence's block-table row, staged in LDS behind the K/V buffers
+    const __attribute__((address_space(3))) int32_t* lbt =
+        (const __attribute__((address_space(3))) int32_t*)(lds + C::LDS_BYTES);
+    [[maybe_unused]] __amdgpu_buffer_rsrc_t rk, rv;
+    if constexpr (PAGED) {
+        rk = make_rsrc(p.k, p.pool_bytes);
+        rv = make_rsrc(p.v, p.pool_bytes);
+        // the row was loaded into registers before the Q tile (both latencies overlap)
+        __attribute__((address_space(3))) int32_t* wbt = (__attribute__((address_space(3))) int32_t*)(lds + C::LDS_BYTES);
+#pragma unroll
+        for (int u = 0; u < kBtPerThread; ++u)
+            if (u * kThreads + tid < npg) wbt[u * kThreads + tid] = btv[u];
+        for (int i = kBtPerThread * kThreads + tid; i < npg; i += kThreads) wbt[i] = p.bt[(int64_t)b * p.mp + i];
+        __syncthreads();
+    }
+    auto issue_k = [&](int tile, int buf) __attribute__((always_inline)) {
+        if constexpr (PAGED) dma_tile_paged<HD>(rk, wave, lane, tile * BK, Lk, p.n_kv, g, lds + buf, lbt);
+        else dma_tile<HD>(p.k, p.ldk, s0, Lb, wave, tile * BK, lds + buf, dma_k);
+    };
+    auto issue_v = [&](int tile, int buf) __attribute__((always_inline)) {
+        if constexpr (PAGED) dma_tile_paged<HD>(rv, wave, lane, tile * BK, Lk, p.n_kv, g, lds + buf, lbt);
+        else dma_tile<HD>(p.v, p.ldv, s0, Lb, wave, tile * BK, lds + buf, dma_v);
+    };
 
     // ---- per-lane LDS read offsets
     // K operand (A of S^T): row = kb*32 + r32, logical chunk dc*2 + half
@@ -395,8 +467,8 @@ void attn_fwd_kernel(Params p) {
         if (t >= wave_ntiles) return;
         const int kbase = t * BK;
         // causal mask per element on tiles that reach past the first query
-        if (kbase + BK - 1 > q0) {
-            const int qry = q0 + r32;
+        if (kbase + BK - 1 > pos0 + q0) {
+            const int qry = pos0 + q0 + r32;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -532,12 +604,14 @@ void attn_fwd_kernel(Params p) {
         }
 }
 
-template <int HD>
+// largest dynamic LDS a workgroup may take (gfx950: 160 KiB per CU)
+constexpr int kMaxLds = 160 * 1024;
+
+template <int HD, bool PAGED>
 hipError_t launch_cfg(const AttnArgs& a, hipStream_t s) {
     using C = Cfg<HD>;
-    static const hipError_t attr = hipFuncSetAttribute((const void*)attn_fwd_kernel<HD>,
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                       C::LDS_BYTES);
+    static const hipError_t attr = hipFuncSetAttribute((const void*)attn_fwd_kernel<HD, PAGED>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
     if (attr != hipSuccess) return attr;
     Params p;
     p.q = a.q; p.k = a.k; p.v = a.v;
@@ -553,20 +627,32 @@ hipError_t launch_cfg(const AttnArgs& a, hipStream_t s) {
     const int nqb = (a.max_seqlen + BQ - 1) / BQ;
     p.ntg = (p.group * nqb + kWaves - 1) / kWaves;
     p.units = a.num_seqs * a.n_kv_head;
+    p.bt = a.block_table;
+    p.mp = a.max_pages_per_seq;
+    p.ctx = a.ctx_lens;
+    p.pool_bytes = (uint32_t)a.pool_bytes;
+    size_t lds = C::LDS_BYTES;
+    if (PAGED) lds += (size_t)(((a.max_ctx + 15) / 16 + 3) / 4) * 16;   // the block-table row, int32
+    if (lds > (size_t)kMaxLds) return hipErrorInvalidValue;
     const int64_t grid = (int64_t)p.ntg * p.units;
-    hipLaunchKernelGGL((attn_fwd_kernel<HD>), dim3((uint32_t)grid), dim3(kThreads), C::LDS_BYTES, s, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<HD, PAGED>), dim3((uint32_t)grid), dim3(kThreads), lds, s, p);
     return hipGetLastError();
+}
+
+template <bool PAGED>
+hipError_t launch_hd(const AttnArgs& a, hipStream_t s) {
+    switch (a.head_dim) {
+        case 32: return launch_cfg<32, PAGED>(a, s);
+        case 64: return launch_cfg<64, PAGED>(a, s);
+        case 128: return launch_cfg<128, PAGED>(a, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
-    switch (a.head_dim) {
-        case 32: return launch_cfg<32>(a, s);
-        case 64: return launch_cfg<64>(a, s);
-        case 128: return launch_cfg<128>(a, s);
-        default: return hipErrorInvalidValue;
-    }
+    return a.block_table != nullptr ? launch_hd<true>(a, s) : launch_hd<false>(a, s);
 }
 
 }  // namespace pca

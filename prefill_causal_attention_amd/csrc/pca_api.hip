@@ -218,11 +218,67 @@ pca_status pca_prefill_attention(const pca_bf16* q, const pca_bf16* k, const pca
         longest * ldv * 2 >= kMaxBufferBytes)
         return fail(PCA_ERR_UNSUPPORTED, "per-sequence q/k/v views beyond 2 GiB are not supported");
     pca::AttnArgs a;
+    memset(&a, 0, sizeof(a));
     a.q = q; a.k = k; a.v = v; a.ldq = ldq; a.ldk = ldk; a.ldv = ldv;
     a.cu_seqlens = cu_seqlens; a.num_seqs = num_seqs; a.max_seqlen = max_seqlen;
     a.total_tokens = total_tokens; a.n_head = n_head; a.n_kv_head = n_kv_head; a.head_dim = head_dim;
     a.scale = scale; a.o = o; a.ldo = ldo;
     return hip_status(pca::launch_attention(a, (hipStream_t)stream), "prefill_attention launch");
+}
+
+pca_status pca_prefill_attention_paged(const pca_bf16* q, int64_t ldq, const int32_t* cu_seqlens_q, int num_seqs,
+                                       int max_seqlen_q, int64_t total_q, const int32_t* ctx_lens, int max_ctx_len,
+                                       const int32_t* block_table, int max_pages_per_seq, int page_size,
+                                       pca_dtype cache_dtype, const void* k_cache, const void* v_cache,
+                                       const float* k_scale, const float* v_scale, int64_t num_pages,
+                                       int n_head, int n_kv_head, int head_dim, float scale, int causal,
+                                       pca_bf16* o, int64_t ldo, void* stream) {
+    if (total_q == 0 && num_seqs >= 1 && causal == 1) return ok();   // empty batch: nothing to read or write
+    if (!q || !o || !k_cache || !v_cache || !block_table || !ctx_lens)
+        return fail(PCA_ERR_INVALID_ARG, "null q, o, k_cache, v_cache, block_table or ctx_lens");
+    if (!aligned16(q) || !aligned16(o) || !aligned16(k_cache) || !aligned16(v_cache))
+        return fail(PCA_ERR_INVALID_ARG, "q, o, k_cache and v_cache must be 16-byte aligned");
+    if (((uintptr_t)block_table & 3u) || ((uintptr_t)ctx_lens & 3u))
+        return fail(PCA_ERR_INVALID_ARG, "block_table and ctx_lens must be 4-byte aligned");
+    if (causal != 1) return fail(PCA_ERR_INVALID_ARG, "only causal attention (causal = 1) is provided");
+    if (n_head <= 0 || n_kv_head <= 0 || n_head % n_kv_head != 0)
+        return fail(PCA_ERR_INVALID_ARG, "need n_head, n_kv_head > 0 and n_head %% n_kv_head == 0 (%d, %d)",
+                    n_head, n_kv_head);
+    if (!supported_head_dim(head_dim))
+        return fail(PCA_ERR_UNSUPPORTED, "head_dim %d not supported (32, 64 or 128)", head_dim);
+    if (page_size != 16) return fail(PCA_ERR_UNSUPPORTED, "page_size must be 16 (got %d)", page_size);
+    if (cache_dtype == PCA_DTYPE_FP8_E4M3)
+        return fail(PCA_ERR_UNSUPPORTED, "an fp8 cache is not read by the paged attention (bf16 only)");
+    if (cache_dtype != PCA_DTYPE_BF16) return fail(PCA_ERR_UNSUPPORTED, "unknown cache dtype %d", (int)cache_dtype);
+    if (k_scale || v_scale) return fail(PCA_ERR_INVALID_ARG, "k_scale/v_scale must be NULL for a bf16 cache");
+    pca_status st = check_batch(cu_seqlens_q, num_seqs, total_q);
+    if (st != PCA_OK) return st;
+    if (!(scale > 0.0f) || scale != scale || scale > 1e30f) return fail(PCA_ERR_INVALID_ARG, "scale must be finite and > 0");
+    if (ldq < (int64_t)n_head * head_dim || ldo < (int64_t)n_head * head_dim || ldq % 8 || ldo % 8)
+        return fail(PCA_ERR_INVALID_ARG, "ldq/ldo must cover n_head*head_dim and be multiples of 8");
+    if (max_pages_per_seq < 1 || num_pages < 1)
+        return fail(PCA_ERR_INVALID_ARG, "max_pages_per_seq and num_pages must be >= 1");
+    if (total_q == 0) return ok();
+    if (max_seqlen_q < 1 || (cu_seqlens_q == nullptr && max_seqlen_q < total_q))
+        return fail(PCA_ERR_INVALID_ARG, "max_seqlen_q must be >= 1 and cover the chunk (got %d)", max_seqlen_q);
+    if (max_ctx_len < max_seqlen_q || (int64_t)max_ctx_len > (int64_t)max_pages_per_seq * page_size)
+        return fail(PCA_ERR_INVALID_ARG, "max_ctx_len (%d) must be >= max_seqlen_q and <= max_pages_per_seq * page_size",
+                    max_ctx_len);
+    const int64_t pool_bytes = num_pages * page_size * (int64_t)n_kv_head * head_dim * 2;
+    if (pool_bytes >= kMaxBufferBytes) return fail(PCA_ERR_UNSUPPORTED, "page pools of 2 GiB or more are not supported");
+    const int64_t lds = 4 * 64 * (int64_t)head_dim * 2 + (((int64_t)max_ctx_len + 15) / 16 + 3) / 4 * 16;
+    if (lds > 160 * 1024) return fail(PCA_ERR_UNSUPPORTED, "max_ctx_len %d too long for the staged block table", max_ctx_len);
+    const int64_t longest = cu_seqlens_q ? (max_seqlen_q < total_q ? max_seqlen_q : total_q) : total_q;
+    if (longest * ldq * 2 >= kMaxBufferBytes) return fail(PCA_ERR_UNSUPPORTED, "per-sequence q views beyond 2 GiB");
+    pca::AttnArgs a;
+    memset(&a, 0, sizeof(a));
+    a.q = q; a.k = (const uint16_t*)k_cache; a.v = (const uint16_t*)v_cache; a.ldq = ldq;
+    a.cu_seqlens = cu_seqlens_q; a.num_seqs = num_seqs; a.max_seqlen = max_seqlen_q;
+    a.total_tokens = total_q; a.n_head = n_head; a.n_kv_head = n_kv_head; a.head_dim = head_dim;
+    a.scale = scale; a.o = o; a.ldo = ldo;
+    a.block_table = block_table; a.max_pages_per_seq = max_pages_per_seq; a.ctx_lens = ctx_lens;
+    a.max_ctx = max_ctx_len; a.pool_bytes = pool_bytes;
+    return hip_status(pca::launch_attention(a, (hipStream_t)stream), "prefill_attention_paged launch");
 }
 
 pca_status pca_kv_cache_write(const pca_bf16* k, const pca_bf16* v, int64_t ldk, int64_t ldv,

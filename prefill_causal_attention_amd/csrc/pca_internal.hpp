@@ -56,6 +56,13 @@ struct AttnArgs {
     float scale;
     uint16_t* o;
     int64_t ldo;
+    // paged K/V (a chunk over a cached prefix); block_table == null: k, v are
+    // token-major rows of the chunk itself
+    const int32_t* block_table;   // [num_seqs][max_pages_per_seq]
+    int max_pages_per_seq;
+    const int32_t* ctx_lens;      // [num_seqs] keys per sequence (prefix + chunk)
+    int max_ctx;
+    int64_t pool_bytes;           // bytes of the K (and of the V) pool, < 2^31
 };
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);

@@ -1,0 +1,133 @@
+"""GPU parity of pca_prefill_attention_paged (a prefill chunk over its cached
+prefix) against the fp64 oracle, plus invariants run on the kernel itself:
+with no prefix it equals pca_prefill_attention bit for bit, and a chunk's rows
+equal the same rows of the whole sequence attended in one piece."""
+import numpy as np
+import pytest
+import torch
+
+import prefill_causal_attention_amd as pca
+import workloads
+from oracle import attention as A
+from oracle import kvcache
+from oracle import prefix as PX
+
+from _gpu_helpers import assert_close, bits, dev, require_gpu, sample_rows, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(seed, chunks, prefixes, H, Hk, hd, spare=3):
+    """Seeded draws: per sequence b, prefix P_b + chunk L_b keys (N(0,1) bf16),
+    placed in permuted pages by the oracle's scatter; chunk queries N(0,1)."""
+    ctx = [p + l for p, l in zip(prefixes, chunks)]
+    rng = np.random.default_rng(seed)
+    npg = [(c + 15) // 16 for c in ctx]
+    pages = sum(npg) + spare
+    order = rng.permutation(pages)
+    bt = np.full((len(ctx), max(npg)), -1, dtype=np.int64)
+    at = 0
+    for b, n in enumerate(npg):
+        bt[b, :n] = order[at:at + n]
+        at += n
+    cu_k = np.concatenate([[0], np.cumsum(ctx)]).astype(np.int64)
+    kb = bits(workloads.normal_bf16(seed + 1, (int(cu_k[-1]), Hk * hd))).reshape(-1, Hk, hd)
+    vb = bits(workloads.normal_bf16(seed + 2, (int(cu_k[-1]), Hk * hd))).reshape(-1, Hk, hd)
+    kc, vc = kvcache.paged_write_bf16(kb, vb, cu_k, bt, pages)
+    cu_q = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    q = workloads.normal_bf16(seed + 3, (int(cu_q[-1]), H * hd))
+    return dict(ctx=np.array(ctx, dtype=np.int32), bt=bt, kb=kb, vb=vb, cu_k=cu_k, kc=kc, vc=vc, cu_q=cu_q, q=q,
+                H=H, Hk=Hk, hd=hd)
+
+
+def _gpu(c, o_pad=8):
+    T = int(c["cu_q"][-1])
+    nq = c["H"] * c["hd"]
+    o = torch.full((T, nq + o_pad), float("nan"), dtype=torch.bfloat16, device="cuda")
+    d_bt = dev(torch.from_numpy(np.where(c["bt"] < 0, 0, c["bt"]).astype(np.int32)))
+    kc = dev(torch.from_numpy(c["kc"].view(np.int16)))
+    vc = dev(torch.from_numpy(c["vc"].view(np.int16)))
+    cu = dev(torch.from_numpy(c["cu_q"])) if len(c["ctx"]) > 1 else None
+    pca.prefill_attention_paged(dev(c["q"]), o[:, :nq], kc, vc, d_bt, dev(torch.from_numpy(c["ctx"])),
+                                c["H"], c["Hk"], c["hd"], cu_seqlens=cu,
+                                max_seqlen=int(np.diff(c["cu_q"]).max()), max_ctx=int(c["ctx"].max()))
+    torch.cuda.synchronize()
+    assert torch.isnan(o[:, nq:].float()).all(), "wrote outside the heads"
+    return o[:, :nq]
+
+
+def _oracle(c, rows=None):
+    qb = bits(c["q"]).reshape(-1, c["H"], c["hd"])
+    return PX.paged_prefix_attention(qb, c["cu_q"], c["ctx"], c["kc"], c["vc"], c["bt"], rows=rows)
+
+
+@pytest.mark.parametrize("chunks,prefixes,H,Hk,hd", [
+    ([37], [100], 4, 2, 128),               # prefix and chunk not tile multiples
+    ([64], [64], 8, 2, 64),
+    ([129, 1, 50], [0, 300, 17], 8, 2, 128),  # varlen: no prefix, a 1-row chunk, ragged
+    ([200], [333], 4, 4, 32),
+    ([96, 40], [512, 1], 10, 2, 128),       # G = 5
+])
+def test_parity_small(chunks, prefixes, H, Hk, hd):
+    require_gpu()
+    c = _case(71, chunks, prefixes, H, Hk, hd)
+    say(f"prefill_attention_paged chunks={chunks} prefixes={prefixes} heads={H}/{Hk} hd={hd} seed=71")
+    got = _gpu(c).float().cpu().numpy()
+    assert_close(got, _oracle(c), "paged")
+
+
+def test_no_prefix_equals_contiguous_kernel_bitwise():
+    """ctx = chunk: the paged kernel reads the same keys through the pages and
+    must give exactly pca_prefill_attention's output."""
+    require_gpu()
+    c = _case(72, [300, 77], [0, 0], 8, 2, 128)
+    got = _gpu(c)
+    kv = np.concatenate([c["kb"].reshape(c["kb"].shape[0], -1), c["vb"].reshape(c["vb"].shape[0], -1)], axis=1)
+    kvt = dev(torch.from_numpy(kv.view(np.int16)).view(torch.bfloat16))
+    nk = c["Hk"] * c["hd"]
+    o = torch.empty_like(got)
+    pca.prefill_attention(dev(c["q"]), kvt[:, :nk], kvt[:, nk:], o, c["H"], c["Hk"], c["hd"],
+                          cu_seqlens=dev(torch.from_numpy(c["cu_q"])), max_seqlen=300)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(got), bits(o))
+
+
+@pytest.mark.parametrize("P", [64, 200, 512])
+def test_chunk_rows_equal_whole_sequence_rows_bitwise(P):
+    """The chunk's rows (positions P ..) equal rows P .. of the whole sequence
+    attended at once: every row sees the same kv tiles in the same order."""
+    require_gpu()
+    L, H, Hk, hd = 700, 8, 2, 128
+    c = _case(73, [L - P], [P], H, Hk, hd)
+    got = _gpu(c)
+    kv = np.concatenate([c["kb"].reshape(L, -1), c["vb"].reshape(L, -1)], axis=1)
+    kvt = dev(torch.from_numpy(kv.view(np.int16)).view(torch.bfloat16))
+    qfull = dev(workloads.normal_bf16(74, (L, H * hd)))
+    qfull[P:] = dev(c["q"])
+    o = torch.empty((L, H * hd), dtype=torch.bfloat16, device="cuda")
+    nk = Hk * hd
+    pca.prefill_attention(qfull, kvt[:, :nk], kvt[:, nk:], o, H, Hk, hd)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(got), bits(o[P:]))
+
+
+def test_long_prefix_gqa_sampled():
+    """s = 8192 GQA 32/8 hd128 processed as a last 512-row chunk over a 7680-key prefix."""
+    require_gpu()
+    c = _case(75, [512], [7680], 32, 8, 128, spare=64)
+    got = _gpu(c).float().cpu().numpy()
+    rows = sample_rows(512, 48, 76, must=(0, 1, 63, 64, 511))
+    assert_close(got[rows], _oracle(c, rows=rows), "paged s=8192 chunk")
+
+
+def test_fp8_cache_rejected():
+    require_gpu()
+    q = torch.zeros((4, 128), dtype=torch.bfloat16, device="cuda")
+    kc = torch.zeros((2, 16, 1, 128), dtype=torch.uint8, device="cuda")
+    sc = torch.zeros((2, 16, 1), dtype=torch.float32, device="cuda")
+    bt = torch.zeros((1, 2), dtype=torch.int32, device="cuda")
+    ctx = torch.tensor([4], dtype=torch.int32, device="cuda")
+    with pytest.raises(pca.PcaError) as e:
+        pca.prefill_attention_paged(q, q.clone(), kc, kc, bt, ctx, 1, 1, 128, cache_dtype="fp8_e4m3",
+                                    k_scale=sc, v_scale=sc)
+    assert e.value.status == 2
