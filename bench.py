@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU oracle sample time")
     ap.add_argument("--kv-cold-reps", type=int, default=20)
+    ap.add_argument("--extra-reps", type=int, default=20,
+                    help="reps of the extra measurements (fused GEMM + KV write, paged chunk attention); 0 skips")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (to scale HBM byte counters)")
     return ap.parse_args()
@@ -213,6 +215,61 @@ def main():
     del sets
     t_kv_cold = np.array(cold)
 
+    extras = {}
+    if args.extra_reps > 0:
+        def timed(fn, reps):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        # the KV-cache write done by the GEMM epilogue, against GEMM + separate write
+        def fused():
+            pca.qkv_proj_kv_write(x, wt, y, bt, kc, vc, w.n_head, w.n_kv_head, w.head_dim, cu_seqlens=cu,
+                                  cache_dtype=cache_dtype, k_scale=ks, v_scale=vs)
+
+        def separate():
+            pca.qkv_proj(x, wt, y)
+            pca.kv_cache_write(k, v, bt, kc, vc, w.n_kv_head, w.head_dim, cu_seqlens=cu,
+                               cache_dtype=cache_dtype, k_scale=ks, v_scale=vs)
+        t_sep = timed(separate, args.extra_reps)
+        t_fused = timed(fused, args.extra_reps)
+        extras["qkv_proj_kv_write"] = {"fused_ms": t_fused, "separate_ms": t_sep,
+                                       "gemm_tflops_fused": w.gemm_flops() / (t_fused * 1e-3) / 1e12}
+
+        # chunked prefill: 8 sequences, each a 512-row chunk over a 7680-key cached
+        # prefix (bf16 pages, GQA as the workload), the chunk's K/V already paged
+        nseq, P, Lq = 8, 7680, 512
+        ctx = P + Lq
+        npg = ctx // 16
+        rng = np.random.default_rng(9001)
+        pbt = torch.from_numpy(rng.permutation(nseq * npg).reshape(nseq, npg).astype(np.int32)).to(dev)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(9002)
+        pk = torch.randn((nseq * npg, 16, w.n_kv_head, w.head_dim), generator=gen, device=dev).to(torch.bfloat16)
+        pv = torch.randn((nseq * npg, 16, w.n_kv_head, w.head_dim), generator=gen, device=dev).to(torch.bfloat16)
+        pq = torch.randn((nseq * Lq, w.n_head * w.head_dim), generator=gen, device=dev).to(torch.bfloat16)
+        po = torch.empty_like(pq)
+        pcu = torch.arange(0, (nseq + 1) * Lq, Lq, dtype=torch.int32, device=dev)
+        pctx = torch.full((nseq,), ctx, dtype=torch.int32, device=dev)
+
+        def paged():
+            pca.prefill_attention_paged(pq, po, pk, pv, pbt, pctx, w.n_head, w.n_kv_head, w.head_dim,
+                                        cu_seqlens=pcu, max_seqlen=Lq, max_ctx=ctx)
+        t_paged = timed(paged, args.extra_reps)
+        pflop = 4.0 * w.head_dim * w.n_head * nseq * (Lq * P + Lq * (Lq + 1) / 2)
+        extras["prefill_attention_paged"] = {
+            "case": f"{nseq} sequences x {Lq}-row chunk over a {P}-key cached prefix, bf16 pages",
+            "ms": t_paged, "flop": pflop, "tflops": pflop / (t_paged * 1e-3) / 1e12,
+            "flop_count": "exact causal pairs, 4*hd*n_head per (query, visible key)"}
+        del pk, pv, pq, po
+
     att_flops = w.attention_flops()
     gemm_flops = w.gemm_flops()
     eb = 1 if fp8 else 2
@@ -240,7 +297,7 @@ def main():
     }
     traffic = measured_traffic(w.name)
     roofline = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": tflops / PEAK_BF16_TFLOPS, "traffic": traffic, "kernel": f"attn_fwd_kernel<{w.head_dim}>",
+                "frac": tflops / PEAK_BF16_TFLOPS, "traffic": traffic, "kernel": f"attn_fwd_kernel<{w.head_dim}, false>",
                 "flop_per_launch": att_flops, "avg_launch_ms": a_ms}
     out = {
         "metric": METRIC,
@@ -262,6 +319,7 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
         "path_tflops": (att_flops + gemm_flops) / (ms_step * 1e-3) / 1e12,
+        "extras": extras,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
