@@ -89,3 +89,57 @@ def paged_prefix_attention(q, cu_q, ctx_lens, k_pool, v_pool, block_table, scale
         k, v = cached_keys(k_pool, v_pool, block_table, b, ctx, k_scale, v_scale, page_size)
         out[pick] = prefix_causal_attention(q[s0:s1], k, v, ctx - (s1 - s0), scale, rows=sel[pick] - s0)
     return out
+
+
+def window_mask_rows(rows, L: int, window: int) -> np.ndarray:
+    """Additive mask of the sliding-window causal rule ([P3] §4.1: each token
+    attends only to a window of W recent positions, O(n W) work instead of
+    O(n^2)): row r sees keys c with r - W < c <= r (W keys, itself included);
+    window <= 0 means no lower bound."""
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.arange(L, dtype=np.int64)
+    m = np.zeros((rows.shape[0], L), dtype=np.float64)
+    hide = cols[None, :] > rows[:, None]
+    if window > 0:
+        hide |= cols[None, :] <= rows[:, None] - window
+    m[hide] = -np.inf
+    return m
+
+
+def window_causal_attention(q, k, v, window: int, prefix_len: int = 0, scale=None, rows=None) -> np.ndarray:
+    """prefix_causal_attention with the sliding-window rule: chunk row r at
+    position prefix_len + r sees keys c with prefix_len + r - window < c <=
+    prefix_len + r."""
+    q, k, v = attention._as_f64(q), attention._as_f64(k), attention._as_f64(v)
+    Lq, H, D = q.shape
+    Lk = k.shape[0]
+    assert Lk == prefix_len + Lq, "keys must be the prefix followed by the chunk"
+    G = H // k.shape[1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    rows = np.arange(Lq) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.empty((rows.shape[0], H * D), dtype=np.float64)
+    for i in range(H):
+        g = i // G
+        s = (q[rows, i, :] @ k[:, g, :].T) * scale
+        s = s + window_mask_rows(rows + prefix_len, Lk, window)
+        p = attention.softmax_two_pass(s)
+        out[:, i * D:(i + 1) * D] = p @ v[:, g, :]
+    return out
+
+
+def varlen_window_attention(q, k, v, cu_seqlens, window: int, scale=None, rows=None) -> np.ndarray:
+    """Packed sequences (no prefix), each attended alone with the window rule."""
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    T = int(cu[-1])
+    H, D = np.asarray(q).shape[1], np.asarray(q).shape[2]
+    sel = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.empty((sel.shape[0], H * D), dtype=np.float64)
+    for b in range(cu.shape[0] - 1):
+        s0, s1 = int(cu[b]), int(cu[b + 1])
+        pick = np.nonzero((sel >= s0) & (sel < s1))[0]
+        if pick.size == 0:
+            continue
+        out[pick] = window_causal_attention(np.asarray(q)[s0:s1], np.asarray(k)[s0:s1], np.asarray(v)[s0:s1],
+                                            window, 0, scale, rows=sel[pick] - s0)
+    return out

@@ -108,3 +108,52 @@ def test_paged_read_back_fp8_decodes_with_scales():
     page, slot = bt[0, 2], 3          # position 35: page 2, slot 3
     pos = 2 * 16 + slot
     assert np.array_equal(k[pos], fp8.decode(kc[page, slot]) * ks[page, slot][:, None])
+
+
+def brute_force_window(q, k, v, W, scale):
+    """Pure-Python loops: row r weighs keys max(0, r - W + 1) .. r."""
+    L, H, D = len(q), len(q[0]), len(q[0][0])
+    G = H // len(k[0])
+    out = [[0.0] * (H * D) for _ in range(L)]
+    for i in range(H):
+        g = i // G
+        for r in range(L):
+            keys = range(max(0, r - W + 1), r + 1)
+            sc = [sum(q[r][i][d] * k[c][g][d] for d in range(D)) * scale for c in keys]
+            mx = max(sc)
+            w = [math.exp(x - mx) for x in sc]
+            tot = sum(w)
+            for d in range(D):
+                out[r][i * D + d] = sum(wi * v[c][g][d] for wi, c in zip(w, keys)) / tot
+    return np.array(out)
+
+
+@pytest.mark.parametrize("L,W,H,Hk,D", [(9, 3, 2, 1, 3), (12, 5, 4, 2, 2), (6, 1, 2, 2, 4)])
+def test_window_brute_force(L, W, H, Hk, D):
+    q, k, v = _rand(21, L, H, D), _rand(22, L, Hk, D), _rand(23, L, Hk, D)
+    ref = brute_force_window(q.tolist(), k.tolist(), v.tolist(), W, 1 / math.sqrt(D))
+    got = PX.window_causal_attention(q, k, v, W)
+    assert np.max(np.abs(got - ref)) < 1e-12
+
+
+def test_window_covering_everything_is_causal():
+    q, k, v = _rand(24, 30, 4, 8), _rand(25, 30, 2, 8), _rand(26, 30, 2, 8)
+    full = A.causal_attention(q, k, v)
+    assert np.max(np.abs(PX.window_causal_attention(q, k, v, 30) - full)) < 1e-12
+    assert np.max(np.abs(PX.window_causal_attention(q, k, v, 0) - full)) < 1e-12
+
+
+def test_window_one_returns_own_value():
+    # W = 1: each row sees only itself, so the output is its own V row
+    q, k, v = _rand(27, 10, 2, 4), _rand(28, 10, 1, 4), _rand(29, 10, 1, 4)
+    got = PX.window_causal_attention(q, k, v, 1)
+    for i in range(2):
+        assert np.array_equal(got[:, i * 4:(i + 1) * 4], v[:, 0, :])
+
+
+def test_window_chunk_rows_equal_whole_rows():
+    L, P, W = 50, 23, 7
+    q, k, v = _rand(30, L, 4, 8), _rand(31, L, 2, 8), _rand(32, L, 2, 8)
+    whole = PX.window_causal_attention(q, k, v, W)
+    chunk = PX.window_causal_attention(q[P:], k, v, W, prefix_len=P)
+    assert np.max(np.abs(chunk - whole[P:])) < 1e-12
