@@ -165,6 +165,23 @@ pca_status pca_prefill_attention(const pca_bf16* q, const pca_bf16* k, const pca
                                  void* stream);
 
 /*
+ * pca_prefill_attention_window -- pca_prefill_attention with a sliding window
+ *   ("Decoding LLM inference latency" (lnwmold.com/news/496245) §4.1: each
+ *   token attends only to its W most recent positions, O(n W) work instead of
+ *   O(n^2)).  Row r of a sequence sees keys c with r - window < c <= r (window
+ *   keys, itself included); kv tiles wholly before a wave's window are never
+ *   visited.  window == 0 means no window (exactly pca_prefill_attention);
+ *   window < 0 is PCA_ERR_INVALID_ARG.  Every other argument as for
+ *   pca_prefill_attention.
+ */
+pca_status pca_prefill_attention_window(const pca_bf16* q, const pca_bf16* k, const pca_bf16* v,
+                                        int64_t ldq, int64_t ldk, int64_t ldv,
+                                        const int32_t* cu_seqlens, int num_seqs, int max_seqlen,
+                                        int64_t total_tokens, int n_head, int n_kv_head, int head_dim,
+                                        float scale, int causal, int window, pca_bf16* o, int64_t ldo,
+                                        void* stream);
+
+/*
  * pca_prefill_attention_paged -- causal GQA attention of a prefill chunk over
  *   its sequence's cached prefix.  Chunked prefill ("Prefill vs decode tuning
  *   notes" (hncyxsy.com/news/227904) §2.1; "Decoding LLM inference latency"

@@ -18,7 +18,8 @@ PCA_OK, PCA_ERR_INVALID_ARG, PCA_ERR_UNSUPPORTED, PCA_ERR_HIP = 0, 1, 2, 3
 DTYPES = {"bf16": 0, "fp8_e4m3": 1}
 
 EXPORTED = ("pca_kv_layout", "pca_qkv_proj", "pca_qkv_proj_kv_write", "pca_prefill_attention",
-            "pca_prefill_attention_paged", "pca_kv_cache_write", "pca_last_error", "pca_version")
+            "pca_prefill_attention_window", "pca_prefill_attention_paged", "pca_kv_cache_write",
+            "pca_last_error", "pca_version")
 
 
 class PcaError(RuntimeError):
@@ -57,10 +58,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                        vp, vp, vp, vp, i64, vp]
     lib.pca_qkv_proj_kv_write.argtypes = [vp, i64, vp, i64, vp, i64, i64, i64, i32, i32, i32, vp, i32,
                                           vp, i32, i32, i32, vp, vp, vp, vp, i64, vp]
+    lib.pca_prefill_attention_window.argtypes = [vp, vp, vp, i64, i64, i64, vp, i32, i32, i64, i32, i32, i32,
+                                                 f32, i32, i32, vp, i64, vp]
     lib.pca_prefill_attention_paged.argtypes = [vp, i64, vp, i32, i32, i64, vp, i32, vp, i32, i32, i32, vp, vp,
                                                 vp, vp, i64, i32, i32, i32, f32, i32, vp, i64, vp]
     for fn in ("pca_kv_layout", "pca_qkv_proj", "pca_prefill_attention", "pca_kv_cache_write",
-               "pca_qkv_proj_kv_write", "pca_prefill_attention_paged"):
+               "pca_qkv_proj_kv_write", "pca_prefill_attention_paged", "pca_prefill_attention_window"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.pca_last_error.restype = ctypes.c_char_p
     lib.pca_last_error.argtypes = []
@@ -144,10 +147,11 @@ def qkv_proj_kv_write(x, w_t, y, block_table, k_cache, v_cache, n_head: int, n_k
 
 def prefill_attention(q, k, v, o, n_head: int, n_kv_head: int, head_dim: int,
                       cu_seqlens=None, max_seqlen: Optional[int] = None, scale: Optional[float] = None,
-                      total_tokens: Optional[int] = None, stream=None):
+                      total_tokens: Optional[int] = None, window: int = 0, stream=None):
     """Causal GQA attention.  q, k, v, o: 2-D token-major views (T, >= heads*hd)
     with unit column stride (e.g. column slices of the fused projection output).
-    cu_seqlens: int32 device tensor [num_seqs + 1] or None (one sequence)."""
+    cu_seqlens: int32 device tensor [num_seqs + 1] or None (one sequence).
+    window > 0: sliding window (row r sees keys r - window < c <= r)."""
     pq, ldq = _rows(q, "q")
     pk, ldk = _rows(k, "k")
     pv, ldv = _rows(v, "v")
@@ -158,6 +162,11 @@ def prefill_attention(q, k, v, o, n_head: int, n_kv_head: int, head_dim: int,
         max_seqlen = T
     if scale is None:
         scale = head_dim ** -0.5
+    if window:
+        _check("pca_prefill_attention_window", load().pca_prefill_attention_window(
+            pq, pk, pv, ldq, ldk, ldv, _ptr(cu_seqlens), num_seqs, int(max_seqlen), T,
+            n_head, n_kv_head, head_dim, float(scale), 1, int(window), po, ldo, _stream(stream)))
+        return o
     _check("pca_prefill_attention", load().pca_prefill_attention(
         pq, pk, pv, ldq, ldk, ldv, _ptr(cu_seqlens), num_seqs, int(max_seqlen), T,
         n_head, n_kv_head, head_dim, float(scale), 1, po, ldo, _stream(stream)))

@@ -190,6 +190,7 @@ struct Params {
     int mp;             // block-table row length
     const int32_t* ctx;
     uint32_t pool_bytes;
+    int window;         // > 0: sliding window, row r sees keys r - window < c <= r
 };
 
 constexpr uint32_t kOob = 0x80000000u;  // a buffer offset past every pool: loads return 0
@@ -244,7 +245,7 @@ __device__ __forceinline__ void dma_tile_paged(__amdgpu_buffer_rsrc_t r, int wav
     }
 }
 
-template <int HD, bool PAGED>
+template <int HD, bool PAGED, bool WIN>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(Params p) {
     using C = Cfg<HD>;
@@ -306,6 +307,13 @@ void attn_fwd_kernel(Params p) {
     const int ntiles = (kv_end + BK - 1) / BK;                 // tiles the workgroup visits
     const int wave_last_q = pos0 + min(q0 + BQ, Lb) - 1;       // key position of the wave's last query
     const int wave_ntiles = active ? wave_last_q / BK + 1 : 0; // tiles this wave computes
+    // sliding window: the first tile holding a key that the wave's (the
+    // workgroup's) first row sees; tiles before it are skipped
+    int wave_first = 0, j0 = 0;
+    if constexpr (WIN) {
+        wave_first = max(0, pos0 + q0 - p.window + 1) / BK;
+        j0 = __builtin_amdgcn_readfirstlane(max(0, pos0 + (tg * kWaves / G) * BQ - p.window + 1) / BK);
+    }
 
     // paged: first part of the sequence's block-table row (staged in LDS below)
     [[maybe_unused]] const int npg = (Lk + 15) >> 4;
@@ -401,6 +409,13 @@ void attn_fwd_kernel(Params p) {
     f32x16_t sinit = {};
     f32x16_t s[2];          // scores of the tile whose softmax is next
     bf16x8_t pb[2][2];      // P of the tile whose P V product is next
+    // zero until the wave's first softmax: the matrix phase before it (which
+    // computes that tile's scores) then adds nothing to O
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) pb[kb][h] = as_bf16x8(u32x4_t{0u, 0u, 0u, 0u});
+    bool rset = false;      // the row has a reference R (set at its first tile with a visible key)
 
     // Matrix phase of tile j: O^T += V^T P^T for tile j (V buffer VC), then
     // S^T = K Q^T for tile j + 1 (K buffer KN), as one sequence of NM MFMAs
@@ -413,7 +428,7 @@ void attn_fwd_kernel(Params p) {
     constexpr int NS = 2 * C::DCH;         // (dc, kb): head_dim step x 32-key block
     constexpr int NM = NPV + NS;
     auto matrix_phase = [&](int j, auto KNc, auto VCc) __attribute__((always_inline)) {
-        if (j >= wave_ntiles) return;
+        if (j + 1 < wave_first || j >= wave_ntiles) return;
         constexpr int KB = decltype(KNc)::value, VB = decltype(VCc)::value;
         u32x2_t vlo[NPV], vhi[NPV];
         u32x4_t kf[NS];
@@ -464,17 +479,22 @@ void attn_fwd_kernel(Params p) {
 
     // Softmax phase of tile t (scores in s): P_t into pb, m and l updated.
     auto softmax_phase = [&](int t) __attribute__((always_inline)) {
-        if (t >= wave_ntiles) return;
+        if (t < wave_first || t >= wave_ntiles) return;
         const int kbase = t * BK;
-        // causal mask per element on tiles that reach past the first query
-        if (kbase + BK - 1 > pos0 + q0) {
+        // causal mask per element on tiles that reach past the first query;
+        // window mask on tiles that start before the last query's window
+        const bool upper = kbase + BK - 1 > pos0 + q0;
+        const bool lower = WIN && kbase <= pos0 + q0 + BQ - 1 - p.window;
+        if (upper || lower) {
             const int qry = pos0 + q0 + r32;
+            // visible iff 0 <= qry - key < wlim: one unsigned compare per score
+            const uint32_t wlim = WIN ? (uint32_t)p.window : 0x7FFFFFFFu;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int key = kbase + kb * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
-                    if (key > qry) s[kb][e] = -__builtin_inff();
+                    if ((uint32_t)(qry - key) >= wlim) s[kb][e] = -__builtin_inff();
                 }
         }
         // Online softmax, one query per lane (its 64 keys split with lane ^ 32).
@@ -506,10 +526,10 @@ void attn_fwd_kernel(Params p) {
                 }
         };
         exps(0.0f);
-        if (t == 0 || __builtin_amdgcn_ballot_w64(rs > 0.5f * kSumLimit) != 0) {
+        if (__builtin_amdgcn_ballot_w64(!rset || rs > 0.5f * kSumLimit) != 0) {
             float rlo, rhi;
             both_halves(rs, rlo, rhi);
-            const bool move = t == 0 || rlo + rhi > kSumLimit;
+            const bool move = !rset || rlo + rhi > kSumLimit;
             // rare: moving rows take their tile max as the new reference,
             // recompute p and rescale O and l (non-moving rows: d = 0, alpha = 1,
             // the same p as above)
@@ -520,7 +540,11 @@ void attn_fwd_kernel(Params p) {
                 for (int e = 0; e < 16; ++e) mx = __builtin_fmaxf(mx, s[kb][e]);
             float lo, hi;
             both_halves(mx, lo, hi);
-            const float d = move ? __builtin_fmaxf(lo, hi) : 0.0f;
+            const float mrow = __builtin_fmaxf(lo, hi);
+            // a row with no visible key in this tile (window) keeps no reference
+            const bool ok = move && mrow > -__builtin_inff();
+            const float d = ok ? mrow : 0.0f;
+            rset = rset || ok;
             exps(d);
             // d > 0 for a row past the limit; on the first tile O and l are 0
             const float alpha = __builtin_fminf(fast_exp2(-d), 1.0f);
@@ -567,17 +591,18 @@ void attn_fwd_kernel(Params p) {
     using V0 = std::integral_constant<int, C::VBUF0>;
     using V1 = std::integral_constant<int, C::VBUF1>;
 
-    // prologue: K_0, V_0 and K_1 in flight, then every wave computes the
-    // scores of tile 0; group B waits one half-step
-    issue_k(0, C::KBUF0);
-    issue_v(0, C::VBUF0);
-    if (1 < ntiles) issue_k(1, C::KBUF1);
+    // prologue: K and V of the first tile j0 (0 unless a window skips the
+    // start) and K of the next in flight, then every wave whose first tile it
+    // is computes its scores; group B waits one half-step
+    issue_k(j0, C::KBUF0);
+    issue_v(j0, C::VBUF0);
+    if (j0 + 1 < ntiles) issue_k(j0 + 1, C::KBUF1);
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();
-    if (0 < wave_ntiles) scores(K0{});
+    if (wave_first == j0 && j0 < wave_ntiles) scores(K0{});
     if (!lead) wg_barrier();
     // two tiles per trip so every buffer offset is a compile-time constant
-    for (int j = 0; j < ntiles; j += 2) {
+    for (int j = j0; j < ntiles; j += 2) {
         tile(j, K0{}, K1{}, V0{}, V1{});
         if (j + 1 >= ntiles) break;
         tile(j + 1, K1{}, K0{}, V1{}, V0{});
@@ -607,10 +632,10 @@ void attn_fwd_kernel(Params p) {
 // largest dynamic LDS a workgroup may take (gfx950: 160 KiB per CU)
 constexpr int kMaxLds = 160 * 1024;
 
-template <int HD, bool PAGED>
+template <int HD, bool PAGED, bool WIN>
 hipError_t launch_cfg(const AttnArgs& a, hipStream_t s) {
     using C = Cfg<HD>;
-    static const hipError_t attr = hipFuncSetAttribute((const void*)attn_fwd_kernel<HD, PAGED>,
+    static const hipError_t attr = hipFuncSetAttribute((const void*)attn_fwd_kernel<HD, PAGED, WIN>,
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
     if (attr != hipSuccess) return attr;
     Params p;
@@ -630,21 +655,22 @@ hipError_t launch_cfg(const AttnArgs& a, hipStream_t s) {
     p.bt = a.block_table;
     p.mp = a.max_pages_per_seq;
     p.ctx = a.ctx_lens;
+    p.window = a.window;
     p.pool_bytes = (uint32_t)a.pool_bytes;
     size_t lds = C::LDS_BYTES;
     if (PAGED) lds += (size_t)(((a.max_ctx + 15) / 16 + 3) / 4) * 16;   // the block-table row, int32
     if (lds > (size_t)kMaxLds) return hipErrorInvalidValue;
     const int64_t grid = (int64_t)p.ntg * p.units;
-    hipLaunchKernelGGL((attn_fwd_kernel<HD, PAGED>), dim3((uint32_t)grid), dim3(kThreads), lds, s, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<HD, PAGED, WIN>), dim3((uint32_t)grid), dim3(kThreads), lds, s, p);
     return hipGetLastError();
 }
 
-template <bool PAGED>
+template <bool PAGED, bool WIN>
 hipError_t launch_hd(const AttnArgs& a, hipStream_t s) {
     switch (a.head_dim) {
-        case 32: return launch_cfg<32, PAGED>(a, s);
-        case 64: return launch_cfg<64, PAGED>(a, s);
-        case 128: return launch_cfg<128, PAGED>(a, s);
+        case 32: return launch_cfg<32, PAGED, WIN>(a, s);
+        case 64: return launch_cfg<64, PAGED, WIN>(a, s);
+        case 128: return launch_cfg<128, PAGED, WIN>(a, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -652,7 +678,8 @@ hipError_t launch_hd(const AttnArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
-    return a.block_table != nullptr ? launch_hd<true>(a, s) : launch_hd<false>(a, s);
+    if (a.block_table != nullptr) return launch_hd<true, false>(a, s);
+    return a.window > 0 ? launch_hd<false, true>(a, s) : launch_hd<false, false>(a, s);
 }
 
 }  // namespace pca

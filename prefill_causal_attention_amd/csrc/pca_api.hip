@@ -191,6 +191,17 @@ pca_status pca_prefill_attention(const pca_bf16* q, const pca_bf16* k, const pca
                                  const int32_t* cu_seqlens, int num_seqs, int max_seqlen,
                                  int64_t total_tokens, int n_head, int n_kv_head, int head_dim,
                                  float scale, int causal, pca_bf16* o, int64_t ldo, void* stream) {
+    return pca_prefill_attention_window(q, k, v, ldq, ldk, ldv, cu_seqlens, num_seqs, max_seqlen, total_tokens,
+                                        n_head, n_kv_head, head_dim, scale, causal, 0, o, ldo, stream);
+}
+
+pca_status pca_prefill_attention_window(const pca_bf16* q, const pca_bf16* k, const pca_bf16* v,
+                                        int64_t ldq, int64_t ldk, int64_t ldv,
+                                        const int32_t* cu_seqlens, int num_seqs, int max_seqlen,
+                                        int64_t total_tokens, int n_head, int n_kv_head, int head_dim,
+                                        float scale, int causal, int window, pca_bf16* o, int64_t ldo,
+                                        void* stream) {
+    if (window < 0) return fail(PCA_ERR_INVALID_ARG, "window must be >= 0 (0: no window), got %d", window);
     if (total_tokens == 0 && num_seqs >= 1 && causal == 1) return ok();   // empty batch: nothing to read or write
     if (!q || !k || !v || !o) return fail(PCA_ERR_INVALID_ARG, "null q, k, v or o");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
@@ -223,6 +234,7 @@ pca_status pca_prefill_attention(const pca_bf16* q, const pca_bf16* k, const pca
     a.cu_seqlens = cu_seqlens; a.num_seqs = num_seqs; a.max_seqlen = max_seqlen;
     a.total_tokens = total_tokens; a.n_head = n_head; a.n_kv_head = n_kv_head; a.head_dim = head_dim;
     a.scale = scale; a.o = o; a.ldo = ldo;
+    a.window = window;
     return hip_status(pca::launch_attention(a, (hipStream_t)stream), "prefill_attention launch");
 }
 

@@ -63,6 +63,7 @@ struct AttnArgs {
     const int32_t* ctx_lens;      // [num_seqs] keys per sequence (prefix + chunk)
     int max_ctx;
     int64_t pool_bytes;           // bytes of the K (and of the V) pool, < 2^31
+    int window;                   // > 0: sliding window of that many keys (row r sees r - window < c <= r)
 };
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
