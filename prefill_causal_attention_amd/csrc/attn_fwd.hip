@@ -467,13 +467,18 @@ void attn_fwd_kernel(Params p) {
     };
 
     // S^T = K Q^T for the tile in K buffer KB (prologue only)
+    // (all NS operand reads issued first, each MFMA waiting only for its own)
     auto scores = [&](auto KBc) __attribute__((always_inline)) {
         constexpr int KB = decltype(KBc)::value;
+        u32x4_t kp[NS];
         static_for<NS>([&](auto Mc) {
             constexpr int m = decltype(Mc)::value, dc = m / 2, kb = m % 2;
-            u32x4_t k = lds_read_b128<KB + kb * 32 * C::ROWB>(kaddr[dc]);
-            lds_wait<0>(k);
-            s[kb] = mfma32x32x16(as_bf16x8(k), qreg[dc], dc == 0 ? sinit : s[kb]);
+            kp[m] = lds_read_b128<KB + kb * 32 * C::ROWB>(kaddr[dc]);
+        });
+        static_for<NS>([&](auto Mc) {
+            constexpr int m = decltype(Mc)::value, dc = m / 2, kb = m % 2;
+            lds_wait<NS - 1 - m>(kp[m]);
+            s[kb] = mfma32x32x16(as_bf16x8(kp[m]), qreg[dc], dc == 0 ? sinit : s[kb]);
         });
     };
 
