@@ -104,6 +104,25 @@ pca_status pca_qkv_proj(const pca_bf16* x, int64_t ldx, const pca_bf16* w_t, int
                         void* stream);
 
 /*
+ * pca_out_proj_residual -- the output projection and residual add that close
+ *   the attention unit: out = res + o * w_t^T.  The data-flow article's §2.1
+ *   writes the layer as residual = input, ..., attend, residual += attention
+ *   output; §3.3 lays the heads out as (s, n_head*head_dim) precisely so that
+ *   the output projection W_o reads them as one matrix.  Same GEMM as
+ *   pca_qkv_proj (fp32 accumulation); the residual is added to the fp32
+ *   accumulators and the sum rounded once to bf16 (RNE).
+ *   o:   device, M rows of K elements (the attention output, K = n_head*hd).
+ *   w_t: device, W_o pre-transposed to (N, K), N = h.
+ *   res: device, M rows of N elements, row stride ldr; may be out itself
+ *        (with ldr == ldout) for an in-place update, else must not overlap it.
+ *   out: device, M rows of N elements, row stride ldout.
+ *   Sizes and strides as for pca_qkv_proj.
+ */
+pca_status pca_out_proj_residual(const pca_bf16* o, int64_t ldo, const pca_bf16* w_t, int64_t ldw,
+                                 const pca_bf16* res, int64_t ldr, pca_bf16* out, int64_t ldout,
+                                 int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
  * pca_qkv_proj_kv_write -- pca_qkv_proj with the KV-cache write done by the
  *   GEMM's epilogue.  The data-flow article's §4.2 notes that the projection
  *   output can be scattered into its cache blocks by the kernel that produces

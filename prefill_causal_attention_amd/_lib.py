@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(PKG, "libpca.so")
 PCA_OK, PCA_ERR_INVALID_ARG, PCA_ERR_UNSUPPORTED, PCA_ERR_HIP = 0, 1, 2, 3
 DTYPES = {"bf16": 0, "fp8_e4m3": 1}
 
-EXPORTED = ("pca_kv_layout", "pca_qkv_proj", "pca_qkv_proj_kv_write", "pca_prefill_attention",
+EXPORTED = ("pca_kv_layout", "pca_qkv_proj", "pca_qkv_proj_kv_write", "pca_out_proj_residual", "pca_prefill_attention",
             "pca_prefill_attention_window", "pca_prefill_attention_paged", "pca_kv_cache_write",
             "pca_last_error", "pca_version")
 
@@ -58,12 +58,14 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                        vp, vp, vp, vp, i64, vp]
     lib.pca_qkv_proj_kv_write.argtypes = [vp, i64, vp, i64, vp, i64, i64, i64, i32, i32, i32, vp, i32,
                                           vp, i32, i32, i32, vp, vp, vp, vp, i64, vp]
+    lib.pca_out_proj_residual.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, i64, i64, i64, vp]
     lib.pca_prefill_attention_window.argtypes = [vp, vp, vp, i64, i64, i64, vp, i32, i32, i64, i32, i32, i32,
                                                  f32, i32, i32, vp, i64, vp]
     lib.pca_prefill_attention_paged.argtypes = [vp, i64, vp, i32, i32, i64, vp, i32, vp, i32, i32, i32, vp, vp,
                                                 vp, vp, i64, i32, i32, i32, f32, i32, vp, i64, vp]
     for fn in ("pca_kv_layout", "pca_qkv_proj", "pca_prefill_attention", "pca_kv_cache_write",
-               "pca_qkv_proj_kv_write", "pca_prefill_attention_paged", "pca_prefill_attention_window"):
+               "pca_qkv_proj_kv_write", "pca_prefill_attention_paged", "pca_prefill_attention_window",
+               "pca_out_proj_residual"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.pca_last_error.restype = ctypes.c_char_p
     lib.pca_last_error.argtypes = []
@@ -119,6 +121,23 @@ def qkv_proj(x, w_t, y, stream=None):
         raise ValueError(f"shape mismatch: x {tuple(x.shape)}, w_t {tuple(w_t.shape)}, y {tuple(y.shape)}")
     _check("pca_qkv_proj", load().pca_qkv_proj(px, ldx, pw, ldw, py, ldy, M, N, K, _stream(stream)))
     return y
+
+
+def out_proj_residual(o, w_t, res, out, stream=None):
+    """out[M, N] = res + o[M, K] @ w_t[N, K]^T (bf16, fp32 accumulate, one
+    rounding); res may be out itself."""
+    po, ldo = _rows(o, "o")
+    pw, ldw = _rows(w_t, "w_t")
+    pr, ldr = _rows(res, "res")
+    pout, ldout = _rows(out, "out")
+    M, K = o.shape
+    N = w_t.shape[0]
+    if w_t.shape[1] != K or tuple(res.shape) != (M, N) or tuple(out.shape) != (M, N):
+        raise ValueError(f"shape mismatch: o {tuple(o.shape)}, w_t {tuple(w_t.shape)}, res {tuple(res.shape)}, "
+                         f"out {tuple(out.shape)}")
+    _check("pca_out_proj_residual", load().pca_out_proj_residual(po, ldo, pw, ldw, pr, ldr, pout, ldout, M, N, K,
+                                                                 _stream(stream)))
+    return out
 
 
 def qkv_proj_kv_write(x, w_t, y, block_table, k_cache, v_cache, n_head: int, n_kv_head: int, head_dim: int,

@@ -151,6 +151,30 @@ pca_status pca_qkv_proj(const pca_bf16* x, int64_t ldx, const pca_bf16* w_t, int
     return hip_status(pca::launch_qkv_gemm(a, (hipStream_t)stream), "qkv_proj launch");
 }
 
+pca_status pca_out_proj_residual(const pca_bf16* o, int64_t ldo, const pca_bf16* w_t, int64_t ldw,
+                                 const pca_bf16* res, int64_t ldr, pca_bf16* out, int64_t ldout,
+                                 int64_t M, int64_t N, int64_t K, void* stream) {
+    pca::GemmArgs a;
+    pca_status st = check_gemm(o, ldo, w_t, ldw, out, ldout, M, N, K, a);
+    if (st != PCA_OK) return st;
+    if (!res) return fail(PCA_ERR_INVALID_ARG, "null res");
+    if (!aligned16(res) || ldr < N || ldr % 8)
+        return fail(PCA_ERR_INVALID_ARG, "res must be 16-byte aligned with ldr >= N and a multiple of 8");
+    if (res != out) {
+        // res may be out itself (in-place residual update) but must not partly overlap it
+        const char* r0 = (const char*)res;
+        const char* r1 = r0 + ((M - 1) * ldr + N) * 2;
+        const char* o0 = (const char*)out;
+        const char* o1 = o0 + ((M - 1) * ldout + N) * 2;
+        if (r0 < o1 && o0 < r1) return fail(PCA_ERR_INVALID_ARG, "res overlaps out without being out");
+    } else if (ldr != ldout) {
+        return fail(PCA_ERR_INVALID_ARG, "in-place residual needs ldr == ldout");
+    }
+    a.res = res;
+    a.ldr = ldr;
+    return hip_status(pca::launch_qkv_gemm(a, (hipStream_t)stream), "out_proj_residual launch");
+}
+
 pca_status pca_qkv_proj_kv_write(const pca_bf16* x, int64_t ldx, const pca_bf16* w_t, int64_t ldw,
                                  pca_bf16* y, int64_t ldy, int64_t M, int64_t K,
                                  int n_head, int n_kv_head, int head_dim,

@@ -39,6 +39,9 @@ struct GemmArgs {
     int kv_mode;          // 0: none, 1: bf16 cache, 2: fp8 E4M3 cache
     int k_col0, v_col0;   // first K / V column of y; each range is n_kv_head * head_dim wide
     KvWriteArgs kv;       // cache side (kv.k, kv.v, kv.ldk, kv.ldv unused; tokens are y's rows)
+    // optional residual: y = x w^T + res (res may be y itself)
+    const uint16_t* res;
+    int64_t ldr;
 };
 
 hipError_t launch_qkv_gemm(const GemmArgs& a, hipStream_t s);

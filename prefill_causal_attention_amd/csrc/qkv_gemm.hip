@@ -117,8 +117,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const uint16_t* p
 }
 
 // KV = 0: plain GEMM; 1 / 2: the epilogue also writes y's K and V columns
-// into the bf16 / fp8 page pools (see kv_epilogue).
-template <int KV>
+// into the bf16 / fp8 page pools.  RES: y = x w^T + res, the residual added
+// to the fp32 accumulators before the single bf16 rounding.
+template <int KV, bool RES>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void qkv_gemm_kernel(GemmArgs a) {
     extern __shared__ __align__(16) uint16_t smem[];
@@ -248,21 +249,48 @@ void qkv_gemm_kernel(GemmArgs a) {
     // group, four rows per store instruction.
     wg_barrier();                                        // every wave is done with the operand stages
     lds_char_t* stg = lds + wave * (128 * 256);          // this wave's 32 KiB
+    const int c = lane & 15;                             // the lane's 16-byte chunk of a row: columns c*8 .. c*8+7
+    const int n = n0 + wn * 128 + c * 8;
+    const int m_lo = m0 + wm * 128;
+    if constexpr (RES) {
+        // the residual sub-tile goes into the staging area first, row by row
+        // (coalesced 16-byte loads), and is added to the accumulators below
+#pragma unroll 8
+        for (int r = 0; r < 32; ++r) {
+            const int ml = r * 4 + (lane >> 4);
+            const int m = m_lo + ml;
+            u32x4_t rv = {0u, 0u, 0u, 0u};
+            if (m < a.M) {
+                const uint16_t* src = a.res + (int64_t)m * a.ldr + n;
+                if (n + 7 < a.N) {
+                    rv = *reinterpret_cast<const u32x4_t*>(src);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (n + e < a.N) rv[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
+                }
+            }
+            *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>(stg + ml * 256 + ((c ^ (ml & 15)) * 16)) = rv;
+        }
+    }
 #pragma unroll
     for (int i = 0; i < FN; ++i)
 #pragma unroll
         for (int j = 0; j < FM; ++j)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int ml = j * 32 + r32, c = i * 4 + g;
-                const u32x2_t w2 = {pack_bf16x2(acc[i][j][g * 4 + 0], acc[i][j][g * 4 + 1]),
-                                    pack_bf16x2(acc[i][j][g * 4 + 2], acc[i][j][g * 4 + 3])};
-                *reinterpret_cast<__attribute__((address_space(3))) u32x2_t*>(
-                    stg + ml * 256 + ((c ^ (ml & 15)) * 16) + half * 8) = w2;
+                const int ml = j * 32 + r32, ci = i * 4 + g;
+                __attribute__((address_space(3))) u32x2_t* slot =
+                    reinterpret_cast<__attribute__((address_space(3))) u32x2_t*>(stg + ml * 256 + ((ci ^ (ml & 15)) * 16) + half * 8);
+                float t0 = acc[i][j][g * 4 + 0], t1 = acc[i][j][g * 4 + 1];
+                float t2 = acc[i][j][g * 4 + 2], t3 = acc[i][j][g * 4 + 3];
+                if constexpr (RES) {
+                    const u32x2_t rr = *slot;                // this lane's own 4 residual values
+                    t0 += bf16_lo(rr[0]); t1 += bf16_hi(rr[0]);
+                    t2 += bf16_lo(rr[1]); t3 += bf16_hi(rr[1]);
+                }
+                *slot = u32x2_t{pack_bf16x2(t0, t1), pack_bf16x2(t2, t3)};
             }
-    const int c = lane & 15;                             // the lane's 16-byte chunk of a row: columns c*8 .. c*8+7
-    const int n = n0 + wn * 128 + c * 8;
-    const int m_lo = m0 + wm * 128;
 
     // fused KV-cache write: where the lane's 8 columns go (the data-flow
     // article's §4.2 point -- the projection output goes straight into its
@@ -350,23 +378,24 @@ void qkv_gemm_kernel(GemmArgs a) {
 
 namespace {
 
-template <int KV>
+template <int KV, bool RES>
 hipError_t launch_kv(const GemmArgs& a, hipStream_t s) {
-    static const hipError_t attr = hipFuncSetAttribute((const void*)qkv_gemm_kernel<KV>,
+    static const hipError_t attr = hipFuncSetAttribute((const void*)qkv_gemm_kernel<KV, RES>,
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
     if (attr != hipSuccess) return attr;
     const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-    hipLaunchKernelGGL(qkv_gemm_kernel<KV>, dim3(tiles), dim3(kThreads), LDS_BYTES, s, a);
+    hipLaunchKernelGGL((qkv_gemm_kernel<KV, RES>), dim3(tiles), dim3(kThreads), LDS_BYTES, s, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_qkv_gemm(const GemmArgs& a, hipStream_t s) {
+    if (a.res != nullptr) return a.kv_mode == 0 ? launch_kv<0, true>(a, s) : hipErrorInvalidValue;
     switch (a.kv_mode) {
-        case 0: return launch_kv<0>(a, s);
-        case 1: return launch_kv<1>(a, s);
-        case 2: return launch_kv<2>(a, s);
+        case 0: return launch_kv<0, false>(a, s);
+        case 1: return launch_kv<1, false>(a, s);
+        case 2: return launch_kv<2, false>(a, s);
         default: return hipErrorInvalidValue;
     }
 }
