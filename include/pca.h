@@ -104,6 +104,23 @@ pca_status pca_qkv_proj(const pca_bf16* x, int64_t ldx, const pca_bf16* w_t, int
                         void* stream);
 
 /*
+ * pca_rms_norm_qkv_proj -- the layer's input RMSNorm folded into the fused
+ *   QKV projection.  The data-flow article's §2.1 normalises the layer input
+ *   before the (h, 3h) projection; here the normalised activations are never
+ *   written: y[m, :] = inv_rms[m] * (x[m, :] * w_t^T) with
+ *   inv_rms[m] = 1 / sqrt(mean_k x[m, k]^2 + eps), applied to the fp32
+ *   accumulators before the single bf16 rounding.  The norm's gain g acts on
+ *   the K axis and is folded into the weight at load time, like the
+ *   transpose: w_t[n, k] = RNE_bf16(W[k, n] * g[k]).
+ *   x, w_t, y, M, N, K: as for pca_qkv_proj.
+ *   eps: >= 0.  inv_rms: device float[M], a caller-owned workspace that
+ *        receives 1/rms per row (the library allocates nothing).
+ */
+pca_status pca_rms_norm_qkv_proj(const pca_bf16* x, int64_t ldx, const pca_bf16* w_t, int64_t ldw, float eps,
+                                 float* inv_rms, pca_bf16* y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                                 void* stream);
+
+/*
  * pca_out_proj_residual -- the output projection and residual add that close
  *   the attention unit: out = res + o * w_t^T.  The data-flow article's §2.1
  *   writes the layer as residual = input, ..., attend, residual += attention

@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(PKG, "libpca.so")
 PCA_OK, PCA_ERR_INVALID_ARG, PCA_ERR_UNSUPPORTED, PCA_ERR_HIP = 0, 1, 2, 3
 DTYPES = {"bf16": 0, "fp8_e4m3": 1}
 
-EXPORTED = ("pca_kv_layout", "pca_qkv_proj", "pca_qkv_proj_kv_write", "pca_out_proj_residual", "pca_prefill_attention",
+EXPORTED = ("pca_kv_layout", "pca_qkv_proj", "pca_qkv_proj_kv_write", "pca_rms_norm_qkv_proj", "pca_out_proj_residual",
+            "pca_prefill_attention",
             "pca_prefill_attention_window", "pca_prefill_attention_paged", "pca_kv_cache_write",
             "pca_last_error", "pca_version")
 
@@ -58,6 +59,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                        vp, vp, vp, vp, i64, vp]
     lib.pca_qkv_proj_kv_write.argtypes = [vp, i64, vp, i64, vp, i64, i64, i64, i32, i32, i32, vp, i32,
                                           vp, i32, i32, i32, vp, vp, vp, vp, i64, vp]
+    lib.pca_rms_norm_qkv_proj.argtypes = [vp, i64, vp, i64, f32, vp, vp, i64, i64, i64, i64, vp]
     lib.pca_out_proj_residual.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, i64, i64, i64, vp]
     lib.pca_prefill_attention_window.argtypes = [vp, vp, vp, i64, i64, i64, vp, i32, i32, i64, i32, i32, i32,
                                                  f32, i32, i32, vp, i64, vp]
@@ -65,7 +67,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                                 vp, vp, i64, i32, i32, i32, f32, i32, vp, i64, vp]
     for fn in ("pca_kv_layout", "pca_qkv_proj", "pca_prefill_attention", "pca_kv_cache_write",
                "pca_qkv_proj_kv_write", "pca_prefill_attention_paged", "pca_prefill_attention_window",
-               "pca_out_proj_residual"):
+               "pca_out_proj_residual", "pca_rms_norm_qkv_proj"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.pca_last_error.restype = ctypes.c_char_p
     lib.pca_last_error.argtypes = []
@@ -120,6 +122,22 @@ def qkv_proj(x, w_t, y, stream=None):
     if w_t.shape[1] != K or tuple(y.shape) != (M, N):
         raise ValueError(f"shape mismatch: x {tuple(x.shape)}, w_t {tuple(w_t.shape)}, y {tuple(y.shape)}")
     _check("pca_qkv_proj", load().pca_qkv_proj(px, ldx, pw, ldw, py, ldy, M, N, K, _stream(stream)))
+    return y
+
+
+def rms_norm_qkv_proj(x, w_t_g, y, inv_rms, eps: float = 1e-6, stream=None):
+    """y = diag(inv_rms) (x @ w_t_g^T) with inv_rms[m] = 1/sqrt(mean x[m]^2 + eps)
+    written into the float32 device tensor inv_rms (M,); w_t_g is W^T with the
+    norm gain folded along K."""
+    px, ldx = _rows(x, "x")
+    pw, ldw = _rows(w_t_g, "w_t_g")
+    py, ldy = _rows(y, "y")
+    M, K = x.shape
+    N = w_t_g.shape[0]
+    if w_t_g.shape[1] != K or tuple(y.shape) != (M, N) or inv_rms.numel() < M:
+        raise ValueError(f"shape mismatch: x {tuple(x.shape)}, w_t_g {tuple(w_t_g.shape)}, y {tuple(y.shape)}")
+    _check("pca_rms_norm_qkv_proj", load().pca_rms_norm_qkv_proj(px, ldx, pw, ldw, float(eps), inv_rms.data_ptr(),
+                                                                 py, ldy, M, N, K, _stream(stream)))
     return y
 
 

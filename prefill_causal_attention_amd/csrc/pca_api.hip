@@ -151,6 +151,20 @@ pca_status pca_qkv_proj(const pca_bf16* x, int64_t ldx, const pca_bf16* w_t, int
     return hip_status(pca::launch_qkv_gemm(a, (hipStream_t)stream), "qkv_proj launch");
 }
 
+pca_status pca_rms_norm_qkv_proj(const pca_bf16* x, int64_t ldx, const pca_bf16* w_t, int64_t ldw, float eps,
+                                 float* inv_rms, pca_bf16* y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                                 void* stream) {
+    pca::GemmArgs a;
+    pca_status st = check_gemm(x, ldx, w_t, ldw, y, ldy, M, N, K, a);
+    if (st != PCA_OK) return st;
+    if (!inv_rms || ((uintptr_t)inv_rms & 3u)) return fail(PCA_ERR_INVALID_ARG, "inv_rms must be a 4-byte aligned device buffer");
+    if (!(eps >= 0.0f) || eps > 1e30f) return fail(PCA_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    a.row_scale = inv_rms;
+    st = hip_status(pca::launch_rms_stats(x, ldx, (int)M, (int)K, eps, inv_rms, (hipStream_t)stream), "rms stats launch");
+    if (st != PCA_OK) return st;
+    return hip_status(pca::launch_qkv_gemm(a, (hipStream_t)stream), "rms_norm_qkv_proj launch");
+}
+
 pca_status pca_out_proj_residual(const pca_bf16* o, int64_t ldo, const pca_bf16* w_t, int64_t ldw,
                                  const pca_bf16* res, int64_t ldr, pca_bf16* out, int64_t ldout,
                                  int64_t M, int64_t N, int64_t K, void* stream) {

@@ -42,9 +42,14 @@ struct GemmArgs {
     // optional residual: y = x w^T + res (res may be y itself)
     const uint16_t* res;
     int64_t ldr;
+    // optional per-row scale of the product (RMSNorm's 1 / rms): y[m] = row_scale[m] * (x w^T)[m]
+    const float* row_scale;
 };
 
 hipError_t launch_qkv_gemm(const GemmArgs& a, hipStream_t s);
+
+// inv_rms[m] = 1 / sqrt(mean_k x[m, k]^2 + eps) for the M rows of x (K columns)
+hipError_t launch_rms_stats(const uint16_t* x, int64_t ldx, int M, int K, float eps, float* inv_rms, hipStream_t s);
 
 struct AttnArgs {
     const uint16_t* q;

@@ -118,8 +118,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const uint16_t* p
 
 // KV = 0: plain GEMM; 1 / 2: the epilogue also writes y's K and V columns
 // into the bf16 / fp8 page pools.  RES: y = x w^T + res, the residual added
-// to the fp32 accumulators before the single bf16 rounding.
-template <int KV, bool RES>
+// to the fp32 accumulators before the single bf16 rounding.  RS: the fp32
+// accumulators of row m are scaled by row_scale[m] before that rounding.
+template <int KV, bool RES, bool RS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void qkv_gemm_kernel(GemmArgs a) {
     extern __shared__ __align__(16) uint16_t smem[];
@@ -273,10 +274,17 @@ void qkv_gemm_kernel(GemmArgs a) {
             *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>(stg + ml * 256 + ((c ^ (ml & 15)) * 16)) = rv;
         }
     }
+    // RMSNorm folded in: the row scale multiplies the fp32 accumulators (the
+    // norm's gain is folded into the weight's K axis at load time)
 #pragma unroll
-    for (int i = 0; i < FN; ++i)
+    for (int j = 0; j < FM; ++j) {
+        [[maybe_unused]] float rsc = 1.0f;
+        if constexpr (RS) {
+            const int m = m_lo + j * 32 + r32;
+            if (m < a.M) rsc = a.row_scale[m];
+        }
 #pragma unroll
-        for (int j = 0; j < FM; ++j)
+        for (int i = 0; i < FN; ++i)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int ml = j * 32 + r32, ci = i * 4 + g;
@@ -284,6 +292,9 @@ void qkv_gemm_kernel(GemmArgs a) {
                     reinterpret_cast<__attribute__((address_space(3))) u32x2_t*>(stg + ml * 256 + ((ci ^ (ml & 15)) * 16) + half * 8);
                 float t0 = acc[i][j][g * 4 + 0], t1 = acc[i][j][g * 4 + 1];
                 float t2 = acc[i][j][g * 4 + 2], t3 = acc[i][j][g * 4 + 3];
+                if constexpr (RS) {
+                    t0 *= rsc; t1 *= rsc; t2 *= rsc; t3 *= rsc;
+                }
                 if constexpr (RES) {
                     const u32x2_t rr = *slot;                // this lane's own 4 residual values
                     t0 += bf16_lo(rr[0]); t1 += bf16_hi(rr[0]);
@@ -291,6 +302,7 @@ void qkv_gemm_kernel(GemmArgs a) {
                 }
                 *slot = u32x2_t{pack_bf16x2(t0, t1), pack_bf16x2(t2, t3)};
             }
+    }
 
     // fused KV-cache write: where the lane's 8 columns go (the data-flow
     // article's §4.2 point -- the projection output goes straight into its
@@ -378,26 +390,57 @@ void qkv_gemm_kernel(GemmArgs a) {
 
 namespace {
 
-template <int KV, bool RES>
+// One wave per row: 16-byte loads along the row, fp32 sum of squares, a
+// cross-lane reduction, then 1 / sqrt(mean + eps) (IEEE division and square
+// root, no fast-math).  HBM-bound: reads x once.
+__global__ __launch_bounds__(256) void rms_stats_kernel(const uint16_t* x, int64_t ldx, int M, int K, float eps,
+                                                        float* inv_rms) {
+    const int lane = threadIdx.x & 63;
+    const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (m >= M) return;                                   // uniform per wave
+    const uint16_t* row = x + (int64_t)m * ldx;
+    float acc = 0.0f;
+    for (int k = lane * 8; k < K; k += 64 * 8) {          // K is a multiple of 8
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(row + k);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const float lo = bf16_lo(v[t]), hi = bf16_hi(v[t]);
+            acc = __builtin_fmaf(lo, lo, acc);
+            acc = __builtin_fmaf(hi, hi, acc);
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+    if (lane == 0) inv_rms[m] = 1.0f / __builtin_sqrtf(acc / (float)K + eps);
+}
+
+template <int KV, bool RES, bool RS>
 hipError_t launch_kv(const GemmArgs& a, hipStream_t s) {
-    static const hipError_t attr = hipFuncSetAttribute((const void*)qkv_gemm_kernel<KV, RES>,
+    static const hipError_t attr = hipFuncSetAttribute((const void*)qkv_gemm_kernel<KV, RES, RS>,
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
     if (attr != hipSuccess) return attr;
     const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-    hipLaunchKernelGGL((qkv_gemm_kernel<KV, RES>), dim3(tiles), dim3(kThreads), LDS_BYTES, s, a);
+    hipLaunchKernelGGL((qkv_gemm_kernel<KV, RES, RS>), dim3(tiles), dim3(kThreads), LDS_BYTES, s, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_qkv_gemm(const GemmArgs& a, hipStream_t s) {
-    if (a.res != nullptr) return a.kv_mode == 0 ? launch_kv<0, true>(a, s) : hipErrorInvalidValue;
+    if (a.res != nullptr)
+        return a.kv_mode == 0 && a.row_scale == nullptr ? launch_kv<0, true, false>(a, s) : hipErrorInvalidValue;
+    if (a.row_scale != nullptr) return a.kv_mode == 0 ? launch_kv<0, false, true>(a, s) : hipErrorInvalidValue;
     switch (a.kv_mode) {
-        case 0: return launch_kv<0, false>(a, s);
-        case 1: return launch_kv<1, false>(a, s);
-        case 2: return launch_kv<2, false>(a, s);
+        case 0: return launch_kv<0, false, false>(a, s);
+        case 1: return launch_kv<1, false, false>(a, s);
+        case 2: return launch_kv<2, false, false>(a, s);
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_rms_stats(const uint16_t* x, int64_t ldx, int M, int K, float eps, float* inv_rms, hipStream_t s) {
+    hipLaunchKernelGGL(rms_stats_kernel, dim3((uint32_t)((M + 3) / 4)), dim3(256), 0, s, x, ldx, M, K, eps, inv_rms);
+    return hipGetLastError();
 }
 
 }  // namespace pca
