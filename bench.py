@@ -270,6 +270,23 @@ def main():
             "flop_count": "exact causal pairs, 4*hd*n_head per (query, visible key)"}
         del pk, pv, pq, po
 
+        # the two ends of the attention unit: RMSNorm folded into the QKV GEMM
+        # (row statistics + scaled epilogue), and W_o with the residual add
+        inv_rms = torch.empty((T,), dtype=torch.float32, device=dev)
+        t_rms = timed(lambda: pca.rms_norm_qkv_proj(x, wt, y, inv_rms, eps=1e-6), args.extra_reps)
+        t_plain = timed(lambda: pca.qkv_proj(x, wt, y), args.extra_reps)
+        extras["rms_norm_qkv_proj"] = {"ms": t_rms, "qkv_proj_ms": t_plain,
+                                       "gemm_tflops": w.gemm_flops() / (t_rms * 1e-3) / 1e12}
+        gen.manual_seed(9003)
+        nq = w.n_head * w.head_dim
+        w_o = (torch.randn((w.h, nq), generator=gen, device=dev) * nq ** -0.5).to(torch.bfloat16)
+        res = torch.randn((T, w.h), generator=gen, device=dev).to(torch.bfloat16)
+        t_op = timed(lambda: pca.out_proj_residual(o, w_o, res, res), args.extra_reps)
+        oflop = 2.0 * T * nq * w.h
+        extras["out_proj_residual"] = {"ms": t_op, "flop": oflop, "tflops": oflop / (t_op * 1e-3) / 1e12,
+                                       "case": f"({T}, {nq}) @ W_o ({nq}, {w.h}) + residual, in place"}
+        del w_o, res, inv_rms
+
     att_flops = w.attention_flops()
     gemm_flops = w.gemm_flops()
     eb = 1 if fp8 else 2
