@@ -236,10 +236,13 @@ pca_status pca_prefill_attention_window(const pca_bf16* q, const pca_bf16* k, co
  *   ctx_lens: device int32[num_seqs], keys per sequence (prefix + chunk);
  *        clamped on the device to [Lq, max_pages_per_seq * 16].
  *        max_ctx_len >= every ctx_lens[b] (sizes the staged block-table row).
- *   block_table, max_pages_per_seq, page_size (16), k_cache, v_cache,
- *        num_pages: the pools of pca_kv_cache_write.  Only a bf16 cache is read
- *        (cache_dtype PCA_DTYPE_FP8_E4M3 gives PCA_ERR_UNSUPPORTED; k_scale and
- *        v_scale must be NULL).  Each pool must be smaller than 2 GiB.
+ *   block_table, max_pages_per_seq, page_size (16), cache_dtype, k_cache,
+ *        v_cache, k_scale, v_scale, num_pages: the pools of pca_kv_cache_write.
+ *        An fp8 cache is dequantised on load (tuning notes §3.3): each tile
+ *        of E4M3 codes is decoded, multiplied by its (token, kv head) scale
+ *        and rounded to bf16 on chip before the matrix products; k_scale and
+ *        v_scale must then be given (NULL for a bf16 cache).  Each pool must
+ *        be smaller than 2 GiB.
  *        Block-table entries outside [0, num_pages) give unspecified output,
  *        never an access outside the pools.
  *   head_dim 32, 64 or 128; causal must be 1.

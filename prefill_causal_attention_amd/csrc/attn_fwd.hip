@@ -91,6 +91,13 @@ struct Cfg {
     static constexpr int DMA_ITERS = (NBLK + kWaves - 1) / kWaves;
     static constexpr int DCH = HD / 16;                  // k16 steps over head_dim
     static constexpr int DB = HD / 32;                   // 32-row blocks of O^T
+    // fp8 pages: a tile of E4M3 codes (1 byte each) is staged behind the bf16
+    // buffers and converted into them by the wave that loaded it
+    static constexpr int T8 = BK * HD;                   // bytes of one fp8 tile
+    static constexpr int NB8 = T8 / 1024;                // 1 KiB DMA blocks per fp8 tile (<= 8 waves)
+    static constexpr int RPI8 = 1024 / HD;               // key rows per fp8 block
+    static constexpr int F8K0 = 4 * TILE, F8K1 = F8K0 + T8, F8V0 = F8K0 + 2 * T8, F8V1 = F8K0 + 3 * T8;
+    static constexpr int LDS_FP8 = 4 * TILE + 4 * T8;
     static_assert(VBUF1 + 3 * 16 * ROWB < 65536, "V reads use 16-bit DS immediate offsets");
 };
 
@@ -191,6 +198,8 @@ struct Params {
     const int32_t* ctx;
     uint32_t pool_bytes;
     int window;         // > 0: sliding window, row r sees keys r - window < c <= r
+    const float* k_scale;   // fp8 pages: per-(slot, kv head) scales [page][16][n_kv]
+    const float* v_scale;
 };
 
 constexpr uint32_t kOob = 0x80000000u;  // a buffer offset past every pool: loads return 0
@@ -245,7 +254,58 @@ __device__ __forceinline__ void dma_tile_paged(__amdgpu_buffer_rsrc_t r, int wav
     }
 }
 
-template <int HD, bool PAGED, bool WIN>
+// DMA of one fp8 tile (E4M3 codes) from a page pool into the staging buffer
+// `dst8`: wave w < NB8 loads block w, lane l the 16 codes of row
+// w * RPI8 + l / (HD/16), column chunk l % (HD/16); it also loads that row's
+// scale (0 for keys at or past Lk).  Returns the scale.
+template <int HD>
+__device__ __forceinline__ float dma_tile_fp8(__amdgpu_buffer_rsrc_t r, const float* scales, int wave, int lane,
+                                              int kbase, int Lk, int n_kv, int g, lds_char_t* dst8,
+                                              const __attribute__((address_space(3))) int32_t* lbt) {
+    using C = Cfg<HD>;
+    float sc = 0.0f;
+    if (wave < C::NB8) {
+        const int row = wave * C::RPI8 + lane / (HD / 16);
+        const int c = kbase + row;
+        uint32_t off = kOob;
+        if (c < Lk) {
+            const int64_t slot = (int64_t)lbt[c >> 4] * 16 + (c & 15);
+            off = (uint32_t)((slot * n_kv + g) * HD + (lane % (HD / 16)) * 16);
+            sc = scales[slot * n_kv + g];
+        }
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(dst8 + wave * 1024), 16, off, 0, 0, 0);
+    }
+    return sc;
+}
+
+// After the wave's own fp8 DMA has landed (vmcnt 0): decode its 16 codes
+// (OCP E4M3, exact in fp32), multiply by the row's scale, round to bf16 and
+// store them as two 16-byte chunks of the bf16 tile, with the K/V swizzle.
+template <int HD>
+__device__ __forceinline__ void convert_fp8(int wave, int lane, const lds_char_t* src8, lds_char_t* dst, float sc) {
+    using C = Cfg<HD>;
+    if (wave >= C::NB8) return;
+    const int row = wave * C::RPI8 + lane / (HD / 16);
+    const int ch = lane % (HD / 16);
+    const u32x4_t codes = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(src8 + wave * 1024 + lane * 16);
+    u32x4_t out[2];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)codes[t], false);
+        const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)codes[t], true);
+        out[t >> 1][(t & 1) * 2 + 0] = pack_bf16x2(a[0] * sc, a[1] * sc);
+        out[t >> 1][(t & 1) * 2 + 1] = pack_bf16x2(b[0] * sc, b[1] * sc);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int lc = ch * 2 + h;
+        *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>(dst + row * C::ROWB + ((lc ^ swz<HD>(row)) * 16)) = out[h];
+    }
+}
+
+// PAGED: 0 = K/V token-major rows of the chunk itself, 1 = bf16 page pools,
+// 2 = fp8 (E4M3 + per-row scale) page pools.
+template <int HD, int PAGED, bool WIN>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(Params p) {
     using C = Cfg<HD>;
@@ -288,7 +348,7 @@ void attn_fwd_kernel(Params p) {
     // keys: the chunk itself, or the cached prefix followed by the chunk; the
     // chunk's row r sits at key position pos0 + r
     int Lk = Lb;
-    if constexpr (PAGED) Lk = __builtin_amdgcn_readfirstlane(min(max(p.ctx[b], Lb), p.mp * 16));
+    if constexpr (PAGED != 0) Lk = __builtin_amdgcn_readfirstlane(min(max(p.ctx[b], Lb), p.mp * 16));
     const int pos0 = Lk - Lb;
     const int G = p.group;
     const int nqb = (Lb + BQ - 1) / BQ;
@@ -318,7 +378,7 @@ void attn_fwd_kernel(Params p) {
     // paged: first part of the sequence's block-table row (staged in LDS below)
     [[maybe_unused]] const int npg = (Lk + 15) >> 4;
     [[maybe_unused]] int32_t btv[kBtPerThread];
-    if constexpr (PAGED) {
+    if constexpr (PAGED != 0) {
 #pragma unroll
         for (int u = 0; u < kBtPerThread; ++u)
             btv[u] = u * kThreads + tid < npg ? p.bt[(int64_t)b * p.mp + u * kThreads + tid] : 0;
@@ -352,28 +412,58 @@ void attn_fwd_kernel(Params p) {
         dma_k[i] = (uint32_t)(((int64_t)row * p.ldk + g * HD + lch * 8) * 2);
         dma_v[i] = (uint32_t)(((int64_t)row * p.ldv + g * HD + lch * 8) * 2);
     }
-    // paged: the sequence's block-table row, staged in LDS behind the K/V buffers
+    // paged: the sequence's block-table row, staged in LDS behind the K/V
+    // buffers (and, for fp8 pages, behind the fp8 staging buffers)
+    constexpr int kBtOff = PAGED == 2 ? C::LDS_FP8 : C::LDS_BYTES;
     const __attribute__((address_space(3))) int32_t* lbt =
-        (const __attribute__((address_space(3))) int32_t*)(lds + C::LDS_BYTES);
+        (const __attribute__((address_space(3))) int32_t*)(lds + kBtOff);
     [[maybe_unused]] __amdgpu_buffer_rsrc_t rk, rv;
-    if constexpr (PAGED) {
+    if constexpr (PAGED != 0) {
         rk = make_rsrc(p.k, p.pool_bytes);
         rv = make_rsrc(p.v, p.pool_bytes);
         // the row was loaded into registers before the Q tile (both latencies overlap)
-        __attribute__((address_space(3))) int32_t* wbt = (__attribute__((address_space(3))) int32_t*)(lds + C::LDS_BYTES);
+        __attribute__((address_space(3))) int32_t* wbt = (__attribute__((address_space(3))) int32_t*)(lds + kBtOff);
 #pragma unroll
         for (int u = 0; u < kBtPerThread; ++u)
             if (u * kThreads + tid < npg) wbt[u * kThreads + tid] = btv[u];
         for (int i = kBtPerThread * kThreads + tid; i < npg; i += kThreads) wbt[i] = p.bt[(int64_t)b * p.mp + i];
         __syncthreads();
     }
+    // fp8 pages: the tiles this wave loaded last and still has to convert
+    // (fp8 staging buffer = bf16 buffer + the fixed distance below)
+    [[maybe_unused]] float pend_ks = 0.0f, pend_vs = 0.0f;
+    [[maybe_unused]] int pend_k = -1, pend_v = -1;   // bf16 buffer offsets, -1: nothing pending
+    auto f8_of = [](int buf) __attribute__((always_inline)) {
+        return buf == C::KBUF0 ? C::F8K0 : buf == C::KBUF1 ? C::F8K1 : buf == C::VBUF0 ? C::F8V0 : C::F8V1;
+    };
     auto issue_k = [&](int tile, int buf) __attribute__((always_inline)) {
-        if constexpr (PAGED) dma_tile_paged<HD>(rk, wave, lane, tile * BK, Lk, p.n_kv, g, lds + buf, lbt);
-        else dma_tile<HD>(p.k, p.ldk, s0, Lb, wave, tile * BK, lds + buf, dma_k);
+        if constexpr (PAGED == 2) {
+            pend_ks = dma_tile_fp8<HD>(rk, p.k_scale, wave, lane, tile * BK, Lk, p.n_kv, g, lds + f8_of(buf), lbt);
+            pend_k = buf;
+        } else if constexpr (PAGED == 1) {
+            dma_tile_paged<HD>(rk, wave, lane, tile * BK, Lk, p.n_kv, g, lds + buf, lbt);
+        } else {
+            dma_tile<HD>(p.k, p.ldk, s0, Lb, wave, tile * BK, lds + buf, dma_k);
+        }
     };
     auto issue_v = [&](int tile, int buf) __attribute__((always_inline)) {
-        if constexpr (PAGED) dma_tile_paged<HD>(rv, wave, lane, tile * BK, Lk, p.n_kv, g, lds + buf, lbt);
-        else dma_tile<HD>(p.v, p.ldv, s0, Lb, wave, tile * BK, lds + buf, dma_v);
+        if constexpr (PAGED == 2) {
+            pend_vs = dma_tile_fp8<HD>(rv, p.v_scale, wave, lane, tile * BK, Lk, p.n_kv, g, lds + f8_of(buf), lbt);
+            pend_v = buf;
+        } else if constexpr (PAGED == 1) {
+            dma_tile_paged<HD>(rv, wave, lane, tile * BK, Lk, p.n_kv, g, lds + buf, lbt);
+        } else {
+            dma_tile<HD>(p.v, p.ldv, s0, Lb, wave, tile * BK, lds + buf, dma_v);
+        }
+    };
+    // wait for this wave's loads; for fp8 pages also convert what it loaded
+    auto retire = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(kVmcnt0);
+        if constexpr (PAGED == 2) {
+            if (pend_k >= 0) convert_fp8<HD>(wave, lane, lds + f8_of(pend_k), lds + pend_k, pend_ks);
+            if (pend_v >= 0) convert_fp8<HD>(wave, lane, lds + f8_of(pend_v), lds + pend_v, pend_vs);
+            pend_k = pend_v = -1;
+        }
     };
 
     // ---- per-lane LDS read offsets
@@ -583,11 +673,11 @@ void attn_fwd_kernel(Params p) {
     auto tile = [&](int j, auto KCc, auto KNc, auto VCc, auto VNc) __attribute__((always_inline)) {
         if (!lead) issue_next(j, KCc, VNc);
         softmax_phase(j);
-        if (lead) __builtin_amdgcn_s_waitcnt(kVmcnt0);
+        if (lead) retire();
         wg_barrier();
         if (lead) issue_next(j, KCc, VNc);
         matrix_phase(j, KNc, VCc);
-        if (!lead) __builtin_amdgcn_s_waitcnt(kVmcnt0);
+        if (!lead) retire();
         wg_barrier();
     };
 
@@ -601,8 +691,9 @@ void attn_fwd_kernel(Params p) {
     // is computes its scores; group B waits one half-step
     issue_k(j0, C::KBUF0);
     issue_v(j0, C::VBUF0);
+    if constexpr (PAGED == 2) retire();   // fp8: K_j0 and V_j0 converted before K_j0+1 takes the pending slot
     if (j0 + 1 < ntiles) issue_k(j0 + 1, C::KBUF1);
-    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    retire();
     __syncthreads();
     if (wave_first == j0 && j0 < wave_ntiles) scores(K0{});
     if (!lead) wg_barrier();
@@ -637,7 +728,7 @@ void attn_fwd_kernel(Params p) {
 // largest dynamic LDS a workgroup may take (gfx950: 160 KiB per CU)
 constexpr int kMaxLds = 160 * 1024;
 
-template <int HD, bool PAGED, bool WIN>
+template <int HD, int PAGED, bool WIN>
 hipError_t launch_cfg(const AttnArgs& a, hipStream_t s) {
     using C = Cfg<HD>;
     static const hipError_t attr = hipFuncSetAttribute((const void*)attn_fwd_kernel<HD, PAGED, WIN>,
@@ -661,16 +752,18 @@ hipError_t launch_cfg(const AttnArgs& a, hipStream_t s) {
     p.mp = a.max_pages_per_seq;
     p.ctx = a.ctx_lens;
     p.window = a.window;
+    p.k_scale = a.k_scale;
+    p.v_scale = a.v_scale;
     p.pool_bytes = (uint32_t)a.pool_bytes;
-    size_t lds = C::LDS_BYTES;
-    if (PAGED) lds += (size_t)(((a.max_ctx + 15) / 16 + 3) / 4) * 16;   // the block-table row, int32
+    size_t lds = PAGED == 2 ? C::LDS_FP8 : C::LDS_BYTES;
+    if (PAGED != 0) lds += (size_t)(((a.max_ctx + 15) / 16 + 3) / 4) * 16;   // the block-table row, int32
     if (lds > (size_t)kMaxLds) return hipErrorInvalidValue;
     const int64_t grid = (int64_t)p.ntg * p.units;
     hipLaunchKernelGGL((attn_fwd_kernel<HD, PAGED, WIN>), dim3((uint32_t)grid), dim3(kThreads), lds, s, p);
     return hipGetLastError();
 }
 
-template <bool PAGED, bool WIN>
+template <int PAGED, bool WIN>
 hipError_t launch_hd(const AttnArgs& a, hipStream_t s) {
     switch (a.head_dim) {
         case 32: return launch_cfg<32, PAGED, WIN>(a, s);
@@ -683,8 +776,8 @@ hipError_t launch_hd(const AttnArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
-    if (a.block_table != nullptr) return launch_hd<true, false>(a, s);
-    return a.window > 0 ? launch_hd<false, true>(a, s) : launch_hd<false, false>(a, s);
+    if (a.block_table != nullptr) return a.k_scale != nullptr ? launch_hd<2, false>(a, s) : launch_hd<1, false>(a, s);
+    return a.window > 0 ? launch_hd<0, true>(a, s) : launch_hd<0, false>(a, s);
 }
 
 }  // namespace pca

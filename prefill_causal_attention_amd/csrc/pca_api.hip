@@ -297,10 +297,18 @@ pca_status pca_prefill_attention_paged(const pca_bf16* q, int64_t ldq, const int
     if (!supported_head_dim(head_dim))
         return fail(PCA_ERR_UNSUPPORTED, "head_dim %d not supported (32, 64 or 128)", head_dim);
     if (page_size != 16) return fail(PCA_ERR_UNSUPPORTED, "page_size must be 16 (got %d)", page_size);
-    if (cache_dtype == PCA_DTYPE_FP8_E4M3)
-        return fail(PCA_ERR_UNSUPPORTED, "an fp8 cache is not read by the paged attention (bf16 only)");
-    if (cache_dtype != PCA_DTYPE_BF16) return fail(PCA_ERR_UNSUPPORTED, "unknown cache dtype %d", (int)cache_dtype);
-    if (k_scale || v_scale) return fail(PCA_ERR_INVALID_ARG, "k_scale/v_scale must be NULL for a bf16 cache");
+    int64_t elem;
+    if (cache_dtype == PCA_DTYPE_BF16) {
+        if (k_scale || v_scale) return fail(PCA_ERR_INVALID_ARG, "k_scale/v_scale must be NULL for a bf16 cache");
+        elem = 2;
+    } else if (cache_dtype == PCA_DTYPE_FP8_E4M3) {
+        if (!k_scale || !v_scale) return fail(PCA_ERR_INVALID_ARG, "an fp8 cache needs k_scale and v_scale");
+        if (((uintptr_t)k_scale & 3u) || ((uintptr_t)v_scale & 3u))
+            return fail(PCA_ERR_INVALID_ARG, "k_scale/v_scale must be 4-byte aligned");
+        elem = 1;
+    } else {
+        return fail(PCA_ERR_UNSUPPORTED, "unknown cache dtype %d", (int)cache_dtype);
+    }
     pca_status st = check_batch(cu_seqlens_q, num_seqs, total_q);
     if (st != PCA_OK) return st;
     if (!(scale > 0.0f) || scale != scale || scale > 1e30f) return fail(PCA_ERR_INVALID_ARG, "scale must be finite and > 0");
@@ -314,9 +322,10 @@ pca_status pca_prefill_attention_paged(const pca_bf16* q, int64_t ldq, const int
     if (max_ctx_len < max_seqlen_q || (int64_t)max_ctx_len > (int64_t)max_pages_per_seq * page_size)
         return fail(PCA_ERR_INVALID_ARG, "max_ctx_len (%d) must be >= max_seqlen_q and <= max_pages_per_seq * page_size",
                     max_ctx_len);
-    const int64_t pool_bytes = num_pages * page_size * (int64_t)n_kv_head * head_dim * 2;
+    const int64_t pool_bytes = num_pages * page_size * (int64_t)n_kv_head * head_dim * elem;
     if (pool_bytes >= kMaxBufferBytes) return fail(PCA_ERR_UNSUPPORTED, "page pools of 2 GiB or more are not supported");
-    const int64_t lds = 4 * 64 * (int64_t)head_dim * 2 + (((int64_t)max_ctx_len + 15) / 16 + 3) / 4 * 16;
+    // LDS: 4 bf16 tiles (+ 4 fp8 staging tiles) + the staged block-table row
+    const int64_t lds = 4 * 64 * (int64_t)head_dim * (elem == 1 ? 3 : 2) + (((int64_t)max_ctx_len + 15) / 16 + 3) / 4 * 16;
     if (lds > 160 * 1024) return fail(PCA_ERR_UNSUPPORTED, "max_ctx_len %d too long for the staged block table", max_ctx_len);
     const int64_t longest = cu_seqlens_q ? (max_seqlen_q < total_q ? max_seqlen_q : total_q) : total_q;
     if (longest * ldq * 2 >= kMaxBufferBytes) return fail(PCA_ERR_UNSUPPORTED, "per-sequence q views beyond 2 GiB");
@@ -328,6 +337,7 @@ pca_status pca_prefill_attention_paged(const pca_bf16* q, int64_t ldq, const int
     a.scale = scale; a.o = o; a.ldo = ldo;
     a.block_table = block_table; a.max_pages_per_seq = max_pages_per_seq; a.ctx_lens = ctx_lens;
     a.max_ctx = max_ctx_len; a.pool_bytes = pool_bytes;
+    a.k_scale = elem == 1 ? k_scale : nullptr; a.v_scale = elem == 1 ? v_scale : nullptr;
     return hip_status(pca::launch_attention(a, (hipStream_t)stream), "prefill_attention_paged launch");
 }
 

@@ -72,6 +72,8 @@ struct AttnArgs {
     int max_ctx;
     int64_t pool_bytes;           // bytes of the K (and of the V) pool, < 2^31
     int window;                   // > 0: sliding window of that many keys (row r sees r - window < c <= r)
+    const float* k_scale;         // paged fp8 pools: per-(slot, kv head) scales; null for bf16 pools
+    const float* v_scale;
 };
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);

@@ -1,5 +1,5 @@
 """GPU parity of pca_prefill_attention_paged (a prefill chunk over its cached
-prefix) against the fp64 oracle, plus invariants run on the kernel itself:
+prefix, bf16 or fp8 pages) against the fp64 oracle, plus invariants run on the kernel itself:
 with no prefix it equals pca_prefill_attention bit for bit, and a chunk's rows
 equal the same rows of the whole sequence attended in one piece."""
 import numpy as np
@@ -120,14 +120,58 @@ def test_long_prefix_gqa_sampled():
     assert_close(got[rows], _oracle(c, rows=rows), "paged s=8192 chunk")
 
 
-def test_fp8_cache_rejected():
+def _case_fp8(seed, chunks, prefixes, H, Hk, hd, spare=3):
+    """As _case, with the keys quantised into fp8 pools (codes + scales) by the oracle."""
+    c = _case(seed, chunks, prefixes, H, Hk, hd, spare)
+    pages = c["kc"].shape[0]
+    kc, vc, ks, vs = kvcache.paged_write_fp8(c["kb"], c["vb"], c["cu_k"], c["bt"], pages)
+    c.update(kc=kc, vc=vc, ks=ks, vs=vs)
+    return c
+
+
+def _gpu_fp8(c, o_pad=8):
+    T = int(c["cu_q"][-1])
+    nq = c["H"] * c["hd"]
+    o = torch.full((T, nq + o_pad), float("nan"), dtype=torch.bfloat16, device="cuda")
+    d_bt = dev(torch.from_numpy(np.where(c["bt"] < 0, 0, c["bt"]).astype(np.int32)))
+    cu = dev(torch.from_numpy(c["cu_q"])) if len(c["ctx"]) > 1 else None
+    pca.prefill_attention_paged(dev(c["q"]), o[:, :nq], dev(torch.from_numpy(c["kc"])), dev(torch.from_numpy(c["vc"])),
+                                d_bt, dev(torch.from_numpy(c["ctx"])), c["H"], c["Hk"], c["hd"], cu_seqlens=cu,
+                                max_seqlen=int(np.diff(c["cu_q"]).max()), max_ctx=int(c["ctx"].max()),
+                                cache_dtype="fp8_e4m3", k_scale=dev(torch.from_numpy(c["ks"])),
+                                v_scale=dev(torch.from_numpy(c["vs"])))
+    torch.cuda.synchronize()
+    assert torch.isnan(o[:, nq:].float()).all(), "wrote outside the heads"
+    return o[:, :nq]
+
+
+def _oracle_fp8(c, rows=None):
+    qb = bits(c["q"]).reshape(-1, c["H"], c["hd"])
+    return PX.paged_prefix_attention(qb, c["cu_q"], c["ctx"], c["kc"], c["vc"], c["bt"], rows=rows,
+                                     k_scale=c["ks"], v_scale=c["vs"])
+
+
+@pytest.mark.parametrize("chunks,prefixes,H,Hk,hd", [
+    ([37], [100], 4, 2, 128),
+    ([129, 1, 50], [0, 300, 17], 8, 2, 128),
+    ([64], [64], 8, 2, 64),
+    ([200], [333], 4, 4, 32),
+    ([96, 40], [512, 1], 10, 2, 128),
+])
+def test_fp8_pages_parity(chunks, prefixes, H, Hk, hd):
+    """E4M3 pages dequantised on load (code x scale, bf16 on chip) against the
+    oracle's fp64 decode of the same codes and scales."""
     require_gpu()
-    q = torch.zeros((4, 128), dtype=torch.bfloat16, device="cuda")
-    kc = torch.zeros((2, 16, 1, 128), dtype=torch.uint8, device="cuda")
-    sc = torch.zeros((2, 16, 1), dtype=torch.float32, device="cuda")
-    bt = torch.zeros((1, 2), dtype=torch.int32, device="cuda")
-    ctx = torch.tensor([4], dtype=torch.int32, device="cuda")
-    with pytest.raises(pca.PcaError) as e:
-        pca.prefill_attention_paged(q, q.clone(), kc, kc, bt, ctx, 1, 1, 128, cache_dtype="fp8_e4m3",
-                                    k_scale=sc, v_scale=sc)
-    assert e.value.status == 2
+    c = _case_fp8(77, chunks, prefixes, H, Hk, hd)
+    say(f"prefill_attention_paged fp8 chunks={chunks} prefixes={prefixes} heads={H}/{Hk} hd={hd} seed=77")
+    got = _gpu_fp8(c).float().cpu().numpy()
+    assert_close(got, _oracle_fp8(c), "paged fp8")
+
+
+def test_fp8_pages_long_prefix_sampled():
+    """s = 32768-style long context: a 512-row chunk over a 16384-key fp8 prefix, GQA 40/8 hd128."""
+    require_gpu()
+    c = _case_fp8(78, [512], [16384], 40, 8, 128, spare=16)
+    got = _gpu_fp8(c).float().cpu().numpy()
+    rows = sample_rows(512, 32, 79, must=(0, 1, 63, 64, 511))
+    assert_close(got[rows], _oracle_fp8(c, rows=rows), "paged fp8 16k prefix")
