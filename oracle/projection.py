@@ -10,7 +10,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import bf16
+from . import bf16, fp8
 
 
 def qkv_projection(x_bits, w_bits) -> np.ndarray:
@@ -28,3 +28,15 @@ def projection_entries(x_bits, w_bits, rows, cols) -> np.ndarray:
 def projection_rows(x_bits, w_bits, rows) -> np.ndarray:
     """Whole rows of Y for the sampled token indices."""
     return bf16.to_f64(np.asarray(x_bits)[np.asarray(rows)]) @ bf16.to_f64(w_bits)
+
+
+def fp8_projection(xq, sx, wq, sw, rows=None) -> np.ndarray:
+    """FP8-operand projection ([P2] §2.3: fp8 inputs, wider accumulation) in
+    fp64: each operand row is its E4M3 codes decoded times its row scale
+    (rows of X are tokens, rows of W^T output features), then Y = Xd @ Wd^T."""
+    xq, sx = np.asarray(xq), np.asarray(sx, dtype=np.float64)
+    if rows is not None:
+        xq, sx = xq[np.asarray(rows)], sx[np.asarray(rows)]
+    xd = fp8.decode(xq) * sx[:, None]
+    wd = fp8.decode(np.asarray(wq)) * np.asarray(sw, dtype=np.float64)[:, None]
+    return xd @ wd.T

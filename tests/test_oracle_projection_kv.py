@@ -134,3 +134,37 @@ def test_workload_recipes():
     assert w3.attention_flops() == 2 * 8192 ** 2 * 128 * 32
     assert w3.n_qkv == 6144 and w3.num_pages == 512
     assert sorted(workloads.block_table(w3)[0].tolist()) == list(range(512))
+
+
+def test_fp8_projection_exact_small_values():
+    """Codes of small powers of two with power-of-two scales: the fp8 product is
+    the exact integer-like product of the decoded values."""
+    from oracle import fp8 as F
+    from oracle import projection as PJ
+    rng = np.random.default_rng(61)
+    table = {0x38: 1.0, 0x40: 2.0, 0x30: 0.5, 0xB8: -1.0, 0x00: 0.0}
+    codes = np.array(list(table), dtype=np.uint8)
+    xq = rng.choice(codes, (5, 32))
+    wq = rng.choice(codes, (7, 32))
+    sx = np.array([1, 2, 4, 0.5, 1], dtype=np.float32)
+    sw = np.array([1, 1, 2, 8, 0.25, 1, 1], dtype=np.float32)
+    xv = np.vectorize(table.get)(xq) * sx[:, None]
+    wv = np.vectorize(table.get)(wq) * sw[:, None]
+    assert np.array_equal(PJ.fp8_projection(xq, sx, wq, sw), xv @ wv.T)
+    assert np.array_equal(F.decode(codes), np.array(list(table.values())))
+
+
+def test_fp8_quantised_projection_close_to_exact():
+    """Row-quantised operands reproduce the fp64 product within the E4M3 step."""
+    from oracle import fp8 as F
+    from oracle import projection as PJ
+    rng = np.random.default_rng(62)
+    x = rng.standard_normal((16, 256)).astype(np.float32)
+    w = rng.standard_normal((24, 256)).astype(np.float32) / 16
+    xq, sx = F.quantize_rows(x)
+    wq, sw = F.quantize_rows(w)
+    exact = x.astype(np.float64) @ w.astype(np.float64).T
+    got = PJ.fp8_projection(xq, sx, wq, sw)
+    # each operand carries a relative error <= 2^-4 per element; the dot
+    # products of random signs average it down: a loose bound
+    assert np.max(np.abs(got - exact)) < 0.15 * np.max(np.abs(exact))
