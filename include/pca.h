@@ -104,6 +104,32 @@ pca_status pca_qkv_proj(const pca_bf16* x, int64_t ldx, const pca_bf16* w_t, int
                         void* stream);
 
 /*
+ * pca_quantize_rows_fp8 -- row-wise OCP E4M3 quantisation for fp8 GEMM
+ *   operands ("Prefill vs decode tuning notes" (hncyxsy.com/news/227904) §2.3:
+ *   FP8 inputs, wider accumulation), with the fp8 KV cache's rule: for each
+ *   row r, amax = max|x[r, :]|, scales[r] = amax / 448,
+ *   q[r, k] = E4M3_RNE_saturate(x[r, k] * (448 / amax)), binary32 RN steps;
+ *   amax == 0 gives scale 0 and codes of +-0.
+ *   x: device bf16, M rows of K elements (stride ldx); q: device uint8, M rows
+ *   (stride ldq, a multiple of 16); scales: device float[M].  K >= 16 and a
+ *   multiple of 16.  Use it on the activations (rows = tokens) and, once at
+ *   load time, on the pre-transposed weight (rows = output features).
+ */
+pca_status pca_quantize_rows_fp8(const pca_bf16* x, int64_t ldx, int64_t M, int64_t K, uint8_t* q, int64_t ldq,
+                                 float* scales, void* stream);
+
+/*
+ * pca_qkv_proj_fp8 -- the fused QKV projection on fp8 operands (tuning notes
+ *   §2.3):  y[m, n] = RNE_bf16(sx[m] * sw[n] * sum_k dec(xq[m, k]) * dec(wq[n, k]))
+ *   with fp32 accumulation on gfx950's fp8 matrix cores (twice the bf16 rate).
+ *   xq, sx: the rows of x from pca_quantize_rows_fp8; wq, sw: the rows of
+ *   w^T (N, K) likewise.  y: device bf16, M rows of N (stride ldy).  K >= 16
+ *   and a multiple of 16; ldxq, ldwq multiples of 16.
+ */
+pca_status pca_qkv_proj_fp8(const uint8_t* xq, int64_t ldxq, const float* sx, const uint8_t* wq, int64_t ldwq,
+                            const float* sw, pca_bf16* y, int64_t ldy, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
  * pca_rms_norm_qkv_proj -- the layer's input RMSNorm folded into the fused
  *   QKV projection.  The data-flow article's §2.1 normalises the layer input
  *   before the (h, 3h) projection; here the normalised activations are never

@@ -18,6 +18,7 @@ PCA_OK, PCA_ERR_INVALID_ARG, PCA_ERR_UNSUPPORTED, PCA_ERR_HIP = 0, 1, 2, 3
 DTYPES = {"bf16": 0, "fp8_e4m3": 1}
 
 EXPORTED = ("pca_kv_layout", "pca_qkv_proj", "pca_qkv_proj_kv_write", "pca_rms_norm_qkv_proj", "pca_out_proj_residual",
+            "pca_quantize_rows_fp8", "pca_qkv_proj_fp8",
             "pca_prefill_attention",
             "pca_prefill_attention_window", "pca_prefill_attention_paged", "pca_kv_cache_write",
             "pca_last_error", "pca_version")
@@ -59,6 +60,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                        vp, vp, vp, vp, i64, vp]
     lib.pca_qkv_proj_kv_write.argtypes = [vp, i64, vp, i64, vp, i64, i64, i64, i32, i32, i32, vp, i32,
                                           vp, i32, i32, i32, vp, vp, vp, vp, i64, vp]
+    lib.pca_quantize_rows_fp8.argtypes = [vp, i64, i64, i64, vp, i64, vp, vp]
+    lib.pca_qkv_proj_fp8.argtypes = [vp, i64, vp, vp, i64, vp, vp, i64, i64, i64, i64, vp]
     lib.pca_rms_norm_qkv_proj.argtypes = [vp, i64, vp, i64, f32, vp, vp, i64, i64, i64, i64, vp]
     lib.pca_out_proj_residual.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, i64, i64, i64, vp]
     lib.pca_prefill_attention_window.argtypes = [vp, vp, vp, i64, i64, i64, vp, i32, i32, i64, i32, i32, i32,
@@ -67,7 +70,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                                 vp, vp, i64, i32, i32, i32, f32, i32, vp, i64, vp]
     for fn in ("pca_kv_layout", "pca_qkv_proj", "pca_prefill_attention", "pca_kv_cache_write",
                "pca_qkv_proj_kv_write", "pca_prefill_attention_paged", "pca_prefill_attention_window",
-               "pca_out_proj_residual", "pca_rms_norm_qkv_proj"):
+               "pca_out_proj_residual", "pca_rms_norm_qkv_proj", "pca_quantize_rows_fp8", "pca_qkv_proj_fp8"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.pca_last_error.restype = ctypes.c_char_p
     lib.pca_last_error.argtypes = []
@@ -122,6 +125,33 @@ def qkv_proj(x, w_t, y, stream=None):
     if w_t.shape[1] != K or tuple(y.shape) != (M, N):
         raise ValueError(f"shape mismatch: x {tuple(x.shape)}, w_t {tuple(w_t.shape)}, y {tuple(y.shape)}")
     _check("pca_qkv_proj", load().pca_qkv_proj(px, ldx, pw, ldw, py, ldy, M, N, K, _stream(stream)))
+    return y
+
+
+def quantize_rows_fp8(x, q, scales, stream=None):
+    """Row-wise E4M3 codes of the bf16 2-D view x into the uint8 view q, with
+    the per-row scales (float32, (M,))."""
+    px, ldx = _rows(x, "x")
+    pq, ldq = _rows(q, "q")
+    M, K = x.shape
+    if tuple(q.shape) != (M, K) or scales.numel() < M:
+        raise ValueError(f"shape mismatch: x {tuple(x.shape)}, q {tuple(q.shape)}")
+    _check("pca_quantize_rows_fp8", load().pca_quantize_rows_fp8(px, ldx, M, K, pq, ldq, scales.data_ptr(),
+                                                                 _stream(stream)))
+    return q
+
+
+def qkv_proj_fp8(xq, sx, wq, sw, y, stream=None):
+    """y = diag(sx) (dec(xq) @ dec(wq)^T) diag(sw) on fp8 matrix cores, bf16 out."""
+    pxq, ldxq = _rows(xq, "xq")
+    pwq, ldwq = _rows(wq, "wq")
+    py, ldy = _rows(y, "y")
+    M, K = xq.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K or tuple(y.shape) != (M, N) or sx.numel() < M or sw.numel() < N:
+        raise ValueError(f"shape mismatch: xq {tuple(xq.shape)}, wq {tuple(wq.shape)}, y {tuple(y.shape)}")
+    _check("pca_qkv_proj_fp8", load().pca_qkv_proj_fp8(pxq, ldxq, sx.data_ptr(), pwq, ldwq, sw.data_ptr(), py, ldy,
+                                                       M, N, K, _stream(stream)))
     return y
 
 

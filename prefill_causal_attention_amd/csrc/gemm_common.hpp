@@ -1,0 +1,94 @@
+// Shared pieces of the two MFMA GEMMs (bf16 and fp8 operands): tile
+// geometry, the LDS swizzle, inline-asm LDS reads and waits, the barrier, the
+// XCD-aware tile order and wave-uniform buffer resources.  Both kernels keep
+// K steps of 128 bytes per operand row (64 bf16 or 128 fp8 elements), so
+// their DMA and LDS layouts are byte-identical.
+#pragma once
+
+#include "pca_device.hpp"
+
+#include <utility>
+
+namespace pca {
+namespace gemm {
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
+
+constexpr int BM = 256, BN = 256;
+constexpr int kThreads = 256;
+constexpr int FN = 4, FM = 4;                 // 32x32 blocks per wave (n, m)
+constexpr int ROWB = 128;                     // bytes per tile row (one K step: 64 bf16 or 128 fp8)
+constexpr int TILE_B = 256 * ROWB;            // 32 KiB: one operand tile
+constexpr int STAGE_B = 2 * TILE_B;           // W tile, then X tile
+constexpr int LDS_BYTES = 2 * STAGE_B;        // 128 KiB
+constexpr int DMA_PER_TILE = TILE_B / 1024;   // 32 one-KiB DMA blocks per operand tile
+constexpr int DMA_PER_WAVE = DMA_PER_TILE / 4;  // 8 per operand per wave
+constexpr int kGroupM = 8;
+constexpr uint32_t kOob = 0x80000000u;        // an offset past every buffer: loads return 0
+
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+__device__ inline int swz(int row) { return (row >> 1) & 7; }
+
+// s_waitcnt immediate waiting for vmcnt <= n only (gfx9 encoding: vmcnt in
+// bits [15:14] and [3:0]; expcnt 7 and lgkmcnt 15 mean "no wait")
+constexpr int vmcnt_imm(int n) { return ((n & 0x30) << 10) | (n & 0xF) | 0x0F70; }
+static_assert(vmcnt_imm(0) == 0x0F70 && vmcnt_imm(16) == 0x4F70, "s_waitcnt encoding");
+
+template <int OFF>
+__device__ __forceinline__ u32x4_t lds_read_b128(uint32_t addr) {
+    static_assert(OFF >= 0 && OFF < 65536, "DS offset field is 16 bits");
+    u32x4_t r;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+    return r;
+}
+
+// Wait until at most N LDS operations are outstanding (LDS returns in order);
+// the fragments pass through the asm so their consumers stay after the wait.
+template <int N>
+__device__ __forceinline__ void lds_wait8(u32x4_t (&f)[8]) {
+    asm volatile("s_waitcnt lgkmcnt(%8)"
+                 : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(f[4]), "+v"(f[5]), "+v"(f[6]), "+v"(f[7])
+                 : "n"(N));
+}
+
+// Workgroup barrier with no implied waits: the operand DMA of the next K step
+// stays in flight across it.  All LDS reads are inline asm retired by explicit
+// lgkmcnt waits, and the DMA by explicit vmcnt waits, before a barrier that
+// needs them; the memory clobber and scheduling barriers pin the order.
+__device__ __forceinline__ void wg_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+__device__ inline void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
+    int total = tiles_m * tiles_n;
+    int id = blockIdx.x;
+    if (total % kNumXcd == 0) id = (id % kNumXcd) * (total / kNumXcd) + id / kNumXcd;
+    int per_group = kGroupM * tiles_n;
+    int group = id / per_group;
+    int first_m = group * kGroupM;
+    int gsize = min(tiles_m - first_m, kGroupM);
+    int in_group = id - group * per_group;
+    tm = first_m + in_group % gsize;
+    tn = in_group / gsize;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* p, int64_t bytes) {
+    const uint64_t b = (uint64_t)p;
+    const uint64_t ub = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(b >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    return make_rsrc((const void*)ub, (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes));
+}
+
+}  // namespace gemm
+}  // namespace pca

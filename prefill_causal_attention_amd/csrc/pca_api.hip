@@ -151,6 +151,38 @@ pca_status pca_qkv_proj(const pca_bf16* x, int64_t ldx, const pca_bf16* w_t, int
     return hip_status(pca::launch_qkv_gemm(a, (hipStream_t)stream), "qkv_proj launch");
 }
 
+pca_status pca_quantize_rows_fp8(const pca_bf16* x, int64_t ldx, int64_t M, int64_t K, uint8_t* q, int64_t ldq,
+                                 float* scales, void* stream) {
+    if (!x || !q || !scales) return fail(PCA_ERR_INVALID_ARG, "null x, q or scales");
+    if (!aligned16(x) || !aligned16(q) || ((uintptr_t)scales & 3u))
+        return fail(PCA_ERR_INVALID_ARG, "x and q must be 16-byte aligned, scales 4-byte aligned");
+    if (M < 1 || K < 16 || K % 16 != 0 || M > INT32_MAX || K > INT32_MAX)
+        return fail(PCA_ERR_INVALID_ARG, "need M >= 1 and K >= 16, K %% 16 == 0 (M=%lld K=%lld)", (long long)M, (long long)K);
+    if (ldx < K || ldq < K || ldx % 8 || ldq % 16)
+        return fail(PCA_ERR_INVALID_ARG, "ldx >= K (multiple of 8) and ldq >= K (multiple of 16) required");
+    return hip_status(pca::launch_quantize_rows(x, ldx, (int)M, (int)K, q, ldq, scales, (hipStream_t)stream),
+                      "quantize_rows_fp8 launch");
+}
+
+pca_status pca_qkv_proj_fp8(const uint8_t* xq, int64_t ldxq, const float* sx, const uint8_t* wq, int64_t ldwq,
+                            const float* sw, pca_bf16* y, int64_t ldy, int64_t M, int64_t N, int64_t K, void* stream) {
+    if (!xq || !sx || !wq || !sw || !y) return fail(PCA_ERR_INVALID_ARG, "null xq, sx, wq, sw or y");
+    if (!aligned16(xq) || !aligned16(wq) || !aligned16(y) || ((uintptr_t)sx & 3u) || ((uintptr_t)sw & 3u))
+        return fail(PCA_ERR_INVALID_ARG, "xq, wq, y must be 16-byte aligned, sx and sw 4-byte aligned");
+    if (M < 1 || N < 1 || K < 16 || K % 16 != 0)
+        return fail(PCA_ERR_INVALID_ARG, "need M >= 1, N >= 1, K >= 16 and K %% 16 == 0 (M=%lld N=%lld K=%lld)",
+                    (long long)M, (long long)N, (long long)K);
+    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return fail(PCA_ERR_INVALID_ARG, "M, N, K must fit in int32");
+    if (ldxq < K || ldwq < K || ldy < N || ldxq % 16 || ldwq % 16 || ldy % 8)
+        return fail(PCA_ERR_INVALID_ARG, "ldxq, ldwq >= K (multiples of 16), ldy >= N (multiple of 8) required");
+    if (256 * ldxq >= kMaxBufferBytes || 256 * ldwq >= kMaxBufferBytes)
+        return fail(PCA_ERR_UNSUPPORTED, "row stride too large for a 256-row tile view");
+    pca::Fp8GemmArgs a;
+    a.x = xq; a.ldx = ldxq; a.sx = sx; a.w = wq; a.ldw = ldwq; a.sw = sw; a.y = y; a.ldy = ldy;
+    a.M = (int)M; a.N = (int)N; a.K = (int)K;
+    return hip_status(pca::launch_gemm_fp8(a, (hipStream_t)stream), "qkv_proj_fp8 launch");
+}
+
 pca_status pca_rms_norm_qkv_proj(const pca_bf16* x, int64_t ldx, const pca_bf16* w_t, int64_t ldw, float eps,
                                  float* inv_rms, pca_bf16* y, int64_t ldy, int64_t M, int64_t N, int64_t K,
                                  void* stream) {

@@ -48,6 +48,25 @@ struct GemmArgs {
 
 hipError_t launch_qkv_gemm(const GemmArgs& a, hipStream_t s);
 
+// fp8 GEMM: y[m, n] = RNE_bf16(sx[m] * sw[n] * sum_k dec(x[m, k]) dec(w[n, k])), E4M3 codes
+struct Fp8GemmArgs {
+    const uint8_t* x;
+    int64_t ldx;
+    const float* sx;
+    const uint8_t* w;   // (N, K) row-major codes
+    int64_t ldw;
+    const float* sw;
+    uint16_t* y;
+    int64_t ldy;
+    int M, N, K;
+};
+
+hipError_t launch_gemm_fp8(const Fp8GemmArgs& a, hipStream_t s);
+
+// Row-wise E4M3 quantisation (absmax scale per row), the fp8 KV cache's rule
+hipError_t launch_quantize_rows(const uint16_t* x, int64_t ldx, int M, int K, uint8_t* q, int64_t ldq, float* scales,
+                                hipStream_t s);
+
 // inv_rms[m] = 1 / sqrt(mean_k x[m, k]^2 + eps) for the M rows of x (K columns)
 hipError_t launch_rms_stats(const uint16_t* x, int64_t ldx, int M, int K, float eps, float* inv_rms, hipStream_t s);
 
