@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA (published)
 KV_SETS = 8                    # rotating buffer sets for the cold KV-write timing
 METRIC = "prefill attention TFLOPS + % bf16 MFMA peak, s=8192 GQA 32q/8kv hd128"
 
@@ -286,6 +287,20 @@ def main():
         extras["out_proj_residual"] = {"ms": t_op, "flop": oflop, "tflops": oflop / (t_op * 1e-3) / 1e12,
                                        "case": f"({T}, {nq}) @ W_o ({nq}, {w.h}) + residual, in place"}
         del w_o, res, inv_rms
+
+        # fp8 operands for the projection: W^T quantised once (load time),
+        # X quantised per step, then the GEMM on the fp8 matrix cores
+        xq = torch.empty((T, w.h), dtype=torch.uint8, device=dev)
+        sx = torch.empty((T,), dtype=torch.float32, device=dev)
+        wq = torch.empty((w.n_qkv, w.h), dtype=torch.uint8, device=dev)
+        sw = torch.empty((w.n_qkv,), dtype=torch.float32, device=dev)
+        pca.quantize_rows_fp8(wt, wq, sw)
+        t_q = timed(lambda: pca.quantize_rows_fp8(x, xq, sx), args.extra_reps)
+        t_g8 = timed(lambda: pca.qkv_proj_fp8(xq, sx, wq, sw, y), args.extra_reps)
+        g8 = w.gemm_flops() / (t_g8 * 1e-3) / 1e12
+        extras["qkv_proj_fp8"] = {"quantize_x_ms": t_q, "gemm_ms": t_g8, "gemm_tflops": g8,
+                                  "frac_fp8_peak": g8 / PEAK_FP8_TFLOPS}
+        del xq, sx, wq, sw
 
     att_flops = w.attention_flops()
     gemm_flops = w.gemm_flops()
