@@ -329,7 +329,7 @@ def main():
     }
     traffic = measured_traffic(w.name)
     roofline = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": tflops / PEAK_BF16_TFLOPS, "traffic": traffic, "kernel": f"attn_fwd_kernel<{w.head_dim}, false>",
+                "frac": tflops / PEAK_BF16_TFLOPS, "traffic": traffic, "kernel": f"attn_fwd_kernel<{w.head_dim}, 0, false>",
                 "flop_per_launch": att_flops, "avg_launch_ms": a_ms}
     out = {
         "metric": METRIC,
