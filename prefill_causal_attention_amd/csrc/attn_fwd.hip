@@ -384,22 +384,7 @@ void attn_fwd_kernel(Params p) {
             btv[u] = u * kThreads + tid < npg ? p.bt[(int64_t)b * p.mp + u * kThreads + tid] : 0;
     }
 
-    // ---- Q tile in registers: B operand of S^T = K Q^T (column = query r32)
-    bf16x8_t qreg[C::DCH];
-    {
-        const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + s0 * p.ldq, (uint32_t)((int64_t)Lb * p.ldq * 2));
-#pragma unroll
-        for (int dc = 0; dc < C::DCH; ++dc) {
-            const uint32_t off = (uint32_t)(((int64_t)(q0 + r32) * p.ldq + head * HD + dc * 16 + half * 8) * 2);
-            // scale * log2(e) folded into Q once (then rounded to bf16), so the
-            // scores come out of the MFMA in log2 units
-            const u32x4_t raw = buf_load16(rq, off);
-            u32x4_t qs;
-#pragma unroll
-            for (int t2 = 0; t2 < 4; ++t2) qs[t2] = pack_bf16x2(bf16_lo(raw[t2]) * p.c, bf16_hi(raw[t2]) * p.c);
-            qreg[dc] = as_bf16x8(qs);
-        }
-    }
+    bf16x8_t qreg[C::DCH];   // the Q tile (loaded in the prologue)
 
     // ---- DMA lane offsets: lane l writes bytes [16 l, 16 l + 16) of a 1 KiB block,
     // i.e. row l / NC, physical chunk l % NC, so it fetches the logical chunk the
@@ -693,6 +678,24 @@ void attn_fwd_kernel(Params p) {
     issue_v(j0, C::VBUF0);
     if constexpr (PAGED == 2) retire();   // fp8: K_j0 and V_j0 converted before K_j0+1 takes the pending slot
     if (j0 + 1 < ntiles) issue_k(j0 + 1, C::KBUF1);
+
+    // ---- Q tile in registers (its loads overlap the first tiles' DMA): B
+    // operand of S^T = K Q^T (column = query r32)
+    {
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + s0 * p.ldq, (uint32_t)((int64_t)Lb * p.ldq * 2));
+#pragma unroll
+        for (int dc = 0; dc < C::DCH; ++dc) {
+            const uint32_t off = (uint32_t)(((int64_t)(q0 + r32) * p.ldq + head * HD + dc * 16 + half * 8) * 2);
+            // scale * log2(e) folded into Q once (then rounded to bf16), so the
+            // scores come out of the MFMA in log2 units
+            const u32x4_t raw = buf_load16(rq, off);
+            u32x4_t qs;
+#pragma unroll
+            for (int t2 = 0; t2 < 4; ++t2) qs[t2] = pack_bf16x2(bf16_lo(raw[t2]) * p.c, bf16_hi(raw[t2]) * p.c);
+            qreg[dc] = as_bf16x8(qs);
+        }
+    }
+
     retire();
     __syncthreads();
     if (wave_first == j0 && j0 < wave_ntiles) scores(K0{});
