@@ -312,6 +312,19 @@ pca_status pca_kv_cache_write(const pca_bf16* k, const pca_bf16* v, int64_t ldk,
                               void* k_cache, void* v_cache, float* k_scale, float* v_scale,
                               int64_t num_pages, void* stream);
 
+/*
+ * pca_e4m3_encode -- codes[i] = E4M3_RNE_saturate(x[i]) for i < n: the OCP
+ *   E4M3 encoder behind every fp8 result of this library (the KV cache of the
+ *   tuning notes §3.3 and the fp8 operands of §2.3), as a plain elementwise op
+ *   (e.g. for values already divided by a caller's own scale).  Round to
+ *   nearest even; finite magnitudes above 448 give the largest normal code
+ *   (0x7E, or 0xFE when negative); the sign bit is kept (-0 gives 0x80).
+ *   NaN inputs give unspecified codes.
+ *   x: device float[n], 16-byte aligned; codes: device uint8[n], 4-byte
+ *   aligned, must not overlap x.  n == 0 is a no-op (NULL buffers allowed).
+ */
+pca_status pca_e4m3_encode(const float* x, uint8_t* codes, int64_t n, void* stream);
+
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char* pca_last_error(void);
 

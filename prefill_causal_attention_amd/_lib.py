@@ -18,7 +18,7 @@ PCA_OK, PCA_ERR_INVALID_ARG, PCA_ERR_UNSUPPORTED, PCA_ERR_HIP = 0, 1, 2, 3
 DTYPES = {"bf16": 0, "fp8_e4m3": 1}
 
 EXPORTED = ("pca_kv_layout", "pca_qkv_proj", "pca_qkv_proj_kv_write", "pca_rms_norm_qkv_proj", "pca_out_proj_residual",
-            "pca_quantize_rows_fp8", "pca_qkv_proj_fp8",
+            "pca_quantize_rows_fp8", "pca_qkv_proj_fp8", "pca_e4m3_encode",
             "pca_prefill_attention",
             "pca_prefill_attention_window", "pca_prefill_attention_paged", "pca_kv_cache_write",
             "pca_last_error", "pca_version")
@@ -61,6 +61,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pca_qkv_proj_kv_write.argtypes = [vp, i64, vp, i64, vp, i64, i64, i64, i32, i32, i32, vp, i32,
                                           vp, i32, i32, i32, vp, vp, vp, vp, i64, vp]
     lib.pca_quantize_rows_fp8.argtypes = [vp, i64, i64, i64, vp, i64, vp, vp]
+    lib.pca_e4m3_encode.argtypes = [vp, vp, i64, vp]
     lib.pca_qkv_proj_fp8.argtypes = [vp, i64, vp, vp, i64, vp, vp, i64, i64, i64, i64, vp]
     lib.pca_rms_norm_qkv_proj.argtypes = [vp, i64, vp, i64, f32, vp, vp, i64, i64, i64, i64, vp]
     lib.pca_out_proj_residual.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, i64, i64, i64, vp]
@@ -70,7 +71,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                                 vp, vp, i64, i32, i32, i32, f32, i32, vp, i64, vp]
     for fn in ("pca_kv_layout", "pca_qkv_proj", "pca_prefill_attention", "pca_kv_cache_write",
                "pca_qkv_proj_kv_write", "pca_prefill_attention_paged", "pca_prefill_attention_window",
-               "pca_out_proj_residual", "pca_rms_norm_qkv_proj", "pca_quantize_rows_fp8", "pca_qkv_proj_fp8"):
+               "pca_out_proj_residual", "pca_rms_norm_qkv_proj", "pca_quantize_rows_fp8", "pca_qkv_proj_fp8",
+               "pca_e4m3_encode"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.pca_last_error.restype = ctypes.c_char_p
     lib.pca_last_error.argtypes = []
@@ -139,6 +141,17 @@ def quantize_rows_fp8(x, q, scales, stream=None):
     _check("pca_quantize_rows_fp8", load().pca_quantize_rows_fp8(px, ldx, M, K, pq, ldq, scales.data_ptr(),
                                                                  _stream(stream)))
     return q
+
+
+def e4m3_encode(x, codes, stream=None):
+    """E4M3 codes (RNE, saturating at +-448) of the contiguous float32 tensor x
+    into the contiguous uint8 tensor codes of the same number of elements."""
+    if not x.is_contiguous() or not codes.is_contiguous() or codes.numel() != x.numel():
+        raise ValueError("x and codes must be contiguous with the same number of elements")
+    if x.element_size() != 4 or codes.element_size() != 1:
+        raise ValueError("x must be float32 and codes uint8")
+    _check("pca_e4m3_encode", load().pca_e4m3_encode(x.data_ptr(), codes.data_ptr(), x.numel(), _stream(stream)))
+    return codes
 
 
 def qkv_proj_fp8(xq, sx, wq, sw, y, stream=None):

@@ -237,14 +237,8 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t* x, i
     const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
     for (int k = lane * 8; k < K; k += 64 * 8) {
         const u32x4_t v = *reinterpret_cast<const u32x4_t*>(row + k);
-        uint32_t lo = 0, hi = 0;
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            lo |= e4m3_rne_sat(bf16_lo(v[t]) * inv) << (16 * t);
-            lo |= e4m3_rne_sat(bf16_hi(v[t]) * inv) << (16 * t + 8);
-            hi |= e4m3_rne_sat(bf16_lo(v[2 + t]) * inv) << (16 * t);
-            hi |= e4m3_rne_sat(bf16_hi(v[2 + t]) * inv) << (16 * t + 8);
-        }
+        const uint32_t lo = e4m3x4(bf16_lo(v[0]) * inv, bf16_hi(v[0]) * inv, bf16_lo(v[1]) * inv, bf16_hi(v[1]) * inv);
+        const uint32_t hi = e4m3x4(bf16_lo(v[2]) * inv, bf16_hi(v[2]) * inv, bf16_lo(v[3]) * inv, bf16_hi(v[3]) * inv);
         *reinterpret_cast<u32x2_t*>(q + (int64_t)m * ldq + k) = u32x2_t{lo, hi};
     }
     if (lane == 0) scales[m] = amax / 448.0f;

@@ -43,21 +43,18 @@ __device__ inline int64_t token_slot(const KvWriteArgs& a, int64_t t) {
     return (int64_t)page * a.page_size + (pos % a.page_size);
 }
 
-// OCP E4M3 encoding of a binary32 value, round to nearest even, finite
-// overflow saturating to +-448; the sign bit is copied from y.  Branch-free:
-// below 2^-6 the code is the subnormal count rint(|y| * 2^9) (exact scaling,
-// ties to even); from there the 3 kept mantissa bits are rounded to nearest
-// even in the integer domain and the exponent rebiased from 127 to 7.
-__device__ inline uint32_t e4m3_rne_sat(float y) {
-    const uint32_t u = __builtin_bit_cast(uint32_t, y);
-    const uint32_t sign = (u >> 24) & 0x80u;
-    const float a = __builtin_fabsf(y);
-    const uint32_t ua = u & 0x7FFFFFFFu;
-    const uint32_t sub = (uint32_t)__builtin_rintf(a * 512.0f);
-    const uint32_t nrm = ((ua + 0x7FFFFu + ((ua >> 20) & 1u)) >> 20) - (120u << 3);
-    uint32_t code = a < 0.015625f ? sub : nrm;
-    code = (a >= 448.0f || code > 0x7Eu) ? 0x7Eu : code;
-    return sign | code;
+// OCP E4M3 codes of four binary32 values packed into a word (byte j holds the
+// code of the j-th argument): round to nearest even, finite overflow
+// saturating to +-448, the sign copied (so -0 gives 0x80).  gfx950's
+// conversion instruction rounds to nearest even but turns magnitudes above 464
+// into NaN, so each value is first clamped to [-448, 448]; values in
+// (448, 464] round to 448 either way, which makes the pair saturating over
+// every finite input.  NaN inputs are outside the contract.
+__device__ inline uint32_t e4m3x4(float a, float b, float c, float d) {
+    const auto cl = [](float x) { return __builtin_amdgcn_fmed3f(x, -448.0f, 448.0f); };
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(cl(a), cl(b), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(cl(c), cl(d), w, true);
+    return (uint32_t)w;
 }
 
 // max over the R-lane group (R = 4, 8 or 16, aligned) holding one (token, kv

@@ -119,11 +119,8 @@ __global__ __launch_bounds__(kThreads) void kv_write_fp8_kernel(KvWriteArgs a) {
         // binary32 round-to-nearest division (no fast-math): scale = amax / 448, inv = 448 / amax
         const float scale = amax / 448.0f;
         const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
-        uint32_t lo = 0, hi = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) lo |= e4m3_rne_sat(x[j] * inv) << (8 * j);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) hi |= e4m3_rne_sat(x[4 + j] * inv) << (8 * j);
+        const uint32_t lo = e4m3x4(x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv);
+        const uint32_t hi = e4m3x4(x[4] * inv, x[5] * inv, x[6] * inv, x[7] * inv);
         if (!live[i]) continue;
         const int64_t slot = slots[tok[i] - first_tok];
         if (slot < 0) continue;
@@ -133,6 +130,22 @@ __global__ __launch_bounds__(kThreads) void kv_write_fp8_kernel(KvWriteArgs a) {
             float* sp = isv[i] ? a.v_scale : a.k_scale;
             sp[slot * a.n_kv_head + cc[i] / R] = scale;
         }
+    }
+}
+
+// Elementwise E4M3 encoding of binary32 values (the encoder of every fp8
+// producer here), four values per thread with one 16-byte load and one
+// 4-byte store; a grid-stride loop covers any n.
+__global__ __launch_bounds__(256) void e4m3_encode_kernel(const float* x, uint8_t* q, int64_t n) {
+    const int64_t n4 = n / 4;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) {
+        const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(x) + i);
+        __builtin_nontemporal_store(e4m3x4(v[0], v[1], v[2], v[3]), reinterpret_cast<uint32_t*>(q) + i);
+    }
+    if (blockIdx.x == 0 && threadIdx.x < n - n4 * 4) {
+        const int64_t i = n4 * 4 + threadIdx.x;
+        q[i] = (uint8_t)(e4m3x4(x[i], 0.0f, 0.0f, 0.0f) & 0xFFu);
     }
 }
 
@@ -155,6 +168,13 @@ hipError_t launch_kv_write_fp8(const KvWriteArgs& a, hipStream_t s) {
         case 16: hipLaunchKernelGGL(kv_write_fp8_kernel<16>, dim3(num_blocks(a)), dim3(kThreads), 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_e4m3_encode(const float* x, uint8_t* q, int64_t n, hipStream_t s) {
+    const int64_t blocks = (n / 4 + 255) / 256;
+    const uint32_t grid = (uint32_t)(blocks < 1 ? 1 : (blocks > 16384 ? 16384 : blocks));
+    hipLaunchKernelGGL(e4m3_encode_kernel, dim3(grid), dim3(256), 0, s, x, q, n);
     return hipGetLastError();
 }
 

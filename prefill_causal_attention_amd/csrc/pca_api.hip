@@ -403,4 +403,13 @@ pca_status pca_kv_cache_write(const pca_bf16* k, const pca_bf16* v, int64_t ldk,
     return hip_status(e, "kv_cache_write launch");
 }
 
+pca_status pca_e4m3_encode(const float* x, uint8_t* codes, int64_t n, void* stream) {
+    if (n == 0) return ok();
+    if (n < 0) return fail(PCA_ERR_INVALID_ARG, "n must be >= 0 (n=%lld)", (long long)n);
+    if (!x || !codes) return fail(PCA_ERR_INVALID_ARG, "null x or codes");
+    if (!aligned16(x) || ((uintptr_t)codes & 3u))
+        return fail(PCA_ERR_INVALID_ARG, "x must be 16-byte aligned, codes 4-byte aligned");
+    return hip_status(pca::launch_e4m3_encode(x, codes, n, (hipStream_t)stream), "e4m3_encode launch");
+}
+
 }  // extern "C"

@@ -26,6 +26,8 @@ struct KvWriteArgs {
 
 hipError_t launch_kv_write_bf16(const KvWriteArgs& a, hipStream_t s);
 hipError_t launch_kv_write_fp8(const KvWriteArgs& a, hipStream_t s);
+// q[i] = E4M3 code of x[i] (RNE, saturating), i < n
+hipError_t launch_e4m3_encode(const float* x, uint8_t* q, int64_t n, hipStream_t s);
 
 struct GemmArgs {
     const uint16_t* x;

@@ -298,11 +298,8 @@ void qkv_gemm_kernel(GemmArgs a) {
                 if (slot >= 0) {
                     // binary32 round-to-nearest division (no fast-math): scale = amax / 448, inv = 448 / amax
                     const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
-                    uint32_t lo = 0, hi = 0;
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) lo |= e4m3_rne_sat(x[t] * inv) << (8 * t);
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) hi |= e4m3_rne_sat(x[4 + t] * inv) << (8 * t);
+                    const uint32_t lo = e4m3x4(x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv);
+                    const uint32_t hi = e4m3x4(x[4] * inv, x[5] * inv, x[6] * inv, x[7] * inv);
                     const int64_t row = (int64_t)slot * kv.n_kv_head + kvh;
                     uint8_t* pool = kv_sel == 0 ? (uint8_t*)kv.k_cache : (uint8_t*)kv.v_cache;
                     *reinterpret_cast<u32x2_t*>(pool + row * hd + dcol) = u32x2_t{lo, hi};

@@ -139,3 +139,10 @@ def test_fused_kv_write_validation():
                       a["K"], a["nh"], a["nkv"], a["hd"], a["cu"], a["ns"], a["bt"], a["mp"], a["ps"], a["dt"],
                       a["kc"], a["vc"], a["ks"], a["vs"], a["np_"], None)
     assert st == 2 and "128" in msg, (st, msg)
+
+
+def test_e4m3_encode_validation():
+    assert _status("pca_e4m3_encode", None, None, 0, None)[0] == 0          # empty: no-op, no buffers needed
+    for c in [(FAKE, FAKE, -1), (0, FAKE, 8), (FAKE, 0, 8), (MISALIGNED, FAKE, 8), (FAKE, FAKE + 2, 8)]:
+        st, msg = _status("pca_e4m3_encode", *c, None)
+        assert st == 1 and msg, c
