@@ -295,6 +295,7 @@ pca_status pca_prefill_attention_paged(const pca_bf16* q, int64_t ldq, const int
  *        [0, num_pages) and positions past max_pages_per_seq*page_size are
  *        skipped on the device (never written out of bounds).
  *   page_size: 16 (else PCA_ERR_UNSUPPORTED).  head_dim: 32, 64 or 128.
+ *   num_pages * page_size < 2^31 (else PCA_ERR_UNSUPPORTED).
  *   cache_dtype PCA_DTYPE_BF16: k_cache, v_cache are bf16 pools, a bit copy;
  *        k_scale and v_scale must be NULL.
  *   cache_dtype PCA_DTYPE_FP8_E4M3 (tuning notes §3.3): k_cache, v_cache are

@@ -57,6 +57,18 @@ __device__ inline uint32_t e4m3x4(float a, float b, float c, float d) {
     return (uint32_t)w;
 }
 
+// max over the L-lane group (L = 1, 2, 4, 8 or 16, aligned) of non-negative
+// binary32 values passed as their bit patterns, whose integer order is their
+// value order; the unsigned max takes each DPP lane permute as an operand.
+template <int L>
+__device__ inline uint32_t group_umax(uint32_t v) {
+    if constexpr (L >= 2) v = __builtin_elementwise_max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+    if constexpr (L >= 4) v = __builtin_elementwise_max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+    if constexpr (L >= 8) v = __builtin_elementwise_max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+    if constexpr (L >= 16) v = __builtin_elementwise_max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
+    return v;
+}
+
 // max over the R-lane group (R = 4, 8 or 16, aligned) holding one (token, kv
 // head) row, with DPP lane permutes inside 16-lane rows: swap neighbours, swap
 // pairs, mirror halves of 8, mirror the 16

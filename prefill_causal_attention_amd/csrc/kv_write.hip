@@ -26,11 +26,12 @@ constexpr int kThreads = 256;
 constexpr int kItems = 4;
 constexpr int kChunksPerBlock = kThreads * kItems;
 
-// Resolve the slots of tokens [first, first + ntok) into LDS.
-__device__ inline void resolve_slots(const KvWriteArgs& a, int64_t first, int ntok, int64_t* slots) {
+// Resolve the slots of tokens [first, first + ntok) into LDS.  Slot indices
+// fit in int32: the host keeps num_pages * page_size below 2^31.
+__device__ inline void resolve_slots(const KvWriteArgs& a, int64_t first, int ntok, int32_t* slots) {
     for (int i = threadIdx.x; i < ntok; i += kThreads) {
         int64_t t = first + i;
-        slots[i] = (t < a.total_tokens) ? token_slot(a, t) : -1;
+        slots[i] = (t < a.total_tokens) ? (int32_t)token_slot(a, t) : -1;
     }
     __syncthreads();
 }
@@ -42,7 +43,7 @@ __global__ __launch_bounds__(kThreads) void kv_write_bf16_kernel(KvWriteArgs a) 
     const uint32_t first_chunk = blockIdx.x * (uint32_t)kChunksPerBlock;
     const int64_t first_tok = first_chunk / C2;
     const int ntok = (int)((first_chunk + kChunksPerBlock - 1) / C2 - first_tok + 1);
-    __shared__ int64_t slots[kChunksPerBlock / 8 + 2];
+    __shared__ int32_t slots[kChunksPerBlock / 8 + 2];
 
     // the data loads go out first; the page-slot lookups (a dependent chain of
     // small loads) overlap them
@@ -67,21 +68,27 @@ __global__ __launch_bounds__(kThreads) void kv_write_bf16_kernel(KvWriteArgs a) 
 #pragma unroll
     for (int i = 0; i < kItems; ++i) {
         if (!live[i]) continue;
-        const int64_t slot = slots[tok[i] - first_tok];
+        const int32_t slot = slots[tok[i] - first_tok];
         if (slot < 0) continue;
         uint16_t* pool = isv[i] ? (uint16_t*)a.v_cache : (uint16_t*)a.k_cache;
-        __builtin_nontemporal_store(val[i], reinterpret_cast<u32x4_t*>(pool + (slot * (int64_t)C + cc[i]) * 8));
+        __builtin_nontemporal_store(val[i], reinterpret_cast<u32x4_t*>(pool + ((uint64_t)(uint32_t)slot * C + cc[i]) * 8));
     }
 }
 
+// R = head_dim / 8 lanes hold one (token, kv head) row of K or V.  The row's
+// amax is a max over those lanes; the divisions that follow are the same on
+// all of them, so lane q of every quad divides for item q only (a quad lies
+// inside one row group, R >= 4) and the quad exchanges the results by DPP:
+// two divisions per lane instead of two per item.
 template <int R>
 __global__ __launch_bounds__(kThreads) void kv_write_fp8_kernel(KvWriteArgs a) {
+    static_assert(kItems == 4 && R >= 4, "one item per quad lane");
     const uint32_t C = (uint32_t)a.n_kv_head * R;            // chunks per token per tensor
     const uint32_t C2 = 2 * C;
     const uint32_t first_chunk = blockIdx.x * (uint32_t)kChunksPerBlock;
     const int64_t first_tok = first_chunk / C2;
     const int ntok = (int)((first_chunk + kChunksPerBlock - 1) / C2 - first_tok + 1);
-    __shared__ int64_t slots[kChunksPerBlock / 8 + 2];
+    __shared__ int32_t slots[kChunksPerBlock / 8 + 2];
 
     // data loads first, page-slot lookups overlapping them
     const uint32_t total_chunks = (uint32_t)a.total_tokens * C2;
@@ -104,31 +111,53 @@ __global__ __launch_bounds__(kThreads) void kv_write_fp8_kernel(KvWriteArgs a) {
         }
     }
     resolve_slots(a, first_tok, ntok, slots);
+
+    float x[kItems][8];
+    float amax[kItems];
 #pragma unroll
     for (int i = 0; i < kItems; ++i) {
-        float x[8];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            x[2 * j] = bf16_lo(w[i][j]);
-            x[2 * j + 1] = bf16_hi(w[i][j]);
+            x[i][2 * j] = bf16_lo(w[i][j]);
+            x[i][2 * j + 1] = bf16_hi(w[i][j]);
         }
-        float amax = 0.0f;
+        float m = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[j]));
-        amax = group_max<R>(amax);
-        // binary32 round-to-nearest division (no fast-math): scale = amax / 448, inv = 448 / amax
-        const float scale = amax / 448.0f;
-        const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
-        const uint32_t lo = e4m3x4(x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv);
-        const uint32_t hi = e4m3x4(x[4] * inv, x[5] * inv, x[6] * inv, x[7] * inv);
+        for (int j = 0; j < 8; ++j) m = __builtin_fmaxf(m, __builtin_fabsf(x[i][j]));
+        amax[i] = __builtin_bit_cast(float, group_umax<R>(__builtin_bit_cast(uint32_t, m)));
+    }
+    // binary32 round-to-nearest divisions (no fast-math): scale = amax / 448, inv = 448 / amax
+    const uint32_t q = threadIdx.x & 3u;
+    const float am = q == 0 ? amax[0] : q == 1 ? amax[1] : q == 2 ? amax[2] : amax[3];
+    const float inv_q = am > 0.0f ? 448.0f / am : 0.0f;
+    float inv[kItems];
+    inv[0] = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, inv_q), 0x00, 0xF, 0xF, false));
+    inv[1] = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, inv_q), 0x55, 0xF, 0xF, false));
+    inv[2] = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, inv_q), 0xAA, 0xF, 0xF, false));
+    inv[3] = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, inv_q), 0xFF, 0xF, 0xF, false));
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+        const uint32_t lo = e4m3x4(x[i][0] * inv[i], x[i][1] * inv[i], x[i][2] * inv[i], x[i][3] * inv[i]);
+        const uint32_t hi = e4m3x4(x[i][4] * inv[i], x[i][5] * inv[i], x[i][6] * inv[i], x[i][7] * inv[i]);
         if (!live[i]) continue;
-        const int64_t slot = slots[tok[i] - first_tok];
+        const int32_t slot = slots[tok[i] - first_tok];
         if (slot < 0) continue;
         uint8_t* pool = isv[i] ? (uint8_t*)a.v_cache : (uint8_t*)a.k_cache;
-        __builtin_nontemporal_store(u32x2_t{lo, hi}, reinterpret_cast<u32x2_t*>(pool + slot * (int64_t)C * 8 + cc[i] * 8));
-        if (cc[i] % R == 0) {
-            float* sp = isv[i] ? a.v_scale : a.k_scale;
-            sp[slot * a.n_kv_head + cc[i] / R] = scale;
+        __builtin_nontemporal_store(u32x2_t{lo, hi},
+                                    reinterpret_cast<u32x2_t*>(pool + ((uint64_t)(uint32_t)slot * C + cc[i]) * 8));
+    }
+    // the scale of item q's row, stored by the lane at offset q inside the row
+    if ((threadIdx.x & (R - 1)) < 4) {
+        const bool lv = q == 0 ? live[0] : q == 1 ? live[1] : q == 2 ? live[2] : live[3];
+        const uint32_t tq = q == 0 ? tok[0] : q == 1 ? tok[1] : q == 2 ? tok[2] : tok[3];
+        const bool vq = q == 0 ? isv[0] : q == 1 ? isv[1] : q == 2 ? isv[2] : isv[3];
+        const uint32_t cq = q == 0 ? cc[0] : q == 1 ? cc[1] : q == 2 ? cc[2] : cc[3];
+        if (lv) {
+            const int32_t slot = slots[tq - first_tok];
+            if (slot >= 0) {
+                float* sp = vq ? a.v_scale : a.k_scale;
+                sp[(uint64_t)(uint32_t)slot * a.n_kv_head + cq / R] = am / 448.0f;
+            }
         }
     }
 }

@@ -85,6 +85,8 @@ pca_status check_kv_cache(const int32_t* cu_seqlens, int num_seqs, int64_t total
     if (st != PCA_OK) return st;
     if (max_pages_per_seq < 1 || num_pages < 1)
         return fail(PCA_ERR_INVALID_ARG, "max_pages_per_seq and num_pages must be >= 1");
+    if (num_pages > INT32_MAX / page_size)
+        return fail(PCA_ERR_UNSUPPORTED, "num_pages * page_size must be below 2^31 (num_pages=%lld)", (long long)num_pages);
     if (cache_dtype == PCA_DTYPE_BF16) {
         if (k_scale || v_scale) return fail(PCA_ERR_INVALID_ARG, "k_scale/v_scale must be NULL for a bf16 cache");
     } else if (cache_dtype == PCA_DTYPE_FP8_E4M3) {

@@ -104,7 +104,7 @@ def test_kv_write_validation():
     base = dict(k=FAKE, v=FAKE, ldk=1024, ldv=1024, cu=None, ns=1, T=64, bt=FAKE, mp=4, nkv=8, hd=128, ps=16,
                 dt=0, kc=FAKE, vc=FAKE, ks=None, vs=None, np_=4)
     bad = {("ps", 32): 2, ("hd", 48): 2, ("dt", 5): 2, ("dt", 1): 1, ("ks", FAKE): 1, ("bt", 0): 1,
-           ("kc", MISALIGNED): 1, ("ldk", 1000): 1, ("mp", 0): 1, ("np_", 0): 1, ("ns", 3): 1, ("nkv", 0): 1}
+           ("kc", MISALIGNED): 1, ("ldk", 1000): 1, ("mp", 0): 1, ("np_", 0): 1, ("ns", 3): 1, ("nkv", 0): 1, ("np_", 1 << 27): 2}
     for (key, val), exp in bad.items():
         a = dict(base, **{key: val})
         st, msg = _status("pca_kv_cache_write", a["k"], a["v"], a["ldk"], a["ldv"], a["cu"], a["ns"], a["T"], a["bt"],
