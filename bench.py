@@ -302,6 +302,40 @@ def main():
                                   "frac_fp8_peak": g8 / PEAK_FP8_TFLOPS}
         del xq, sx, wq, sw
 
+        # the fp8 KV write at the long-context shape (s=32768, 40 q / 8 kv heads,
+        # hd 128, permuted pages), K and V read as column slices of the fused
+        # projection output as on the path; cold: 4 independent (output, pools)
+        # sets written back to back, per-launch time = span / 4
+        w5 = workloads.BY_NAME["long_gqa_s32768_fp8kv"]
+        T5, nk5 = w5.total_tokens, w5.n_kv_head * w5.head_dim
+        lay5 = pca.kv_layout(w5.n_head, w5.n_kv_head, w5.head_dim, 16, "fp8_e4m3")
+        k5o, v5o = lay5["k_off"], lay5["v_off"]
+        bt5h = workloads.block_table(w5)
+        bt5 = torch.from_numpy(np.where(bt5h < 0, 0, bt5h).astype(np.int32)).to(dev)
+        shape5 = (w5.num_pages, 16, w5.n_kv_head, w5.head_dim)
+        gen.manual_seed(9004)
+        sets5 = []
+        for _ in range(4):
+            y5 = torch.zeros((T5, lay5["qkv_ld"]), dtype=torch.bfloat16, device=dev)
+            y5[:, k5o:v5o + nk5] = torch.randn((T5, v5o + nk5 - k5o), generator=gen, device=dev).to(torch.bfloat16)
+            sets5.append((y5[:, k5o:k5o + nk5], y5[:, v5o:v5o + nk5], torch.empty(shape5, dtype=torch.uint8, device=dev),
+                          torch.empty(shape5, dtype=torch.uint8, device=dev),
+                          torch.empty(shape5[:3], dtype=torch.float32, device=dev),
+                          torch.empty(shape5[:3], dtype=torch.float32, device=dev)))
+
+        def kv5_round():
+            for k5, v5, kc5, vc5, ks5, vs5 in sets5:
+                pca.kv_cache_write(k5, v5, bt5, kc5, vc5, w5.n_kv_head, w5.head_dim, cache_dtype="fp8_e4m3",
+                                   k_scale=ks5, v_scale=vs5)
+        t5 = timed(kv5_round, max(2, args.extra_reps // 4)) / len(sets5)
+        b5 = 2 * T5 * nk5 * 2 + 2 * T5 * nk5 + 2 * T5 * w5.n_kv_head * 4 + 4 * T5 // 16
+        extras["kv_cache_write_fp8"] = {
+            "case": f"s={T5}, {w5.n_kv_head} kv heads x {w5.head_dim} (slices of the ({T5}, {lay5['qkv_ld']}) "
+                    "projection output), fp8 E4M3 pages, cold",
+            "ms": t5, "algorithmic_bytes": b5, "gbs": b5 / (t5 * 1e-3) / 1e9,
+            "frac_hbm": b5 / (t5 * 1e-3) / 1e9 / PEAK_HBM_GBS}
+        del sets5
+
     att_flops = w.attention_flops()
     gemm_flops = w.gemm_flops()
     eb = 1 if fp8 else 2
