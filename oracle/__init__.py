@@ -26,3 +26,4 @@ values the pages print, closed forms, invariants or brute force; nothing is
 "parity unpinned".
 """
 from . import bf16, fp8, attention, projection, kvcache  # noqa: F401
+from . import fp8_attention  # noqa: F401

@@ -89,3 +89,41 @@ def quantize_rows(x_f32) -> tuple:
     y = (x * inv[..., None]).astype(np.float32)
     codes = encode(y)
     return codes, scale.astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# Power-of-two row scales (fp8 operands of the attention scores).
+#
+# [P2] §2.3 lists FP8 inputs with wider accumulation and the softmax kept in
+# higher precision; it fixes no scale format.  The reading taken for the
+# attention scores: each row (one token, one head) gets a scale that is a
+# power of two, 2**e, with e the smallest integer in [-127, 127] for which
+# amax * 2**-e <= 448, so the row's largest magnitude lands in (224, 448] and
+# nothing saturates; the codes are E4M3 (round to nearest even) of
+# y * 2**-e, which is exact scaling.  The scale is stored as the byte e + 127
+# (the OCP microscaling E8M0 form: value 2**(byte - 127)).  amax == 0 (or a
+# row so small that e would fall below -127) takes e = -127.
+
+def pow2_exponent(amax) -> np.ndarray:
+    """Smallest integer e in [-127, 127] with amax * 2**-e <= 448 (array)."""
+    a = np.asarray(amax, dtype=np.float64)
+    m, E = np.frexp(a)                        # a = m * 2**E, m in [0.5, 1) (0 -> m = 0)
+    # 448 = 0.875 * 2**9: m * 2**(E - e) <= 0.875 * 2**9
+    e = np.where(m <= 0.875, E - 9, E - 8)
+    e = np.where(a == 0, -127, e)
+    return np.maximum(e, -127).astype(np.int64)
+
+
+def quantize_rows_pow2(y_f32) -> tuple:
+    """Rows of a float32 array -> (codes uint8, scale bytes uint8 = e + 127)."""
+    y = np.asarray(y_f32, dtype=np.float32)
+    amax = np.max(np.abs(y), axis=-1).astype(np.float64)
+    e = pow2_exponent(amax)
+    scaled = y.astype(np.float64) * np.ldexp(1.0, -e)[..., None]     # exact: a power of two
+    return encode(scaled), (e + 127).astype(np.uint8)
+
+
+def decode_rows_pow2(codes, scale_bytes) -> np.ndarray:
+    """fp64 values code * 2**(byte - 127), rows along the last axis."""
+    e = np.asarray(scale_bytes, dtype=np.int64) - 127
+    return decode(codes) * np.ldexp(1.0, e)[..., None]
