@@ -302,6 +302,19 @@ def main():
                                   "frac_fp8_peak": g8 / PEAK_FP8_TFLOPS}
         del xq, sx, wq, sw
 
+        # fp8 operands for the scores: K quantised per (token, kv head) with
+        # power-of-two scales (once per step, timed apart), Q inside the kernel
+        k8 = torch.empty((T, nk), dtype=torch.uint8, device=dev)
+        kex = torch.empty((T, (w.n_kv_head + 3) // 4 * 4), dtype=torch.uint8, device=dev)
+        kex_v = kex[:, :w.n_kv_head]
+        t_kq = timed(lambda: pca.quantize_heads_fp8(k, k8, kex_v, w.n_kv_head, w.head_dim), args.extra_reps)
+        t_a8 = timed(lambda: pca.prefill_attention_fp8qk(q, k8, kex_v, v, o, w.n_head, w.n_kv_head, w.head_dim,
+                                                         cu_seqlens=cu, max_seqlen=w.max_seqlen), args.extra_reps)
+        extras["prefill_attention_fp8qk"] = {
+            "case": "same workload, fp8 E4M3 Q.K^T operands with power-of-two row scales, bf16 P.V",
+            "ms": t_a8, "tflops": w.attention_flops() / (t_a8 * 1e-3) / 1e12, "quantize_k_ms": t_kq}
+        del k8, kex, kex_v
+
         # the fp8 KV write at the long-context shape (s=32768, 40 q / 8 kv heads,
         # hd 128, permuted pages), K and V read as column slices of the fused
         # projection output as on the path; cold: 4 independent (output, pools)

@@ -314,6 +314,48 @@ pca_status pca_kv_cache_write(const pca_bf16* k, const pca_bf16* v, int64_t ldk,
                               int64_t num_pages, void* stream);
 
 /*
+ * pca_quantize_heads_fp8 -- per-(token, head) E4M3 rows with power-of-two
+ *   scales, the operand form of pca_prefill_attention_fp8qk (tuning notes
+ *   §2.3: FP8 inputs, wider accumulation).  For token t and head h, with
+ *   y = RN32(x[t, h, :] * prescale) and amax = max|y|: e is the smallest
+ *   integer in [-127, 127] with amax * 2^-e <= 448 (amax == 0: e = -127),
+ *   codes[t, h, :] = E4M3_RNE(y * 2^-e) (an exact scaling, so one rounding)
+ *   and exps[t, h] = e + 127 (the OCP microscaling E8M0 byte: 2^(byte-127)).
+ *   x: device bf16, T rows, head h of row t at x + t*ldx + h*head_dim
+ *      (ldx >= n_heads*head_dim, a multiple of 8; 16-byte aligned) -- e.g.
+ *      the K columns of the fused projection output.
+ *   codes: device uint8, same layout with row stride ldc (multiple of 8,
+ *      8-byte aligned).  exps: device uint8, T rows of n_heads, stride lde.
+ *   head_dim: 32, 64 or 128.  prescale: finite, > 0 (1 for K).  T == 0 is a
+ *   no-op.
+ */
+pca_status pca_quantize_heads_fp8(const pca_bf16* x, int64_t ldx, int64_t T, int n_heads, int head_dim, float prescale,
+                                  uint8_t* codes, int64_t ldc, uint8_t* exps, int64_t lde, void* stream);
+
+/*
+ * pca_prefill_attention_fp8qk -- pca_prefill_attention with fp8 operands for
+ *   the scores (tuning notes §2.3: FP8 inputs with wider accumulation, the
+ *   softmax kept in higher precision).  K arrives as pca_quantize_heads_fp8
+ *   output (prescale 1): codes k_codes (T rows, stride ldk bytes, a multiple
+ *   of 16; head j of token t at k_codes + t*ldk + j*128) and scale bytes
+ *   k_exps (T rows of n_kv_head, stride lde: a multiple of 4, k_exps 4-byte
+ *   aligned).  Q (bf16, as for
+ *   pca_prefill_attention) is quantised inside with the same rule after the
+ *   factor c = RN32(scale * RN32(log2 e)): per (token, head), codes of
+ *   RN32(q * c) * 2^-e.  The scores are exact products of the dequantised
+ *   operands accumulated in fp32 (in log2 units), the softmax is taken in
+ *   base 2 with fp32 exp2 and sums, P is rounded to bf16 for P.V with V in
+ *   bf16, and o gets the normalised rows as bf16 (same layout as
+ *   pca_prefill_attention).  head_dim must be 128 (else PCA_ERR_UNSUPPORTED);
+ *   other arguments and errors as pca_prefill_attention.
+ */
+pca_status pca_prefill_attention_fp8qk(const pca_bf16* q, int64_t ldq, const uint8_t* k_codes, int64_t ldk,
+                                       const uint8_t* k_exps, int64_t lde, const pca_bf16* v, int64_t ldv,
+                                       const int32_t* cu_seqlens, int num_seqs, int max_seqlen,
+                                       int64_t total_tokens, int n_head, int n_kv_head, int head_dim,
+                                       float scale, int causal, pca_bf16* o, int64_t ldo, void* stream);
+
+/*
  * pca_e4m3_encode -- codes[i] = E4M3_RNE_saturate(x[i]) for i < n: the OCP
  *   E4M3 encoder behind every fp8 result of this library (the KV cache of the
  *   tuning notes §3.3 and the fp8 operands of §2.3), as a plain elementwise op

@@ -10,17 +10,20 @@ Calls (same names as the C ABI in include/pca.h, minus the ``pca_`` prefix):
   qkv_proj_fp8       the QKV GEMM on fp8 operands (fp8 matrix cores, fp32 accumulate)
   e4m3_encode        elementwise float32 -> E4M3 codes (the encoder of every fp8 result)
   prefill_attention  causal GQA flash attention with online softmax
+  quantize_heads_fp8 per-(token, head) E4M3 rows with power-of-two scales
+  prefill_attention_fp8qk  the same attention with fp8 Q.K^T operands
   prefill_attention_paged  the same for a chunk over its cached (paged) prefix
   kv_cache_write     scatter of K/V into 16-token pages (bf16 or fp8 E4M3)
 All compute runs in hand-written HIP kernels; PyTorch only provides device
 memory and the current stream.
 """
-from ._lib import (EXPORTED, PcaError, e4m3_encode, kv_cache_write, kv_layout, load, prefill_attention,  # noqa: F401
-                   out_proj_residual, prefill_attention_paged, qkv_proj, qkv_proj_fp8, qkv_proj_kv_write,
-                   quantize_rows_fp8, rms_norm_qkv_proj, version)
+from ._lib import (EXPORTED, PcaError, e4m3_encode, kv_cache_write, kv_layout, load,  # noqa: F401
+                   out_proj_residual, prefill_attention, prefill_attention_fp8qk, prefill_attention_paged,
+                   qkv_proj, qkv_proj_fp8, qkv_proj_kv_write, quantize_heads_fp8, quantize_rows_fp8,
+                   rms_norm_qkv_proj, version)
 
 __all__ = ["kv_layout", "qkv_proj", "qkv_proj_kv_write", "rms_norm_qkv_proj", "out_proj_residual", "quantize_rows_fp8",
-           "qkv_proj_fp8", "e4m3_encode", "prefill_attention",
+           "qkv_proj_fp8", "e4m3_encode", "quantize_heads_fp8", "prefill_attention", "prefill_attention_fp8qk",
            "prefill_attention_paged",
            "kv_cache_write", "load", "version",
            "PcaError", "EXPORTED"]

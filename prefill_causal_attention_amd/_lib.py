@@ -19,6 +19,7 @@ DTYPES = {"bf16": 0, "fp8_e4m3": 1}
 
 EXPORTED = ("pca_kv_layout", "pca_qkv_proj", "pca_qkv_proj_kv_write", "pca_rms_norm_qkv_proj", "pca_out_proj_residual",
             "pca_quantize_rows_fp8", "pca_qkv_proj_fp8", "pca_e4m3_encode",
+            "pca_quantize_heads_fp8", "pca_prefill_attention_fp8qk",
             "pca_prefill_attention",
             "pca_prefill_attention_window", "pca_prefill_attention_paged", "pca_kv_cache_write",
             "pca_last_error", "pca_version")
@@ -62,6 +63,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                           vp, i32, i32, i32, vp, vp, vp, vp, i64, vp]
     lib.pca_quantize_rows_fp8.argtypes = [vp, i64, i64, i64, vp, i64, vp, vp]
     lib.pca_e4m3_encode.argtypes = [vp, vp, i64, vp]
+    lib.pca_quantize_heads_fp8.argtypes = [vp, i64, i64, i32, i32, f32, vp, i64, vp, i64, vp]
+    lib.pca_prefill_attention_fp8qk.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, vp, i32, i32, i64, i32, i32, i32,
+                                                f32, i32, vp, i64, vp]
     lib.pca_qkv_proj_fp8.argtypes = [vp, i64, vp, vp, i64, vp, vp, i64, i64, i64, i64, vp]
     lib.pca_rms_norm_qkv_proj.argtypes = [vp, i64, vp, i64, f32, vp, vp, i64, i64, i64, i64, vp]
     lib.pca_out_proj_residual.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, i64, i64, i64, vp]
@@ -72,7 +76,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     for fn in ("pca_kv_layout", "pca_qkv_proj", "pca_prefill_attention", "pca_kv_cache_write",
                "pca_qkv_proj_kv_write", "pca_prefill_attention_paged", "pca_prefill_attention_window",
                "pca_out_proj_residual", "pca_rms_norm_qkv_proj", "pca_quantize_rows_fp8", "pca_qkv_proj_fp8",
-               "pca_e4m3_encode"):
+               "pca_e4m3_encode", "pca_quantize_heads_fp8", "pca_prefill_attention_fp8qk"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.pca_last_error.restype = ctypes.c_char_p
     lib.pca_last_error.argtypes = []
@@ -249,6 +253,44 @@ def prefill_attention(q, k, v, o, n_head: int, n_kv_head: int, head_dim: int,
         return o
     _check("pca_prefill_attention", load().pca_prefill_attention(
         pq, pk, pv, ldq, ldk, ldv, _ptr(cu_seqlens), num_seqs, int(max_seqlen), T,
+        n_head, n_kv_head, head_dim, float(scale), 1, po, ldo, _stream(stream)))
+    return o
+
+
+def quantize_heads_fp8(x, codes, exps, n_heads: int, head_dim: int, prescale: float = 1.0, stream=None):
+    """Per-(token, head) E4M3 rows of x * prescale with power-of-two scales.
+    x: bf16 (T, >= n_heads*head_dim) view; codes: uint8 (T, >= n_heads*head_dim)
+    view; exps: uint8 (T, >= n_heads) view (scale bytes e + 127)."""
+    px, ldx = _rows(x, "x")
+    pc, ldc = _rows(codes, "codes")
+    pe, lde = _rows(exps, "exps")
+    T = x.shape[0]
+    if codes.shape[0] != T or exps.shape[0] != T:
+        raise ValueError("x, codes and exps must have the same number of rows")
+    _check("pca_quantize_heads_fp8", load().pca_quantize_heads_fp8(px, ldx, T, n_heads, head_dim, float(prescale),
+                                                                   pc, ldc, pe, lde, _stream(stream)))
+    return codes, exps
+
+
+def prefill_attention_fp8qk(q, k_codes, k_exps, v, o, n_head: int, n_kv_head: int, head_dim: int,
+                            cu_seqlens=None, max_seqlen: Optional[int] = None, scale: Optional[float] = None,
+                            total_tokens: Optional[int] = None, stream=None):
+    """Causal GQA attention with fp8 score operands: q bf16 (quantised inside
+    after the scale * log2(e) factor), K as codes + scale bytes from
+    quantize_heads_fp8, v bf16; o bf16 (T, n_head*head_dim)."""
+    pq, ldq = _rows(q, "q")
+    pk, ldk = _rows(k_codes, "k_codes")
+    pe, lde = _rows(k_exps, "k_exps")
+    pv, ldv = _rows(v, "v")
+    po, ldo = _rows(o, "o")
+    T = q.shape[0] if total_tokens is None else int(total_tokens)
+    num_seqs = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
+    if max_seqlen is None:
+        max_seqlen = T
+    if scale is None:
+        scale = head_dim ** -0.5
+    _check("pca_prefill_attention_fp8qk", load().pca_prefill_attention_fp8qk(
+        pq, ldq, pk, ldk, pe, lde, pv, ldv, _ptr(cu_seqlens), num_seqs, int(max_seqlen), T,
         n_head, n_kv_head, head_dim, float(scale), 1, po, ldo, _stream(stream)))
     return o
 

@@ -165,15 +165,57 @@ template <int N>
 __device__ __forceinline__ void lds_wait(u32x2_t& a, u32x2_t& b) {
     asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N));
 }
+template <int N>
+__device__ __forceinline__ void lds_wait(u32x4_t& a, u32x4_t& b) {
+    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N));
+}
+template <int N>
+__device__ __forceinline__ void lds_wait(u32x4_t& a, u32x4_t& b, u32x2_t& c) {
+    asm volatile("s_waitcnt lgkmcnt(%3)" : "+v"(a), "+v"(b), "+v"(c) : "n"(N));
+}
+template <int OFF>
+__device__ __forceinline__ uint32_t lds_read_b32(uint32_t addr) {
+    static_assert(OFF >= 0 && OFF < 65536, "DS offset field is 16 bits");
+    uint32_t r;
+    asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+    return r;
+}
 
 // LDS reads still in flight after those of MFMA i of a matrix phase, when
-// the reads run LA MFMAs ahead: MFMAs [0, NPV) take two reads, the rest one.
-template <int NPV, int NM, int LA>
+// the reads run LA MFMAs ahead: MFMAs [0, NPV) take two reads, the rest RS.
+template <int NPV, int NM, int LA, int RS>
 constexpr int reads_after(int i) {
     int n = 0;
-    for (int m = i + 1; m <= i + LA - 1 && m < NM; ++m) n += (m < NPV) ? 2 : 1;
+    for (int m = i + 1; m <= i + LA - 1 && m < NM; ++m) n += (m < NPV) ? 2 : RS;
     return n;
 }
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+// S^T block from fp8 operands: 32 keys x 32 queries over 64 head dims, A = K
+// rows (32 bytes per lane), B = Q^T columns, each lane's 32-element block
+// scaled by 2^(byte - 127) of its own row (key) and column (query).
+// The A fragment is used again after the instruction (an empty asm), so it
+// stays live across it and the result registers cannot be allocated on top
+// of it: the compiler otherwise lets this instruction's destination overlap
+// its A source, which no other MFMA of the kernel is allowed to do.
+__device__ inline f32x16_t mfma_f8s(u32x4_t a0, u32x4_t a1, u32x4_t b0, u32x4_t b1, f32x16_t c, int sa, int sb) {
+    const i32x8_t a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+    const i32x8_t b = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+    const f32x16_t d = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+    asm volatile("" ::"v"(a), "v"(b));
+    return d;
+}
+
+// fp8 K tiles sit in the first 8 KiB of a K buffer; the 64 keys' scale words
+// (the 4-byte word holding each key's scale byte) follow at this offset
+constexpr int kExpOff = 8192;
+
+// fp8 K tiles: 128-byte rows; physical 16-byte chunk of logical chunk c in
+// row r is c ^ swz8(r), so any 8 consecutive rows read at one logical chunk
+// hit 8 different chunk slots, and so do the rows of equal parity among 16
+// consecutive ones (the two 128-byte halves of a 256-byte bank line).
+__device__ inline int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 struct Params {
     const uint16_t* q;
@@ -200,6 +242,12 @@ struct Params {
     int window;         // > 0: sliding window, row r sees keys r - window < c <= r
     const float* k_scale;   // fp8 pages: per-(slot, kv head) scales [page][16][n_kv]
     const float* v_scale;
+    // fp8 score operands: K codes (token rows, stride ldk8 bytes) and their
+    // power-of-two scale bytes (token rows of n_kv, stride ldke)
+    const uint8_t* k8;
+    int64_t ldk8;
+    const uint8_t* kex;
+    int64_t ldke;
 };
 
 constexpr uint32_t kOob = 0x80000000u;  // a buffer offset past every pool: loads return 0
@@ -225,6 +273,33 @@ __device__ __forceinline__ void dma_tile(const uint16_t* src, int64_t ld, int64_
         const int blk = wave + i * kWaves;
         if (C::NBLK % kWaves == 0 || blk < C::NBLK)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(dst + blk * 1024), 16, off[i], 0, 0, 0);
+    }
+}
+
+// DMA of one fp8 K tile (keys [kbase, kbase + 64), 128 code bytes each) into
+// the first 8 KiB of a K buffer: wave w fills the 1 KiB block of rows
+// 8w .. 8w + 7; keys at or past the sequence end read 0.  `off` is the lane's
+// byte offset (row, swizzled chunk, kv head) inside the tile.
+// Wave 0 also moves the tile's scale words: lane l the 4-byte word holding
+// key kbase + l's scale byte (ex_off = l * lde + the word of kv head g; the
+// row stride lde is a multiple of 4, so the byte sits at bit 8 (g % 4) of
+// every word), to kExpOff + 4 l.
+__device__ __forceinline__ void dma_tile_k8(const uint8_t* src, int64_t ld, const uint8_t* ex, int64_t lde, int64_t s0,
+                                            int Lb, int wave, int kbase, lds_char_t* dst, uint32_t off,
+                                            uint32_t ex_off) {
+    const uint64_t base = (uint64_t)(src + (s0 + kbase) * ld);
+    const uint64_t ubase = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(base >> 32)) << 32) |
+                           (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base);
+    const uint32_t bytes = (uint32_t)__builtin_amdgcn_readfirstlane((int)((int64_t)(Lb - kbase) * ld));
+    const __amdgpu_buffer_rsrc_t r = make_rsrc((const void*)ubase, bytes);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(dst + wave * 1024), 16, off, 0, 0, 0);
+    if (wave == 0) {
+        const uint64_t eb = (uint64_t)(ex + (s0 + kbase) * lde);
+        const uint64_t ueb = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(eb >> 32)) << 32) |
+                             (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)eb);
+        const uint32_t ebytes = (uint32_t)__builtin_amdgcn_readfirstlane((int)((int64_t)(Lb - kbase) * lde));
+        const __amdgpu_buffer_rsrc_t re = make_rsrc((const void*)ueb, ebytes);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(re, (lds_void_t*)(dst + kExpOff), 4, ex_off, 0, 0, 0);
     }
 }
 
@@ -304,11 +379,16 @@ __device__ __forceinline__ void convert_fp8(int wave, int lane, const lds_char_t
 }
 
 // PAGED: 0 = K/V token-major rows of the chunk itself, 1 = bf16 page pools,
-// 2 = fp8 (E4M3 + per-row scale) page pools.
+// 2 = fp8 (E4M3 + per-row scale) page pools, 3 = token-major rows with fp8
+// score operands (K as E4M3 codes with power-of-two row scales, Q quantised
+// here; V bf16).
 template <int HD, int PAGED, bool WIN>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(Params p) {
     using C = Cfg<HD>;
+    constexpr bool kPaged = PAGED == 1 || PAGED == 2;
+    constexpr bool kF8S = PAGED == 3;
+    static_assert(!kF8S || HD == 128, "fp8 score operands: two 64-wide head_dim slices");
     extern __shared__ __align__(16) uint16_t smem[];
     lds_char_t* lds = (lds_char_t*)smem;
     const int tid = threadIdx.x;
@@ -348,7 +428,7 @@ void attn_fwd_kernel(Params p) {
     // keys: the chunk itself, or the cached prefix followed by the chunk; the
     // chunk's row r sits at key position pos0 + r
     int Lk = Lb;
-    if constexpr (PAGED != 0) Lk = __builtin_amdgcn_readfirstlane(min(max(p.ctx[b], Lb), p.mp * 16));
+    if constexpr (kPaged) Lk = __builtin_amdgcn_readfirstlane(min(max(p.ctx[b], Lb), p.mp * 16));
     const int pos0 = Lk - Lb;
     const int G = p.group;
     const int nqb = (Lb + BQ - 1) / BQ;
@@ -378,13 +458,26 @@ void attn_fwd_kernel(Params p) {
     // paged: first part of the sequence's block-table row (staged in LDS below)
     [[maybe_unused]] const int npg = (Lk + 15) >> 4;
     [[maybe_unused]] int32_t btv[kBtPerThread];
-    if constexpr (PAGED != 0) {
+    if constexpr (kPaged) {
 #pragma unroll
         for (int u = 0; u < kBtPerThread; ++u)
             btv[u] = u * kThreads + tid < npg ? p.bt[(int64_t)b * p.mp + u * kThreads + tid] : 0;
     }
 
     bf16x8_t qreg[C::DCH];   // the Q tile (loaded in the prologue)
+    // fp8 score operands: the Q tile as codes (slice s of 64 head dims, two
+    // 16-byte halves) and the row's scale byte; DMA offsets of the fp8 K tile
+    // and of its scale words; LDS address of key r32's scale word
+    [[maybe_unused]] u32x4_t q8[2][2];
+    [[maybe_unused]] int qexp = 127;
+    [[maybe_unused]] uint32_t dma_k8 = 0, dma_ex = 0, exaddr = 0;
+    [[maybe_unused]] const int ex_shift = (g & 3) * 8;
+    if constexpr (kF8S) {
+        const int row = wave * 8 + lane / 8;
+        dma_k8 = (uint32_t)(row * p.ldk8 + g * HD + (((lane & 7) ^ swz8(row)) * 16));
+        dma_ex = (uint32_t)(lane * p.ldke + (g & ~3));
+        exaddr = lds_addr(lds) + r32 * 4;              // + buffer + kExpOff as the immediate
+    }
 
     // ---- DMA lane offsets: lane l writes bytes [16 l, 16 l + 16) of a 1 KiB block,
     // i.e. row l / NC, physical chunk l % NC, so it fetches the logical chunk the
@@ -403,7 +496,7 @@ void attn_fwd_kernel(Params p) {
     const __attribute__((address_space(3))) int32_t* lbt =
         (const __attribute__((address_space(3))) int32_t*)(lds + kBtOff);
     [[maybe_unused]] __amdgpu_buffer_rsrc_t rk, rv;
-    if constexpr (PAGED != 0) {
+    if constexpr (kPaged) {
         rk = make_rsrc(p.k, p.pool_bytes);
         rv = make_rsrc(p.v, p.pool_bytes);
         // the row was loaded into registers before the Q tile (both latencies overlap)
@@ -422,7 +515,9 @@ void attn_fwd_kernel(Params p) {
         return buf == C::KBUF0 ? C::F8K0 : buf == C::KBUF1 ? C::F8K1 : buf == C::VBUF0 ? C::F8V0 : C::F8V1;
     };
     auto issue_k = [&](int tile, int buf) __attribute__((always_inline)) {
-        if constexpr (PAGED == 2) {
+        if constexpr (kF8S) {
+            dma_tile_k8(p.k8, p.ldk8, p.kex, p.ldke, s0, Lb, wave, tile * BK, lds + buf, dma_k8, dma_ex);
+        } else if constexpr (PAGED == 2) {
             pend_ks = dma_tile_fp8<HD>(rk, p.k_scale, wave, lane, tile * BK, Lk, p.n_kv, g, lds + f8_of(buf), lbt);
             pend_k = buf;
         } else if constexpr (PAGED == 1) {
@@ -432,7 +527,9 @@ void attn_fwd_kernel(Params p) {
         }
     };
     auto issue_v = [&](int tile, int buf) __attribute__((always_inline)) {
-        if constexpr (PAGED == 2) {
+        if constexpr (kF8S) {
+            dma_tile<HD>(p.v, p.ldv, s0, Lb, wave, tile * BK, lds + buf, dma_v);
+        } else if constexpr (PAGED == 2) {
             pend_vs = dma_tile_fp8<HD>(rv, p.v_scale, wave, lane, tile * BK, Lk, p.n_kv, g, lds + f8_of(buf), lbt);
             pend_v = buf;
         } else if constexpr (PAGED == 1) {
@@ -457,6 +554,16 @@ void attn_fwd_kernel(Params p) {
 #pragma unroll
     for (int dc = 0; dc < C::DCH; ++dc)
         kaddr[dc] = lds_addr(lds) + r32 * C::ROWB + (((dc * 2 + half) ^ swz<HD>(r32)) * 16);
+    // fp8 K operand: row kb*32 + r32, bytes [64 s + 32 half, +32) = logical
+    // chunks 4 s + 2 half + c2
+    [[maybe_unused]] uint32_t k8addr[2][2];
+    if constexpr (kF8S) {
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2)
+                k8addr[sl][c2] = lds_addr(lds) + r32 * HD + (((4 * sl + 2 * half + c2) ^ swz8(r32)) * 16);
+    }
     // V operand (A of O^T) through the transpose read: 16-lane group (u, dh), lane i = 4 kk + qq
     // reads key row 4u + 8jb + kk (+ kb*32 + h*16), d = db*32 + 16dh + 4qq .. +3.
     uint32_t vaddr[C::DB][2];
@@ -498,15 +605,29 @@ void attn_fwd_kernel(Params p) {
     // order, so every read has LA MFMAs (~LA * 32 cycles) to land.  P_j is
     // dead before the score accumulators come alive.  On the wave's last tile
     // the scores computed here are never used.
+    // (fp8 score operands: NS = 4 MFMAs (sl, kb) of 64 head dims, two K reads
+    // each; their scale bytes are the key's and the query's.)
     constexpr int LA = 4;
     constexpr int NPV = 4 * C::DB;         // (db, kb, h): V^T block x 16-key group
-    constexpr int NS = 2 * C::DCH;         // (dc, kb): head_dim step x 32-key block
+    constexpr int NS = kF8S ? 4 : 2 * C::DCH;   // (dc, kb): head_dim step x 32-key block
+    constexpr int RS = kF8S ? 2 : 1;       // LDS reads per score MFMA
     constexpr int NM = NPV + NS;
+    // scale byte of key kb * 32 + r32 from its word
+    auto kexp = [&](const u32x2_t& w, int kb) __attribute__((always_inline)) {
+        return (int)__builtin_amdgcn_ubfe(w[kb], (uint32_t)ex_shift, 8u);
+    };
     auto matrix_phase = [&](int j, auto KNc, auto VCc) __attribute__((always_inline)) {
         if (j + 1 < wave_first || j >= wave_ntiles) return;
         constexpr int KB = decltype(KNc)::value, VB = decltype(VCc)::value;
         u32x2_t vlo[NPV], vhi[NPV];
-        u32x4_t kf[NS];
+        u32x4_t kf[NS * RS];
+        // fp8: the two scale words of the next tile's keys go out first (older
+        // than every operand read, so retired before the first score MFMA's)
+        [[maybe_unused]] u32x2_t kw;
+        if constexpr (kF8S) {
+            kw[0] = lds_read_b32<KB + kExpOff>(exaddr);
+            kw[1] = lds_read_b32<KB + kExpOff + 128>(exaddr);
+        }
         auto issue = [&](auto Ic) __attribute__((always_inline)) {
             constexpr int i = decltype(Ic)::value;
             if constexpr (i < NPV) {
@@ -514,6 +635,10 @@ void attn_fwd_kernel(Params p) {
                 constexpr int off = VB + f * 16 * C::ROWB;      // key group f = (kb, h)
                 vlo[i] = lds_read_tr16<off>(vaddr[db][0]);      // key rows 0-3 of the group
                 vhi[i] = lds_read_tr16<off>(vaddr[db][1]);      // key rows 8-11
+            } else if constexpr (kF8S) {
+                constexpr int m = i - NPV, sl = m / 2, kb = m % 2;
+                kf[2 * m] = lds_read_b128<KB + kb * 32 * HD>(k8addr[sl][0]);
+                kf[2 * m + 1] = lds_read_b128<KB + kb * 32 * HD>(k8addr[sl][1]);
             } else {
                 constexpr int m = i - NPV, dc = m / 2, kb = m % 2;
                 kf[m] = lds_read_b128<KB + kb * 32 * C::ROWB>(kaddr[dc]);
@@ -523,12 +648,18 @@ void attn_fwd_kernel(Params p) {
         static_for<LA>([&](auto Ic) { issue(Ic); });
         static_for<NM>([&](auto Ic) {
             constexpr int i = decltype(Ic)::value;
-            constexpr int n = reads_after<NPV, NM, LA>(i);
+            constexpr int n = reads_after<NPV, NM, LA, RS>(i);
             if constexpr (i < NPV) {
                 constexpr int db = i / 4, kb = (i % 4) / 2, h = i % 2;
                 lds_wait<n>(vlo[i], vhi[i]);
                 const u32x4_t w = {vlo[i][0], vlo[i][1], vhi[i][0], vhi[i][1]};
                 oacc[db] = mfma32x32x16(as_bf16x8(w), pb[kb][h], oacc[db]);
+            } else if constexpr (kF8S) {
+                constexpr int m = i - NPV, sl = m / 2, kb = m % 2;
+                if constexpr (m == 0) lds_wait<n>(kf[0], kf[1], kw);
+                else lds_wait<n>(kf[2 * m], kf[2 * m + 1]);
+                s[kb] = mfma_f8s(kf[2 * m], kf[2 * m + 1], q8[sl][0], q8[sl][1], sl == 0 ? sinit : s[kb],
+                                 kexp(kw, kb), qexp);
             } else {
                 constexpr int m = i - NPV, dc = m / 2, kb = m % 2;
                 lds_wait<n>(kf[m]);
@@ -542,19 +673,38 @@ void attn_fwd_kernel(Params p) {
     };
 
     // S^T = K Q^T for the tile in K buffer KB (prologue only)
-    // (all NS operand reads issued first, each MFMA waiting only for its own)
+    // (all operand reads issued first, each MFMA waiting only for its own)
     auto scores = [&](auto KBc) __attribute__((always_inline)) {
         constexpr int KB = decltype(KBc)::value;
-        u32x4_t kp[NS];
-        static_for<NS>([&](auto Mc) {
-            constexpr int m = decltype(Mc)::value, dc = m / 2, kb = m % 2;
-            kp[m] = lds_read_b128<KB + kb * 32 * C::ROWB>(kaddr[dc]);
-        });
-        static_for<NS>([&](auto Mc) {
-            constexpr int m = decltype(Mc)::value, dc = m / 2, kb = m % 2;
-            lds_wait<NS - 1 - m>(kp[m]);
-            s[kb] = mfma32x32x16(as_bf16x8(kp[m]), qreg[dc], dc == 0 ? sinit : s[kb]);
-        });
+        if constexpr (kF8S) {
+            u32x4_t kp[2 * NS];
+            u32x2_t kw;
+            kw[0] = lds_read_b32<KB + kExpOff>(exaddr);
+            kw[1] = lds_read_b32<KB + kExpOff + 128>(exaddr);
+            static_for<NS>([&](auto Mc) {
+                constexpr int m = decltype(Mc)::value, sl = m / 2, kb = m % 2;
+                kp[2 * m] = lds_read_b128<KB + kb * 32 * HD>(k8addr[sl][0]);
+                kp[2 * m + 1] = lds_read_b128<KB + kb * 32 * HD>(k8addr[sl][1]);
+            });
+            static_for<NS>([&](auto Mc) {
+                constexpr int m = decltype(Mc)::value, sl = m / 2, kb = m % 2;
+                if constexpr (m == 0) lds_wait<2 * (NS - 1 - m)>(kp[0], kp[1], kw);
+                else lds_wait<2 * (NS - 1 - m)>(kp[2 * m], kp[2 * m + 1]);
+                s[kb] = mfma_f8s(kp[2 * m], kp[2 * m + 1], q8[sl][0], q8[sl][1], sl == 0 ? sinit : s[kb],
+                                 kexp(kw, kb), qexp);
+            });
+        } else {
+            u32x4_t kp[NS];
+            static_for<NS>([&](auto Mc) {
+                constexpr int m = decltype(Mc)::value, dc = m / 2, kb = m % 2;
+                kp[m] = lds_read_b128<KB + kb * 32 * C::ROWB>(kaddr[dc]);
+            });
+            static_for<NS>([&](auto Mc) {
+                constexpr int m = decltype(Mc)::value, dc = m / 2, kb = m % 2;
+                lds_wait<NS - 1 - m>(kp[m]);
+                s[kb] = mfma32x32x16(as_bf16x8(kp[m]), qreg[dc], dc == 0 ? sinit : s[kb]);
+            });
+        }
     };
 
     // Softmax phase of tile t (scores in s): P_t into pb, m and l updated.
@@ -681,7 +831,43 @@ void attn_fwd_kernel(Params p) {
 
     // ---- Q tile in registers (its loads overlap the first tiles' DMA): B
     // operand of S^T = K Q^T (column = query r32)
-    {
+    if constexpr (kF8S) {
+        // lane (r32, half) holds head dims 64 s + 32 half .. +31 of its query:
+        // y = q * c in binary32, the row's power-of-two scale from its amax
+        // (the two halves exchange their maxima), codes of y * 2^-e
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + s0 * p.ldq, (uint32_t)((int64_t)Lb * p.ldq * 2));
+        float y[2][32];
+        float m = 0.0f;
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+            for (int c4 = 0; c4 < 4; ++c4) {
+                const uint32_t off =
+                    (uint32_t)(((int64_t)(q0 + r32) * p.ldq + head * HD + sl * 64 + half * 32 + c4 * 8) * 2);
+                const u32x4_t raw = buf_load16(rq, off);
+#pragma unroll
+                for (int t2 = 0; t2 < 4; ++t2) {
+                    y[sl][c4 * 8 + 2 * t2] = bf16_lo(raw[t2]) * p.c;
+                    y[sl][c4 * 8 + 2 * t2 + 1] = bf16_hi(raw[t2]) * p.c;
+                    m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(y[sl][c4 * 8 + 2 * t2]),
+                                                           __builtin_fabsf(y[sl][c4 * 8 + 2 * t2 + 1])));
+                }
+            }
+        float mlo, mhi;
+        both_halves(m, mlo, mhi);
+        const int e = pow2_exponent(__builtin_bit_cast(uint32_t, __builtin_fmaxf(mlo, mhi)));
+        qexp = e + 127;
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const float* yy = &y[sl][c2 * 16 + w * 4];
+                    q8[sl][c2][w] = e4m3x4(__builtin_ldexpf(yy[0], -e), __builtin_ldexpf(yy[1], -e),
+                                           __builtin_ldexpf(yy[2], -e), __builtin_ldexpf(yy[3], -e));
+                }
+    } else {
         const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + s0 * p.ldq, (uint32_t)((int64_t)Lb * p.ldq * 2));
 #pragma unroll
         for (int dc = 0; dc < C::DCH; ++dc) {
@@ -758,8 +944,12 @@ hipError_t launch_cfg(const AttnArgs& a, hipStream_t s) {
     p.k_scale = a.k_scale;
     p.v_scale = a.v_scale;
     p.pool_bytes = (uint32_t)a.pool_bytes;
+    p.k8 = a.k8;
+    p.ldk8 = a.ldk8;
+    p.kex = a.kex;
+    p.ldke = a.ldke;
     size_t lds = PAGED == 2 ? C::LDS_FP8 : C::LDS_BYTES;
-    if (PAGED != 0) lds += (size_t)(((a.max_ctx + 15) / 16 + 3) / 4) * 16;   // the block-table row, int32
+    if (PAGED == 1 || PAGED == 2) lds += (size_t)(((a.max_ctx + 15) / 16 + 3) / 4) * 16;   // the block-table row, int32
     if (lds > (size_t)kMaxLds) return hipErrorInvalidValue;
     const int64_t grid = (int64_t)p.ntg * p.units;
     hipLaunchKernelGGL((attn_fwd_kernel<HD, PAGED, WIN>), dim3((uint32_t)grid), dim3(kThreads), lds, s, p);
@@ -779,6 +969,7 @@ hipError_t launch_hd(const AttnArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
+    if (a.k8 != nullptr) return a.head_dim == 128 ? launch_cfg<128, 3, false>(a, s) : hipErrorInvalidValue;
     if (a.block_table != nullptr) return a.k_scale != nullptr ? launch_hd<2, false>(a, s) : launch_hd<1, false>(a, s);
     return a.window > 0 ? launch_hd<0, true>(a, s) : launch_hd<0, false>(a, s);
 }

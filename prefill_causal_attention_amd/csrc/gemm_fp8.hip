@@ -244,7 +244,58 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t* x, i
     if (lane == 0) scales[m] = amax / 448.0f;
 }
 
+// Per-(token, head) E4M3 rows with power-of-two scales (the fp8 operands of
+// the attention scores): R = head_dim / 8 lanes hold one row, 16 bytes each;
+// y = x * prescale in binary32, the row's amax by DPP (unsigned max of the
+// bit patterns), e = pow2_exponent(amax), codes of y * 2^-e (exact scaling)
+// and the scale byte e + 127 from the row's first lane.  Rows are R-aligned
+// groups of consecutive ids and the grid stride is a multiple of 256, so a
+// row's lanes run every loop trip together.
+template <int R>
+__global__ __launch_bounds__(256) void quantize_heads_kernel(const uint16_t* x, int64_t ldx, int64_t T, int H,
+                                                             float prescale, uint8_t* q, int64_t ldq, uint8_t* ex,
+                                                             int64_t lde) {
+    const int64_t total = T * H * R;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x; id < total; id += stride) {
+        const int64_t row = id / R;
+        const int ch = (int)(id - row * R);
+        const int64_t t = row / H;
+        const int h = (int)(row - t * H);
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(x + t * ldx + (int64_t)h * R * 8 + ch * 8);
+        float y[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            y[2 * j] = bf16_lo(v[j]) * prescale;
+            y[2 * j + 1] = bf16_hi(v[j]) * prescale;
+        }
+        float m = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) m = __builtin_fmaxf(m, __builtin_fabsf(y[j]));
+        const int e = pow2_exponent(group_umax<R>(__builtin_bit_cast(uint32_t, m)));
+#pragma unroll
+        for (int j = 0; j < 8; ++j) y[j] = __builtin_ldexpf(y[j], -e);
+        const uint32_t lo = e4m3x4(y[0], y[1], y[2], y[3]);
+        const uint32_t hi = e4m3x4(y[4], y[5], y[6], y[7]);
+        *reinterpret_cast<u32x2_t*>(q + t * ldq + (int64_t)h * R * 8 + ch * 8) = u32x2_t{lo, hi};
+        if (ch == 0) ex[t * lde + h] = (uint8_t)(e + 127);
+    }
+}
+
 }  // namespace
+
+hipError_t launch_quantize_heads(const uint16_t* x, int64_t ldx, int64_t T, int H, int hd, float prescale, uint8_t* q,
+                                 int64_t ldq, uint8_t* ex, int64_t lde, hipStream_t s) {
+    const int64_t blocks = (T * H * (hd / 8) + 255) / 256;
+    const dim3 grid((uint32_t)(blocks > 16384 ? 16384 : (blocks < 1 ? 1 : blocks)));
+    switch (hd) {
+        case 32: hipLaunchKernelGGL(quantize_heads_kernel<4>, grid, dim3(256), 0, s, x, ldx, T, H, prescale, q, ldq, ex, lde); break;
+        case 64: hipLaunchKernelGGL(quantize_heads_kernel<8>, grid, dim3(256), 0, s, x, ldx, T, H, prescale, q, ldq, ex, lde); break;
+        case 128: hipLaunchKernelGGL(quantize_heads_kernel<16>, grid, dim3(256), 0, s, x, ldx, T, H, prescale, q, ldq, ex, lde); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_gemm_fp8(const Fp8GemmArgs& a, hipStream_t s) {
     static const hipError_t attr = hipFuncSetAttribute((const void*)gemm_fp8_kernel,

@@ -1,5 +1,6 @@
 // Device helpers shared by the kernels that write the paged KV cache: the
-// page-slot lookup of a token and the E4M3 encoder.
+// page-slot lookup of a token and the row maxima over lane groups (the E4M3
+// encoder itself sits with the other device helpers).
 //
 // Placement: token position p of sequence b goes to page
 // block_table[b][p / page_size], slot p % page_size (prefill data-flow article
@@ -41,20 +42,6 @@ __device__ inline int64_t token_slot(const KvWriteArgs& a, int64_t t) {
     int32_t page = a.block_table[(int64_t)b * a.max_pages_per_seq + pidx];
     if (page < 0 || (int64_t)page >= a.num_pages) return -1;
     return (int64_t)page * a.page_size + (pos % a.page_size);
-}
-
-// OCP E4M3 codes of four binary32 values packed into a word (byte j holds the
-// code of the j-th argument): round to nearest even, finite overflow
-// saturating to +-448, the sign copied (so -0 gives 0x80).  gfx950's
-// conversion instruction rounds to nearest even but turns magnitudes above 464
-// into NaN, so each value is first clamped to [-448, 448]; values in
-// (448, 464] round to 448 either way, which makes the pair saturating over
-// every finite input.  NaN inputs are outside the contract.
-__device__ inline uint32_t e4m3x4(float a, float b, float c, float d) {
-    const auto cl = [](float x) { return __builtin_amdgcn_fmed3f(x, -448.0f, 448.0f); };
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(cl(a), cl(b), 0, false);
-    w = __builtin_amdgcn_cvt_pk_fp8_f32(cl(c), cl(d), w, true);
-    return (uint32_t)w;
 }
 
 // max over the L-lane group (L = 1, 2, 4, 8 or 16, aligned) of non-negative

@@ -310,6 +310,46 @@ pca_status pca_prefill_attention_window(const pca_bf16* q, const pca_bf16* k, co
     return hip_status(pca::launch_attention(a, (hipStream_t)stream), "prefill_attention launch");
 }
 
+pca_status pca_prefill_attention_fp8qk(const pca_bf16* q, int64_t ldq, const uint8_t* k_codes, int64_t ldk,
+                                       const uint8_t* k_exps, int64_t lde, const pca_bf16* v, int64_t ldv,
+                                       const int32_t* cu_seqlens, int num_seqs, int max_seqlen,
+                                       int64_t total_tokens, int n_head, int n_kv_head, int head_dim,
+                                       float scale, int causal, pca_bf16* o, int64_t ldo, void* stream) {
+    if (total_tokens == 0 && num_seqs >= 1 && causal == 1) return ok();   // empty batch: nothing to read or write
+    if (!q || !k_codes || !k_exps || !v || !o) return fail(PCA_ERR_INVALID_ARG, "null q, k_codes, k_exps, v or o");
+    if (!aligned16(q) || !aligned16(k_codes) || !aligned16(v) || !aligned16(o) || ((uintptr_t)k_exps & 3u))
+        return fail(PCA_ERR_INVALID_ARG, "q, k_codes, v and o must be 16-byte aligned, k_exps 4-byte aligned");
+    if (causal != 1) return fail(PCA_ERR_INVALID_ARG, "only causal attention (causal = 1) is provided");
+    if (n_head <= 0 || n_kv_head <= 0 || n_head % n_kv_head != 0)
+        return fail(PCA_ERR_INVALID_ARG, "need n_head, n_kv_head > 0 and n_head %% n_kv_head == 0 (%d, %d)",
+                    n_head, n_kv_head);
+    if (head_dim != 128) return fail(PCA_ERR_UNSUPPORTED, "fp8 score operands need head_dim 128 (got %d)", head_dim);
+    pca_status st = check_batch(cu_seqlens, num_seqs, total_tokens);
+    if (st != PCA_OK) return st;
+    if (!(scale > 0.0f) || scale != scale || scale > 1e30f) return fail(PCA_ERR_INVALID_ARG, "scale must be finite and > 0");
+    if (ldq < (int64_t)n_head * head_dim || ldk < (int64_t)n_kv_head * head_dim || lde < n_kv_head ||
+        ldv < (int64_t)n_kv_head * head_dim || ldo < (int64_t)n_head * head_dim ||
+        ldq % 8 || ldk % 16 || lde % 4 || ldv % 8 || ldo % 8)
+        return fail(PCA_ERR_INVALID_ARG, "row strides must cover the heads; ldq, ldv, ldo multiples of 8, ldk of 16, lde of 4 "
+                    "(ldq=%lld ldk=%lld lde=%lld ldv=%lld ldo=%lld)", (long long)ldq, (long long)ldk, (long long)lde,
+                    (long long)ldv, (long long)ldo);
+    if (total_tokens == 0) return ok();
+    if (max_seqlen < 1 || (cu_seqlens == nullptr && max_seqlen < total_tokens))
+        return fail(PCA_ERR_INVALID_ARG, "max_seqlen must be >= 1 and cover the sequence (got %d)", max_seqlen);
+    const int64_t longest = cu_seqlens ? (max_seqlen < total_tokens ? max_seqlen : total_tokens) : total_tokens;
+    if (longest * ldq * 2 >= kMaxBufferBytes || longest * ldk >= kMaxBufferBytes || longest * lde >= kMaxBufferBytes ||
+        longest * ldv * 2 >= kMaxBufferBytes)
+        return fail(PCA_ERR_UNSUPPORTED, "per-sequence q/k/v views beyond 2 GiB are not supported");
+    pca::AttnArgs a;
+    memset(&a, 0, sizeof(a));
+    a.q = q; a.v = v; a.ldq = ldq; a.ldv = ldv;
+    a.k8 = k_codes; a.ldk8 = ldk; a.kex = k_exps; a.ldke = lde;
+    a.cu_seqlens = cu_seqlens; a.num_seqs = num_seqs; a.max_seqlen = max_seqlen;
+    a.total_tokens = total_tokens; a.n_head = n_head; a.n_kv_head = n_kv_head; a.head_dim = head_dim;
+    a.scale = scale; a.o = o; a.ldo = ldo;
+    return hip_status(pca::launch_attention(a, (hipStream_t)stream), "prefill_attention_fp8qk launch");
+}
+
 pca_status pca_prefill_attention_paged(const pca_bf16* q, int64_t ldq, const int32_t* cu_seqlens_q, int num_seqs,
                                        int max_seqlen_q, int64_t total_q, const int32_t* ctx_lens, int max_ctx_len,
                                        const int32_t* block_table, int max_pages_per_seq, int page_size,
@@ -403,6 +443,25 @@ pca_status pca_kv_cache_write(const pca_bf16* k, const pca_bf16* v, int64_t ldk,
     hipError_t e = cache_dtype == PCA_DTYPE_BF16 ? pca::launch_kv_write_bf16(a, (hipStream_t)stream)
                                                  : pca::launch_kv_write_fp8(a, (hipStream_t)stream);
     return hip_status(e, "kv_cache_write launch");
+}
+
+pca_status pca_quantize_heads_fp8(const pca_bf16* x, int64_t ldx, int64_t T, int n_heads, int head_dim, float prescale,
+                                  uint8_t* codes, int64_t ldc, uint8_t* exps, int64_t lde, void* stream) {
+    if (T == 0) return ok();
+    if (T < 0 || n_heads < 1) return fail(PCA_ERR_INVALID_ARG, "need T >= 0 and n_heads >= 1");
+    if (!x || !codes || !exps) return fail(PCA_ERR_INVALID_ARG, "null x, codes or exps");
+    if (!supported_head_dim(head_dim))
+        return fail(PCA_ERR_UNSUPPORTED, "head_dim %d not supported (32, 64 or 128)", head_dim);
+    if (!aligned16(x) || ((uintptr_t)codes & 7u))
+        return fail(PCA_ERR_INVALID_ARG, "x must be 16-byte aligned, codes 8-byte aligned");
+    const int64_t w = (int64_t)n_heads * head_dim;
+    if (ldx < w || ldx % 8 || ldc < w || ldc % 8 || lde < n_heads)
+        return fail(PCA_ERR_INVALID_ARG, "ldx, ldc >= n_heads*head_dim (multiples of 8) and lde >= n_heads required");
+    if (!(prescale > 0.0f && prescale <= 3.40282347e38f)) return fail(PCA_ERR_INVALID_ARG, "prescale must be finite and > 0");
+    if (T * w / 8 >= (int64_t(1) << 40)) return fail(PCA_ERR_UNSUPPORTED, "input too large");
+    return hip_status(pca::launch_quantize_heads(x, ldx, T, n_heads, head_dim, prescale, codes, ldc, exps, lde,
+                                                 (hipStream_t)stream),
+                      "quantize_heads_fp8 launch");
 }
 
 pca_status pca_e4m3_encode(const float* x, uint8_t* codes, int64_t n, void* stream) {

@@ -49,6 +49,31 @@ __device__ inline f32x16_t mfma32x32x16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// OCP E4M3 codes of four binary32 values packed into a word (byte j holds the
+// code of the j-th argument): round to nearest even, finite overflow
+// saturating to +-448, the sign copied (so -0 gives 0x80).  gfx950's
+// conversion instruction rounds to nearest even but turns magnitudes above 464
+// into NaN, so each value is first clamped to [-448, 448]; values in
+// (448, 464] round to 448 either way, which makes the pair saturating over
+// every finite input.  NaN inputs are outside the contract.
+__device__ inline uint32_t e4m3x4(float a, float b, float c, float d) {
+    const auto cl = [](float x) { return __builtin_amdgcn_fmed3f(x, -448.0f, 448.0f); };
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(cl(a), cl(b), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(cl(c), cl(d), w, true);
+    return (uint32_t)w;
+}
+
+// Power-of-two scale of an fp8 operand row: the smallest e in [-127, 127]
+// with amax * 2^-e <= 448 = 1.75 * 2^8, from amax's bit pattern (a
+// non-negative finite binary32).  amax = 1.m * 2^E fits 448 * 2^(E-8) when
+// 1.m <= 1.75, else needs 2^(E-7); a zero or subnormal amax takes -127.
+__device__ inline int pow2_exponent(uint32_t amax_bits) {
+    if (amax_bits < 0x00800000u) return -127;
+    const int E = (int)(amax_bits >> 23) - 127;
+    const int e = (amax_bits & 0x7FFFFFu) <= 0x600000u ? E - 8 : E - 7;
+    return e < -127 ? -127 : e;
+}
+
 // For every lane l: lo = v of lane l % 32, hi = v of lane l % 32 + 32.
 // v_permlane32_swap exchanges the upper 32 lanes of one register with the
 // lower 32 lanes of another in the VALU, so this needs no LDS round trip

@@ -69,6 +69,11 @@ hipError_t launch_gemm_fp8(const Fp8GemmArgs& a, hipStream_t s);
 hipError_t launch_quantize_rows(const uint16_t* x, int64_t ldx, int M, int K, uint8_t* q, int64_t ldq, float* scales,
                                 hipStream_t s);
 
+// Per-(token, head) E4M3 rows of x * prescale with power-of-two scales
+// (codes (T, H*hd) stride ldq, scale bytes e + 127 (T, H) stride lde)
+hipError_t launch_quantize_heads(const uint16_t* x, int64_t ldx, int64_t T, int H, int hd, float prescale, uint8_t* q,
+                                 int64_t ldq, uint8_t* ex, int64_t lde, hipStream_t s);
+
 // inv_rms[m] = 1 / sqrt(mean_k x[m, k]^2 + eps) for the M rows of x (K columns)
 hipError_t launch_rms_stats(const uint16_t* x, int64_t ldx, int M, int K, float eps, float* inv_rms, hipStream_t s);
 
@@ -95,6 +100,13 @@ struct AttnArgs {
     int window;                   // > 0: sliding window of that many keys (row r sees r - window < c <= r)
     const float* k_scale;         // paged fp8 pools: per-(slot, kv head) scales; null for bf16 pools
     const float* v_scale;
+    // fp8 score operands (k unused): K as E4M3 codes (token rows, stride ldk8
+    // bytes) with power-of-two scale bytes (token rows of n_kv, stride ldke);
+    // Q is quantised inside the kernel
+    const uint8_t* k8;
+    int64_t ldk8;
+    const uint8_t* kex;
+    int64_t ldke;
 };
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);

@@ -146,3 +146,34 @@ def test_e4m3_encode_validation():
     for c in [(FAKE, FAKE, -1), (0, FAKE, 8), (FAKE, 0, 8), (MISALIGNED, FAKE, 8), (FAKE, FAKE + 2, 8)]:
         st, msg = _status("pca_e4m3_encode", *c, None)
         assert st == 1 and msg, c
+
+
+def test_quantize_heads_fp8_validation():
+    # x, ldx, T, H, hd, prescale, codes, ldc, exps, lde
+    base = dict(x=FAKE, ldx=1024, T=4, H=8, hd=128, ps=1.0, c=FAKE, ldc=1024, e=FAKE, lde=8)
+    assert _status("pca_quantize_heads_fp8", None, 1024, 0, 8, 128, ctypes.c_float(1.0), None, 1024, None, 8,
+                   None)[0] == 0                                         # T == 0: no-op
+    bad = {("x", 0): 1, ("x", MISALIGNED): 1, ("c", FAKE + 4): 1, ("hd", 96): 2, ("H", 0): 1, ("ldx", 1000): 1,
+           ("ldc", 1016): 1, ("lde", 7): 1, ("ps", 0.0): 1, ("ps", float("inf")): 1, ("ps", float("nan")): 1,
+           ("T", -1): 1}
+    for (key, val), exp in bad.items():
+        a = dict(base, **{key: val})
+        st, msg = _status("pca_quantize_heads_fp8", a["x"], a["ldx"], a["T"], a["H"], a["hd"], ctypes.c_float(a["ps"]),
+                          a["c"], a["ldc"], a["e"], a["lde"], None)
+        assert st == exp and msg, (key, val, st, msg)
+
+
+def test_fp8qk_attention_validation():
+    base = dict(q=FAKE, ldq=4096, k=FAKE, ldk=1024, e=FAKE, lde=8, v=FAKE, ldv=1024, cu=None, ns=1, mx=64, T=64,
+                nh=32, nkv=8, hd=128, scale=0.088, causal=1, o=FAKE, ldo=4096)
+    bad = {("hd", 64): 2, ("nkv", 7): 1, ("causal", 0): 1, ("k", 0): 1, ("e", FAKE + 2): 1, ("ldk", 1032): 1,
+           ("lde", 6): 1, ("lde", 10): 1, ("ldq", 4000): 1, ("scale", 0.0): 1, ("mx", 10): 1, ("v", MISALIGNED): 1}
+    for (key, val), exp in bad.items():
+        a = dict(base, **{key: val})
+        st, msg = _status("pca_prefill_attention_fp8qk", a["q"], a["ldq"], a["k"], a["ldk"], a["e"], a["lde"], a["v"],
+                          a["ldv"], a["cu"], a["ns"], a["mx"], a["T"], a["nh"], a["nkv"], a["hd"],
+                          ctypes.c_float(a["scale"]), a["causal"], a["o"], a["ldo"], None)
+        assert st == exp and msg, (key, val, st, msg)
+    st, _ = _status("pca_prefill_attention_fp8qk", None, 4096, None, 1024, None, 8, None, 1024, None, 1, 0, 0, 32, 8,
+                    128, ctypes.c_float(0.088), 1, None, 4096, None)
+    assert st == 0                                                       # empty batch
