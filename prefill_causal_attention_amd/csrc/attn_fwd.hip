@@ -229,7 +229,8 @@ struct Params {
     float c;            // scale * log2(e)
     uint16_t* o;
     int64_t ldo;
-    int ntg;            // task groups per (sequence, kv head) in the grid
+    int ntg;            // workgroup ranks per (sequence, kv head) in the grid
+    int pair;           // 1: a workgroup takes a heavy and a light task group of its unit
     int units;          // num_seqs * n_kv
     // paged K/V (chunk over a cached prefix): k, v are the page pools
     // [page][slot][n_kv][hd]; key c of sequence b sits in page bt[b][c / 16],
@@ -413,8 +414,28 @@ void attn_fwd_kernel(Params p) {
             rank = L / p.units;
         }
     }
-    const int b = unit / p.n_kv;
-    const int g = unit - b * p.n_kv;
+    const int g = unit % p.n_kv;
+    int b = unit / p.n_kv;
+    if (p.cu != nullptr && p.num_seqs > 1 && p.num_seqs <= 64) {
+        // slot b takes the b-th longest sequence (ties by index): batches
+        // then run as if packed longest first, which measured up to 1.2x
+        // faster than arbitrary orders of the same lengths.  Lane i ranks
+        // sequence i against all others (every wave does it alike).
+        auto seq_len = [&](int i) __attribute__((always_inline)) {
+            const int64_t a0 = min<int64_t>(max<int64_t>(p.cu[i], 0), p.total);
+            return min<int64_t>(max<int64_t>(p.cu[i + 1], a0), p.total) - a0;
+        };
+        int rank_i = 64;
+        if (lane < p.num_seqs) {
+            const int64_t li = seq_len(lane);
+            rank_i = 0;
+            for (int j = 0; j < p.num_seqs; ++j) {
+                const int64_t lj = seq_len(j);
+                rank_i += (lj > li || (lj == li && j < lane)) ? 1 : 0;
+            }
+        }
+        b = (int)__builtin_ctzll(__builtin_amdgcn_ballot_w64(rank_i == b));
+    }
     int64_t s0 = 0, s1 = p.total;
     if (p.cu != nullptr) {
         s0 = min<int64_t>(max<int64_t>(p.cu[b], 0), p.total);
@@ -434,25 +455,23 @@ void attn_fwd_kernel(Params p) {
     const int nqb = (Lb + BQ - 1) / BQ;
     const int ntasks = G * nqb;
     const int ntg_b = (ntasks + kWaves - 1) / kWaves;
-    const int tg = p.ntg - 1 - rank;
-    if (tg >= ntg_b) return;                                   // uniform per workgroup
-
-    const int task = tg * kWaves + wave;
-    const bool active = task < ntasks;
-    const int qblk = active ? task / G : 0;
-    const int head = g * G + (active ? task % G : 0);
-    const int q0 = qblk * BQ;                                  // first query row (in sequence)
-    const int last_task = min(tg * kWaves + kWaves - 1, ntasks - 1);
-    const int kv_end = pos0 + min(Lb, (last_task / G + 1) * BQ);
-    const int ntiles = (kv_end + BK - 1) / BK;                 // tiles the workgroup visits
-    const int wave_last_q = pos0 + min(q0 + BQ, Lb) - 1;       // key position of the wave's last query
-    const int wave_ntiles = active ? wave_last_q / BK + 1 : 0; // tiles this wave computes
-    // sliding window: the first tile holding a key that the wave's (the
-    // workgroup's) first row sees; tiles before it are skipped
-    int wave_first = 0, j0 = 0;
-    if constexpr (WIN) {
-        wave_first = max(0, pos0 + q0 - p.window + 1) / BK;
-        j0 = __builtin_amdgcn_readfirstlane(max(0, pos0 + (tg * kWaves / G) * BQ - p.window + 1) / BK);
+    // the workgroup's task groups (8 tasks = (query block, head) pairs each):
+    // task group ntg - 1 - rank, or, paired, task groups ntg_b - 1 - i and i of
+    // its own (sequence, kv head) with i = ntg - 1 - rank -- a heavy and a
+    // light one, so every pair does about the same work and the per-workgroup
+    // start-up is paid half as often; heaviest first either way
+    int items[2], nitems;
+    if (p.pair) {
+        const int i = p.ntg - 1 - rank;
+        const int hi = ntg_b - 1 - i;
+        if (i > hi) return;                                    // uniform per workgroup
+        items[0] = hi;
+        items[1] = i;
+        nitems = i < hi ? 2 : 1;
+    } else {
+        items[0] = p.ntg - 1 - rank;
+        if (items[0] >= ntg_b) return;                         // uniform per workgroup
+        nitems = 1;
     }
 
     // paged: first part of the sequence's block-table row (staged in LDS below)
@@ -580,342 +599,370 @@ void attn_fwd_kernel(Params p) {
             }
     }
 
-    f32x16_t oacc[C::DB];
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[db][e] = 0.0f;
-    // Per row (lane): reference R in log2 units; every score chain starts from
-    // the accumulator sinit = -R, so the MFMA hands over s * c - R directly.
-    float R = 0.0f, l_run = 0.0f;
-    f32x16_t sinit = {};
-    f32x16_t s[2];          // scores of the tile whose softmax is next
-    bf16x8_t pb[2][2];      // P of the tile whose P V product is next
-    // zero until the wave's first softmax: the matrix phase before it (which
-    // computes that tile's scores) then adds nothing to O
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) pb[kb][h] = as_bf16x8(u32x4_t{0u, 0u, 0u, 0u});
-    bool rset = false;      // the row has a reference R (set at its first tile with a visible key)
-
-    // Matrix phase of tile j: O^T += V^T P^T for tile j (V buffer VC), then
-    // S^T = K Q^T for tile j + 1 (K buffer KN), as one sequence of NM MFMAs
-    // whose LDS operands are read LA MFMAs ahead; scheduling barriers pin the
-    // order, so every read has LA MFMAs (~LA * 32 cycles) to land.  P_j is
-    // dead before the score accumulators come alive.  On the wave's last tile
-    // the scores computed here are never used.
-    // (fp8 score operands: NS = 4 MFMAs (sl, kb) of 64 head dims, two K reads
-    // each; their scale bytes are the key's and the query's.)
-    constexpr int LA = 4;
-    constexpr int NPV = 4 * C::DB;         // (db, kb, h): V^T block x 16-key group
-    constexpr int NS = kF8S ? 4 : 2 * C::DCH;   // (dc, kb): head_dim step x 32-key block
-    constexpr int RS = kF8S ? 2 : 1;       // LDS reads per score MFMA
-    constexpr int NM = NPV + NS;
-    // scale byte of key kb * 32 + r32 from its word
-    auto kexp = [&](const u32x2_t& w, int kb) __attribute__((always_inline)) {
-        return (int)__builtin_amdgcn_ubfe(w[kb], (uint32_t)ex_shift, 8u);
-    };
-    auto matrix_phase = [&](int j, auto KNc, auto VCc) __attribute__((always_inline)) {
-        if (j + 1 < wave_first || j >= wave_ntiles) return;
-        constexpr int KB = decltype(KNc)::value, VB = decltype(VCc)::value;
-        u32x2_t vlo[NPV], vhi[NPV];
-        u32x4_t kf[NS * RS];
-        // fp8: the two scale words of the next tile's keys go out first (older
-        // than every operand read, so retired before the first score MFMA's)
-        [[maybe_unused]] u32x2_t kw;
-        if constexpr (kF8S) {
-            kw[0] = lds_read_b32<KB + kExpOff>(exaddr);
-            kw[1] = lds_read_b32<KB + kExpOff + 128>(exaddr);
+    // The LDS buffers are free between items: each item ends with a barrier
+    // that follows every wave's last LDS read.
+    for (int it = 0; it < nitems; ++it) {
+        const int tg = items[it];
+        const int task = tg * kWaves + wave;
+        const bool active = task < ntasks;
+        const int qblk = active ? task / G : 0;
+        const int head = g * G + (active ? task % G : 0);
+        const int q0 = qblk * BQ;                                  // first query row (in sequence)
+        const int last_task = min(tg * kWaves + kWaves - 1, ntasks - 1);
+        const int kv_end = pos0 + min(Lb, (last_task / G + 1) * BQ);
+        const int ntiles = (kv_end + BK - 1) / BK;                 // tiles the workgroup visits
+        const int wave_last_q = pos0 + min(q0 + BQ, Lb) - 1;       // key position of the wave's last query
+        const int wave_ntiles = active ? wave_last_q / BK + 1 : 0; // tiles this wave computes
+        // sliding window: the first tile holding a key that the wave's (the
+        // workgroup's) first row sees; tiles before it are skipped
+        int wave_first = 0, j0 = 0;
+        if constexpr (WIN) {
+            wave_first = max(0, pos0 + q0 - p.window + 1) / BK;
+            j0 = __builtin_amdgcn_readfirstlane(max(0, pos0 + (tg * kWaves / G) * BQ - p.window + 1) / BK);
         }
-        auto issue = [&](auto Ic) __attribute__((always_inline)) {
-            constexpr int i = decltype(Ic)::value;
-            if constexpr (i < NPV) {
-                constexpr int db = i / 4, f = i % 4;
-                constexpr int off = VB + f * 16 * C::ROWB;      // key group f = (kb, h)
-                vlo[i] = lds_read_tr16<off>(vaddr[db][0]);      // key rows 0-3 of the group
-                vhi[i] = lds_read_tr16<off>(vaddr[db][1]);      // key rows 8-11
-            } else if constexpr (kF8S) {
-                constexpr int m = i - NPV, sl = m / 2, kb = m % 2;
-                kf[2 * m] = lds_read_b128<KB + kb * 32 * HD>(k8addr[sl][0]);
-                kf[2 * m + 1] = lds_read_b128<KB + kb * 32 * HD>(k8addr[sl][1]);
+
+        f32x16_t oacc[C::DB];
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) oacc[db][e] = 0.0f;
+        // Per row (lane): reference R in log2 units; every score chain starts from
+        // the accumulator sinit = -R, so the MFMA hands over s * c - R directly.
+        float R = 0.0f, l_run = 0.0f;
+        f32x16_t sinit = {};
+        f32x16_t s[2];          // scores of the tile whose softmax is next
+        bf16x8_t pb[2][2];      // P of the tile whose P V product is next
+        // zero until the wave's first softmax: the matrix phase before it (which
+        // computes that tile's scores) then adds nothing to O
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) pb[kb][h] = as_bf16x8(u32x4_t{0u, 0u, 0u, 0u});
+        bool rset = false;      // the row has a reference R (set at its first tile with a visible key)
+
+        // Matrix phase of tile j: O^T += V^T P^T for tile j (V buffer VC), then
+        // S^T = K Q^T for tile j + 1 (K buffer KN), as one sequence of NM MFMAs
+        // whose LDS operands are read LA MFMAs ahead; scheduling barriers pin the
+        // order, so every read has LA MFMAs (~LA * 32 cycles) to land.  P_j is
+        // dead before the score accumulators come alive.  On the wave's last tile
+        // the scores computed here are never used.
+        // (fp8 score operands: NS = 4 MFMAs (sl, kb) of 64 head dims, two K reads
+        // each; their scale bytes are the key's and the query's.)
+        constexpr int LA = 4;
+        constexpr int NPV = 4 * C::DB;         // (db, kb, h): V^T block x 16-key group
+        constexpr int NS = kF8S ? 4 : 2 * C::DCH;   // (dc, kb): head_dim step x 32-key block
+        constexpr int RS = kF8S ? 2 : 1;       // LDS reads per score MFMA
+        constexpr int NM = NPV + NS;
+        // scale byte of key kb * 32 + r32 from its word
+        auto kexp = [&](const u32x2_t& w, int kb) __attribute__((always_inline)) {
+            return (int)__builtin_amdgcn_ubfe(w[kb], (uint32_t)ex_shift, 8u);
+        };
+        auto matrix_phase = [&](int j, auto KNc, auto VCc) __attribute__((always_inline)) {
+            if (j + 1 < wave_first || j >= wave_ntiles) return;
+            constexpr int KB = decltype(KNc)::value, VB = decltype(VCc)::value;
+            u32x2_t vlo[NPV], vhi[NPV];
+            u32x4_t kf[NS * RS];
+            // fp8: the two scale words of the next tile's keys go out first (older
+            // than every operand read, so retired before the first score MFMA's)
+            [[maybe_unused]] u32x2_t kw;
+            if constexpr (kF8S) {
+                kw[0] = lds_read_b32<KB + kExpOff>(exaddr);
+                kw[1] = lds_read_b32<KB + kExpOff + 128>(exaddr);
+            }
+            auto issue = [&](auto Ic) __attribute__((always_inline)) {
+                constexpr int i = decltype(Ic)::value;
+                if constexpr (i < NPV) {
+                    constexpr int db = i / 4, f = i % 4;
+                    constexpr int off = VB + f * 16 * C::ROWB;      // key group f = (kb, h)
+                    vlo[i] = lds_read_tr16<off>(vaddr[db][0]);      // key rows 0-3 of the group
+                    vhi[i] = lds_read_tr16<off>(vaddr[db][1]);      // key rows 8-11
+                } else if constexpr (kF8S) {
+                    constexpr int m = i - NPV, sl = m / 2, kb = m % 2;
+                    kf[2 * m] = lds_read_b128<KB + kb * 32 * HD>(k8addr[sl][0]);
+                    kf[2 * m + 1] = lds_read_b128<KB + kb * 32 * HD>(k8addr[sl][1]);
+                } else {
+                    constexpr int m = i - NPV, dc = m / 2, kb = m % 2;
+                    kf[m] = lds_read_b128<KB + kb * 32 * C::ROWB>(kaddr[dc]);
+                }
+            };
+            __builtin_amdgcn_s_setprio(1);
+            static_for<LA>([&](auto Ic) { issue(Ic); });
+            static_for<NM>([&](auto Ic) {
+                constexpr int i = decltype(Ic)::value;
+                constexpr int n = reads_after<NPV, NM, LA, RS>(i);
+                if constexpr (i < NPV) {
+                    constexpr int db = i / 4, kb = (i % 4) / 2, h = i % 2;
+                    lds_wait<n>(vlo[i], vhi[i]);
+                    const u32x4_t w = {vlo[i][0], vlo[i][1], vhi[i][0], vhi[i][1]};
+                    oacc[db] = mfma32x32x16(as_bf16x8(w), pb[kb][h], oacc[db]);
+                } else if constexpr (kF8S) {
+                    constexpr int m = i - NPV, sl = m / 2, kb = m % 2;
+                    if constexpr (m == 0) lds_wait<n>(kf[0], kf[1], kw);
+                    else lds_wait<n>(kf[2 * m], kf[2 * m + 1]);
+                    s[kb] = mfma_f8s(kf[2 * m], kf[2 * m + 1], q8[sl][0], q8[sl][1], sl == 0 ? sinit : s[kb],
+                                     kexp(kw, kb), qexp);
+                } else {
+                    constexpr int m = i - NPV, dc = m / 2, kb = m % 2;
+                    lds_wait<n>(kf[m]);
+                    // the first head_dim step starts from a zero accumulator
+                    s[kb] = mfma32x32x16(as_bf16x8(kf[m]), qreg[dc], dc == 0 ? sinit : s[kb]);
+                }
+                if constexpr (i + LA < NM) issue(std::integral_constant<int, i + LA>{});
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            __builtin_amdgcn_s_setprio(0);
+        };
+
+        // S^T = K Q^T for the tile in K buffer KB (prologue only)
+        // (all operand reads issued first, each MFMA waiting only for its own)
+        auto scores = [&](auto KBc) __attribute__((always_inline)) {
+            constexpr int KB = decltype(KBc)::value;
+            if constexpr (kF8S) {
+                u32x4_t kp[2 * NS];
+                u32x2_t kw;
+                kw[0] = lds_read_b32<KB + kExpOff>(exaddr);
+                kw[1] = lds_read_b32<KB + kExpOff + 128>(exaddr);
+                static_for<NS>([&](auto Mc) {
+                    constexpr int m = decltype(Mc)::value, sl = m / 2, kb = m % 2;
+                    kp[2 * m] = lds_read_b128<KB + kb * 32 * HD>(k8addr[sl][0]);
+                    kp[2 * m + 1] = lds_read_b128<KB + kb * 32 * HD>(k8addr[sl][1]);
+                });
+                static_for<NS>([&](auto Mc) {
+                    constexpr int m = decltype(Mc)::value, sl = m / 2, kb = m % 2;
+                    if constexpr (m == 0) lds_wait<2 * (NS - 1 - m)>(kp[0], kp[1], kw);
+                    else lds_wait<2 * (NS - 1 - m)>(kp[2 * m], kp[2 * m + 1]);
+                    s[kb] = mfma_f8s(kp[2 * m], kp[2 * m + 1], q8[sl][0], q8[sl][1], sl == 0 ? sinit : s[kb],
+                                     kexp(kw, kb), qexp);
+                });
             } else {
-                constexpr int m = i - NPV, dc = m / 2, kb = m % 2;
-                kf[m] = lds_read_b128<KB + kb * 32 * C::ROWB>(kaddr[dc]);
+                u32x4_t kp[NS];
+                static_for<NS>([&](auto Mc) {
+                    constexpr int m = decltype(Mc)::value, dc = m / 2, kb = m % 2;
+                    kp[m] = lds_read_b128<KB + kb * 32 * C::ROWB>(kaddr[dc]);
+                });
+                static_for<NS>([&](auto Mc) {
+                    constexpr int m = decltype(Mc)::value, dc = m / 2, kb = m % 2;
+                    lds_wait<NS - 1 - m>(kp[m]);
+                    s[kb] = mfma32x32x16(as_bf16x8(kp[m]), qreg[dc], dc == 0 ? sinit : s[kb]);
+                });
             }
         };
-        __builtin_amdgcn_s_setprio(1);
-        static_for<LA>([&](auto Ic) { issue(Ic); });
-        static_for<NM>([&](auto Ic) {
-            constexpr int i = decltype(Ic)::value;
-            constexpr int n = reads_after<NPV, NM, LA, RS>(i);
-            if constexpr (i < NPV) {
-                constexpr int db = i / 4, kb = (i % 4) / 2, h = i % 2;
-                lds_wait<n>(vlo[i], vhi[i]);
-                const u32x4_t w = {vlo[i][0], vlo[i][1], vhi[i][0], vhi[i][1]};
-                oacc[db] = mfma32x32x16(as_bf16x8(w), pb[kb][h], oacc[db]);
-            } else if constexpr (kF8S) {
-                constexpr int m = i - NPV, sl = m / 2, kb = m % 2;
-                if constexpr (m == 0) lds_wait<n>(kf[0], kf[1], kw);
-                else lds_wait<n>(kf[2 * m], kf[2 * m + 1]);
-                s[kb] = mfma_f8s(kf[2 * m], kf[2 * m + 1], q8[sl][0], q8[sl][1], sl == 0 ? sinit : s[kb],
-                                 kexp(kw, kb), qexp);
-            } else {
-                constexpr int m = i - NPV, dc = m / 2, kb = m % 2;
-                lds_wait<n>(kf[m]);
-                // the first head_dim step starts from a zero accumulator
-                s[kb] = mfma32x32x16(as_bf16x8(kf[m]), qreg[dc], dc == 0 ? sinit : s[kb]);
+
+        // Softmax phase of tile t (scores in s): P_t into pb, m and l updated.
+        auto softmax_phase = [&](int t) __attribute__((always_inline)) {
+            if (t < wave_first || t >= wave_ntiles) return;
+            const int kbase = t * BK;
+            // causal mask per element on tiles that reach past the first query;
+            // window mask on tiles that start before the last query's window
+            const bool upper = kbase + BK - 1 > pos0 + q0;
+            const bool lower = WIN && kbase <= pos0 + q0 + BQ - 1 - p.window;
+            if (upper || lower) {
+                const int qry = pos0 + q0 + r32;
+                // visible iff 0 <= qry - key < wlim: one unsigned compare per score
+                const uint32_t wlim = WIN ? (uint32_t)p.window : 0x7FFFFFFFu;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int key = kbase + kb * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
+                        if ((uint32_t)(qry - key) >= wlim) s[kb][e] = -__builtin_inff();
+                    }
             }
-            if constexpr (i + LA < NM) issue(std::integral_constant<int, i + LA>{});
-            __builtin_amdgcn_sched_barrier(0);
-        });
-        __builtin_amdgcn_s_setprio(0);
-    };
+            // Online softmax, one query per lane (its 64 keys split with lane ^ 32).
+            // The scores already hold s * c - R, so the common case is one exp2 and
+            // one add per score (p in fp32 for the row sum, rounded to bf16 for
+            // the MFMA).  A row moves its reference R up to its tile max on the
+            // wave's first tile and when its tile sum of p exceeds kSumLimit; the
+            // fast path stays only while every lane's half-row sum is at most
+            // kSumLimit / 2, which bounds every p by kSumLimit.  The result does
+            // not depend on R (it cancels in O / l), and a row's arithmetic depends
+            // on its own scores alone.
+            float rs;
+            auto exps = [&](float d) __attribute__((always_inline)) {
+                rs = 0.0f;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        u32x4_t w;
+#pragma unroll
+                        for (int t2 = 0; t2 < 4; ++t2) {
+                            const float e0 = fast_exp2(s[kb][h * 8 + 2 * t2] - d);
+                            const float e1 = fast_exp2(s[kb][h * 8 + 2 * t2 + 1] - d);
+                            w[t2] = pack_bf16x2(e0, e1);
+                            rs += e0;
+                            rs += e1;
+                        }
+                        pb[kb][h] = as_bf16x8(w);
+                    }
+            };
+            exps(0.0f);
+            if (__builtin_amdgcn_ballot_w64(!rset || rs > 0.5f * kSumLimit) != 0) {
+                float rlo, rhi;
+                both_halves(rs, rlo, rhi);
+                const bool move = !rset || rlo + rhi > kSumLimit;
+                // rare: moving rows take their tile max as the new reference,
+                // recompute p and rescale O and l (non-moving rows: d = 0, alpha = 1,
+                // the same p as above)
+                float mx = s[0][0];
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) mx = __builtin_fmaxf(mx, s[kb][e]);
+                float lo, hi;
+                both_halves(mx, lo, hi);
+                const float mrow = __builtin_fmaxf(lo, hi);
+                // a row with no visible key in this tile (window) keeps no reference
+                const bool ok = move && mrow > -__builtin_inff();
+                const float d = ok ? mrow : 0.0f;
+                rset = rset || ok;
+                exps(d);
+                // d > 0 for a row past the limit; on the first tile O and l are 0
+                const float alpha = __builtin_fminf(fast_exp2(-d), 1.0f);
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+                R += d;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) sinit[e] = -R;
+            }
+            l_run += rs;
+        };
 
-    // S^T = K Q^T for the tile in K buffer KB (prologue only)
-    // (all operand reads issued first, each MFMA waiting only for its own)
-    auto scores = [&](auto KBc) __attribute__((always_inline)) {
-        constexpr int KB = decltype(KBc)::value;
+        // The two groups run the same sequence of phases -- softmax of tile j,
+        // then the matrix phase of tile j -- with group B one half-step behind
+        // group A, so that in every half-step one wave of each SIMD is in its
+        // matrix phase and the other in its softmax.  Half-steps end at workgroup
+        // barriers; B starts with one extra barrier and A ends with one.
+        //
+        // DMA: in half-step 2m + 1 (A's matrix phase of tile m, B's softmax of
+        // tile m) every wave issues its share of K_{m+2} (into K_m's buffer) and
+        // V_{m+1} (into V_{m-1}'s); both were last read in half-step 2m.  They are
+        // waited for at the end of half-step 2m + 2 and first read in 2m + 3.
+        // KC/KN: K buffers of tiles j and j + 1; VC/VN: V buffers of j and j + 1.
+        auto issue_next = [&](int j, auto KCc, auto VNc) __attribute__((always_inline)) {
+            if (j + 2 < ntiles) issue_k(j + 2, decltype(KCc)::value);
+            if (j + 1 < ntiles) issue_v(j + 1, decltype(VNc)::value);
+        };
+        auto tile = [&](int j, auto KCc, auto KNc, auto VCc, auto VNc) __attribute__((always_inline)) {
+            if (!lead) issue_next(j, KCc, VNc);
+            softmax_phase(j);
+            if (lead) retire();
+            wg_barrier();
+            if (lead) issue_next(j, KCc, VNc);
+            matrix_phase(j, KNc, VCc);
+            if (!lead) retire();
+            wg_barrier();
+        };
+
+        using K0 = std::integral_constant<int, C::KBUF0>;
+        using K1 = std::integral_constant<int, C::KBUF1>;
+        using V0 = std::integral_constant<int, C::VBUF0>;
+        using V1 = std::integral_constant<int, C::VBUF1>;
+
+        // prologue: K and V of the first tile j0 (0 unless a window skips the
+        // start) and K of the next in flight, then every wave whose first tile it
+        // is computes its scores; group B waits one half-step
+        issue_k(j0, C::KBUF0);
+        issue_v(j0, C::VBUF0);
+        if constexpr (PAGED == 2) retire();   // fp8: K_j0 and V_j0 converted before K_j0+1 takes the pending slot
+        if (j0 + 1 < ntiles) issue_k(j0 + 1, C::KBUF1);
+
+        // ---- Q tile in registers (its loads overlap the first tiles' DMA): B
+        // operand of S^T = K Q^T (column = query r32)
         if constexpr (kF8S) {
-            u32x4_t kp[2 * NS];
-            u32x2_t kw;
-            kw[0] = lds_read_b32<KB + kExpOff>(exaddr);
-            kw[1] = lds_read_b32<KB + kExpOff + 128>(exaddr);
-            static_for<NS>([&](auto Mc) {
-                constexpr int m = decltype(Mc)::value, sl = m / 2, kb = m % 2;
-                kp[2 * m] = lds_read_b128<KB + kb * 32 * HD>(k8addr[sl][0]);
-                kp[2 * m + 1] = lds_read_b128<KB + kb * 32 * HD>(k8addr[sl][1]);
-            });
-            static_for<NS>([&](auto Mc) {
-                constexpr int m = decltype(Mc)::value, sl = m / 2, kb = m % 2;
-                if constexpr (m == 0) lds_wait<2 * (NS - 1 - m)>(kp[0], kp[1], kw);
-                else lds_wait<2 * (NS - 1 - m)>(kp[2 * m], kp[2 * m + 1]);
-                s[kb] = mfma_f8s(kp[2 * m], kp[2 * m + 1], q8[sl][0], q8[sl][1], sl == 0 ? sinit : s[kb],
-                                 kexp(kw, kb), qexp);
-            });
-        } else {
-            u32x4_t kp[NS];
-            static_for<NS>([&](auto Mc) {
-                constexpr int m = decltype(Mc)::value, dc = m / 2, kb = m % 2;
-                kp[m] = lds_read_b128<KB + kb * 32 * C::ROWB>(kaddr[dc]);
-            });
-            static_for<NS>([&](auto Mc) {
-                constexpr int m = decltype(Mc)::value, dc = m / 2, kb = m % 2;
-                lds_wait<NS - 1 - m>(kp[m]);
-                s[kb] = mfma32x32x16(as_bf16x8(kp[m]), qreg[dc], dc == 0 ? sinit : s[kb]);
-            });
-        }
-    };
-
-    // Softmax phase of tile t (scores in s): P_t into pb, m and l updated.
-    auto softmax_phase = [&](int t) __attribute__((always_inline)) {
-        if (t < wave_first || t >= wave_ntiles) return;
-        const int kbase = t * BK;
-        // causal mask per element on tiles that reach past the first query;
-        // window mask on tiles that start before the last query's window
-        const bool upper = kbase + BK - 1 > pos0 + q0;
-        const bool lower = WIN && kbase <= pos0 + q0 + BQ - 1 - p.window;
-        if (upper || lower) {
-            const int qry = pos0 + q0 + r32;
-            // visible iff 0 <= qry - key < wlim: one unsigned compare per score
-            const uint32_t wlim = WIN ? (uint32_t)p.window : 0x7FFFFFFFu;
+            // lane (r32, half) holds head dims 64 s + 32 half .. +31 of its query:
+            // y = q * c in binary32, the row's power-of-two scale from its amax
+            // (the two halves exchange their maxima), codes of y * 2^-e
+            const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + s0 * p.ldq, (uint32_t)((int64_t)Lb * p.ldq * 2));
+            float y[2][32];
+            float m = 0.0f;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int sl = 0; sl < 2; ++sl)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int key = kbase + kb * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
-                    if ((uint32_t)(qry - key) >= wlim) s[kb][e] = -__builtin_inff();
-                }
-        }
-        // Online softmax, one query per lane (its 64 keys split with lane ^ 32).
-        // The scores already hold s * c - R, so the common case is one exp2 and
-        // one add per score (p in fp32 for the row sum, rounded to bf16 for
-        // the MFMA).  A row moves its reference R up to its tile max on the
-        // wave's first tile and when its tile sum of p exceeds kSumLimit; the
-        // fast path stays only while every lane's half-row sum is at most
-        // kSumLimit / 2, which bounds every p by kSumLimit.  The result does
-        // not depend on R (it cancels in O / l), and a row's arithmetic depends
-        // on its own scores alone.
-        float rs;
-        auto exps = [&](float d) __attribute__((always_inline)) {
-            rs = 0.0f;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    u32x4_t w;
+                for (int c4 = 0; c4 < 4; ++c4) {
+                    const uint32_t off =
+                        (uint32_t)(((int64_t)(q0 + r32) * p.ldq + head * HD + sl * 64 + half * 32 + c4 * 8) * 2);
+                    const u32x4_t raw = buf_load16(rq, off);
 #pragma unroll
                     for (int t2 = 0; t2 < 4; ++t2) {
-                        const float e0 = fast_exp2(s[kb][h * 8 + 2 * t2] - d);
-                        const float e1 = fast_exp2(s[kb][h * 8 + 2 * t2 + 1] - d);
-                        w[t2] = pack_bf16x2(e0, e1);
-                        rs += e0;
-                        rs += e1;
+                        y[sl][c4 * 8 + 2 * t2] = bf16_lo(raw[t2]) * p.c;
+                        y[sl][c4 * 8 + 2 * t2 + 1] = bf16_hi(raw[t2]) * p.c;
+                        m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(y[sl][c4 * 8 + 2 * t2]),
+                                                               __builtin_fabsf(y[sl][c4 * 8 + 2 * t2 + 1])));
                     }
-                    pb[kb][h] = as_bf16x8(w);
                 }
-        };
-        exps(0.0f);
-        if (__builtin_amdgcn_ballot_w64(!rset || rs > 0.5f * kSumLimit) != 0) {
-            float rlo, rhi;
-            both_halves(rs, rlo, rhi);
-            const bool move = !rset || rlo + rhi > kSumLimit;
-            // rare: moving rows take their tile max as the new reference,
-            // recompute p and rescale O and l (non-moving rows: d = 0, alpha = 1,
-            // the same p as above)
-            float mx = s[0][0];
+            float mlo, mhi;
+            both_halves(m, mlo, mhi);
+            const int e = pow2_exponent(__builtin_bit_cast(uint32_t, __builtin_fmaxf(mlo, mhi)));
+            qexp = e + 127;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int sl = 0; sl < 2; ++sl)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) mx = __builtin_fmaxf(mx, s[kb][e]);
-            float lo, hi;
-            both_halves(mx, lo, hi);
-            const float mrow = __builtin_fmaxf(lo, hi);
-            // a row with no visible key in this tile (window) keeps no reference
-            const bool ok = move && mrow > -__builtin_inff();
-            const float d = ok ? mrow : 0.0f;
-            rset = rset || ok;
-            exps(d);
-            // d > 0 for a row past the limit; on the first tile O and l are 0
-            const float alpha = __builtin_fminf(fast_exp2(-d), 1.0f);
-            l_run *= alpha;
+                for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
-            for (int db = 0; db < C::DB; ++db)
+                    for (int w = 0; w < 4; ++w) {
+                        const float* yy = &y[sl][c2 * 16 + w * 4];
+                        q8[sl][c2][w] = e4m3x4(__builtin_ldexpf(yy[0], -e), __builtin_ldexpf(yy[1], -e),
+                                               __builtin_ldexpf(yy[2], -e), __builtin_ldexpf(yy[3], -e));
+                    }
+        } else {
+            const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + s0 * p.ldq, (uint32_t)((int64_t)Lb * p.ldq * 2));
 #pragma unroll
-                for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
-            R += d;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) sinit[e] = -R;
-        }
-        l_run += rs;
-    };
-
-    // The two groups run the same sequence of phases -- softmax of tile j,
-    // then the matrix phase of tile j -- with group B one half-step behind
-    // group A, so that in every half-step one wave of each SIMD is in its
-    // matrix phase and the other in its softmax.  Half-steps end at workgroup
-    // barriers; B starts with one extra barrier and A ends with one.
-    //
-    // DMA: in half-step 2m + 1 (A's matrix phase of tile m, B's softmax of
-    // tile m) every wave issues its share of K_{m+2} (into K_m's buffer) and
-    // V_{m+1} (into V_{m-1}'s); both were last read in half-step 2m.  They are
-    // waited for at the end of half-step 2m + 2 and first read in 2m + 3.
-    // KC/KN: K buffers of tiles j and j + 1; VC/VN: V buffers of j and j + 1.
-    auto issue_next = [&](int j, auto KCc, auto VNc) __attribute__((always_inline)) {
-        if (j + 2 < ntiles) issue_k(j + 2, decltype(KCc)::value);
-        if (j + 1 < ntiles) issue_v(j + 1, decltype(VNc)::value);
-    };
-    auto tile = [&](int j, auto KCc, auto KNc, auto VCc, auto VNc) __attribute__((always_inline)) {
-        if (!lead) issue_next(j, KCc, VNc);
-        softmax_phase(j);
-        if (lead) retire();
-        wg_barrier();
-        if (lead) issue_next(j, KCc, VNc);
-        matrix_phase(j, KNc, VCc);
-        if (!lead) retire();
-        wg_barrier();
-    };
-
-    using K0 = std::integral_constant<int, C::KBUF0>;
-    using K1 = std::integral_constant<int, C::KBUF1>;
-    using V0 = std::integral_constant<int, C::VBUF0>;
-    using V1 = std::integral_constant<int, C::VBUF1>;
-
-    // prologue: K and V of the first tile j0 (0 unless a window skips the
-    // start) and K of the next in flight, then every wave whose first tile it
-    // is computes its scores; group B waits one half-step
-    issue_k(j0, C::KBUF0);
-    issue_v(j0, C::VBUF0);
-    if constexpr (PAGED == 2) retire();   // fp8: K_j0 and V_j0 converted before K_j0+1 takes the pending slot
-    if (j0 + 1 < ntiles) issue_k(j0 + 1, C::KBUF1);
-
-    // ---- Q tile in registers (its loads overlap the first tiles' DMA): B
-    // operand of S^T = K Q^T (column = query r32)
-    if constexpr (kF8S) {
-        // lane (r32, half) holds head dims 64 s + 32 half .. +31 of its query:
-        // y = q * c in binary32, the row's power-of-two scale from its amax
-        // (the two halves exchange their maxima), codes of y * 2^-e
-        const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + s0 * p.ldq, (uint32_t)((int64_t)Lb * p.ldq * 2));
-        float y[2][32];
-        float m = 0.0f;
-#pragma unroll
-        for (int sl = 0; sl < 2; ++sl)
-#pragma unroll
-            for (int c4 = 0; c4 < 4; ++c4) {
-                const uint32_t off =
-                    (uint32_t)(((int64_t)(q0 + r32) * p.ldq + head * HD + sl * 64 + half * 32 + c4 * 8) * 2);
+            for (int dc = 0; dc < C::DCH; ++dc) {
+                const uint32_t off = (uint32_t)(((int64_t)(q0 + r32) * p.ldq + head * HD + dc * 16 + half * 8) * 2);
+                // scale * log2(e) folded into Q once (then rounded to bf16), so the
+                // scores come out of the MFMA in log2 units
                 const u32x4_t raw = buf_load16(rq, off);
+                u32x4_t qs;
 #pragma unroll
-                for (int t2 = 0; t2 < 4; ++t2) {
-                    y[sl][c4 * 8 + 2 * t2] = bf16_lo(raw[t2]) * p.c;
-                    y[sl][c4 * 8 + 2 * t2 + 1] = bf16_hi(raw[t2]) * p.c;
-                    m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(y[sl][c4 * 8 + 2 * t2]),
-                                                           __builtin_fabsf(y[sl][c4 * 8 + 2 * t2 + 1])));
-                }
+                for (int t2 = 0; t2 < 4; ++t2) qs[t2] = pack_bf16x2(bf16_lo(raw[t2]) * p.c, bf16_hi(raw[t2]) * p.c);
+                qreg[dc] = as_bf16x8(qs);
             }
-        float mlo, mhi;
-        both_halves(m, mlo, mhi);
-        const int e = pow2_exponent(__builtin_bit_cast(uint32_t, __builtin_fmaxf(mlo, mhi)));
-        qexp = e + 127;
+        }
+
+        retire();
+        __syncthreads();
+        if (wave_first == j0 && j0 < wave_ntiles) scores(K0{});
+        if (!lead) wg_barrier();
+        // two tiles per trip so every buffer offset is a compile-time constant
+        for (int j = j0; j < ntiles; j += 2) {
+            tile(j, K0{}, K1{}, V0{}, V1{});
+            if (j + 1 >= ntiles) break;
+            tile(j + 1, K1{}, K0{}, V1{}, V0{});
+        }
+        if (lead) wg_barrier();
+
+        // ---- epilogue: O / l, bf16 RNE, 4 consecutive d per store (no early
+        // return: every wave runs every item's barriers)
+        if (active) {
+            float l_lo, l_hi;
+            both_halves(l_run, l_lo, l_hi);
+            const float l_tot = l_lo + l_hi;
+            const float inv = 1.0f / l_tot;
+            const int row = q0 + r32;
+            if (row < Lb) {
+                uint16_t* dst = p.o + (s0 + row) * p.ldo + head * HD;
 #pragma unroll
-        for (int sl = 0; sl < 2; ++sl)
+                for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-            for (int c2 = 0; c2 < 2; ++c2)
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const float* yy = &y[sl][c2 * 16 + w * 4];
-                    q8[sl][c2][w] = e4m3x4(__builtin_ldexpf(yy[0], -e), __builtin_ldexpf(yy[1], -e),
-                                           __builtin_ldexpf(yy[2], -e), __builtin_ldexpf(yy[3], -e));
-                }
-    } else {
-        const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + s0 * p.ldq, (uint32_t)((int64_t)Lb * p.ldq * 2));
-#pragma unroll
-        for (int dc = 0; dc < C::DCH; ++dc) {
-            const uint32_t off = (uint32_t)(((int64_t)(q0 + r32) * p.ldq + head * HD + dc * 16 + half * 8) * 2);
-            // scale * log2(e) folded into Q once (then rounded to bf16), so the
-            // scores come out of the MFMA in log2 units
-            const u32x4_t raw = buf_load16(rq, off);
-            u32x4_t qs;
-#pragma unroll
-            for (int t2 = 0; t2 < 4; ++t2) qs[t2] = pack_bf16x2(bf16_lo(raw[t2]) * p.c, bf16_hi(raw[t2]) * p.c);
-            qreg[dc] = as_bf16x8(qs);
+                    for (int gq = 0; gq < 4; ++gq) {
+                        const int d = db * 32 + gq * 8 + half * 4;
+                        u32x2_t w2 = {pack_bf16x2(oacc[db][gq * 4 + 0] * inv, oacc[db][gq * 4 + 1] * inv),
+                                      pack_bf16x2(oacc[db][gq * 4 + 2] * inv, oacc[db][gq * 4 + 3] * inv)};
+                        *reinterpret_cast<u32x2_t*>(dst + d) = w2;
+                    }
+            }
         }
     }
-
-    retire();
-    __syncthreads();
-    if (wave_first == j0 && j0 < wave_ntiles) scores(K0{});
-    if (!lead) wg_barrier();
-    // two tiles per trip so every buffer offset is a compile-time constant
-    for (int j = j0; j < ntiles; j += 2) {
-        tile(j, K0{}, K1{}, V0{}, V1{});
-        if (j + 1 >= ntiles) break;
-        tile(j + 1, K1{}, K0{}, V1{}, V0{});
-    }
-    if (lead) wg_barrier();
-
-    if (!active) return;
-    // ---- epilogue: O / l, bf16 RNE, 4 consecutive d per store
-    float l_lo, l_hi;
-    both_halves(l_run, l_lo, l_hi);
-    const float l_tot = l_lo + l_hi;
-    const float inv = 1.0f / l_tot;
-    const int row = q0 + r32;
-    if (row >= Lb) return;
-    uint16_t* dst = p.o + (s0 + row) * p.ldo + head * HD;
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-            const int d = db * 32 + gq * 8 + half * 4;
-            u32x2_t w2 = {pack_bf16x2(oacc[db][gq * 4 + 0] * inv, oacc[db][gq * 4 + 1] * inv),
-                          pack_bf16x2(oacc[db][gq * 4 + 2] * inv, oacc[db][gq * 4 + 3] * inv)};
-            *reinterpret_cast<u32x2_t*>(dst + d) = w2;
-        }
 }
 
 // largest dynamic LDS a workgroup may take (gfx950: 160 KiB per CU)
 constexpr int kMaxLds = 160 * 1024;
+// unpaired grids at least this large (4 workgroups per CU) use pairing
+constexpr int64_t kPairMinWorkgroups = 1024;
 
 template <int HD, int PAGED, bool WIN>
 hipError_t launch_cfg(const AttnArgs& a, hipStream_t s) {
@@ -935,8 +982,11 @@ hipError_t launch_cfg(const AttnArgs& a, hipStream_t s) {
     p.o = a.o;
     p.ldo = a.ldo;
     const int nqb = (a.max_seqlen + BQ - 1) / BQ;
-    p.ntg = (p.group * nqb + kWaves - 1) / kWaves;
+    const int ntg = (p.group * nqb + kWaves - 1) / kWaves;
     p.units = a.num_seqs * a.n_kv_head;
+    // pair task groups only when the grid stays several workgroups per CU deep
+    p.pair = (int64_t)ntg * p.units >= kPairMinWorkgroups ? 1 : 0;
+    p.ntg = p.pair ? (ntg + 1) / 2 : ntg;
     p.bt = a.block_table;
     p.mp = a.max_pages_per_seq;
     p.ctx = a.ctx_lens;
