@@ -310,9 +310,13 @@ def main():
         t_kq = timed(lambda: pca.quantize_heads_fp8(k, k8, kex_v, w.n_kv_head, w.head_dim), args.extra_reps)
         t_a8 = timed(lambda: pca.prefill_attention_fp8qk(q, k8, kex_v, v, o, w.n_head, w.n_kv_head, w.head_dim,
                                                          cu_seqlens=cu, max_seqlen=w.max_seqlen), args.extra_reps)
+        # half of the FLOPs (Q.K^T) at the fp8 rate, half (P.V) at the bf16 rate
+        mixed_peak = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
+        a8 = w.attention_flops() / (t_a8 * 1e-3) / 1e12
         extras["prefill_attention_fp8qk"] = {
             "case": "same workload, fp8 E4M3 Q.K^T operands with power-of-two row scales, bf16 P.V",
-            "ms": t_a8, "tflops": w.attention_flops() / (t_a8 * 1e-3) / 1e12, "quantize_k_ms": t_kq}
+            "ms": t_a8, "tflops": a8, "frac_bf16_peak": a8 / PEAK_BF16_TFLOPS,
+            "frac_mixed_peak": a8 / mixed_peak, "mixed_peak_tflops": mixed_peak, "quantize_k_ms": t_kq}
         del k8, kex, kex_v
 
         # the fp8 KV write at the long-context shape (s=32768, 40 q / 8 kv heads,
