@@ -92,8 +92,9 @@ def cpu_baseline(w, target_s):
         flops = float(np.sum(4.0 * (pos + 1) * w.head_dim * w.n_head))   # causal work of these rows
         return dt, flops
 
-    dt, _ = run(32)
-    n = int(min(w.total_tokens, max(64, 32 * target_s / max(dt, 1e-3))))
+    run(32)                      # first call pays numpy/BLAS start-up
+    dt, _ = run(128)
+    n = int(min(w.total_tokens, max(128, 128 * target_s / max(dt, 1e-3))))
     dt, flops = run(n)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
