@@ -36,7 +36,8 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=400,
+                    help="untimed steps first (the clocks settle over the first ~0.3 s of load)")
     ap.add_argument("--workload", default="gqa_s8192",
                     help="gqa_s8192 (default), mha_s2048, varlen16_gqa, long_gqa_s32768_fp8kv")
     ap.add_argument("--no-cpu-baseline", action="store_true")
