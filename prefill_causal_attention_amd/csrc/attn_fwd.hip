@@ -407,8 +407,16 @@ void attn_fwd_kernel(Params p) {
             // one kv head of every sequence, so the XCDs get equal shares of work
             const int per_xcd = p.units / kNumXcd;
             const int xcd = L % kNumXcd, local = L / kNumXcd;
-            unit = (local % per_xcd) * kNumXcd + xcd;
-            rank = local / per_xcd;
+            if (p.pair) {
+                // paired workgroups of one unit carry about equal work (its
+                // task-group count plus one), so heaviest first is unit-major:
+                // batch slot 0, the longest sequence, goes out first
+                unit = (local / p.ntg) * kNumXcd + xcd;
+                rank = local % p.ntg;
+            } else {
+                unit = (local % per_xcd) * kNumXcd + xcd;
+                rank = local / per_xcd;
+            }
         } else {
             unit = L % p.units;
             rank = L / p.units;
