@@ -55,9 +55,11 @@
 //    rescale of O and l and the -R accumulator refreshed, behind one branch.
 //  * The causal rule: a wave skips kv tiles that start after its last query,
 //    and masks per element only on tiles that reach past its first query.
-//    Workgroups are ordered heaviest-first, and units (sequence, kv head) go
-//    round-robin over the 8 XCDs (workgroup ids are dispatched that way), so
-//    one unit's K/V stays in one XCD's L2 and, with 8 kv heads, every XCD
+//    Workgroups are ordered heaviest-first (rank-major when every workgroup
+//    takes one task group, unit-major with the longest sequence first when
+//    workgroups take a heavy and a light one), and units (sequence, kv head)
+//    go round-robin over the 8 XCDs (workgroup ids are dispatched that way),
+//    so one unit's K/V stays in one XCD's L2 and, with 8 kv heads, every XCD
 //    gets one kv head of every sequence.
 #include "pca_device.hpp"
 #include "pca_internal.hpp"
