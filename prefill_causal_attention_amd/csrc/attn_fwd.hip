@@ -64,6 +64,7 @@
 #include "pca_device.hpp"
 #include "pca_internal.hpp"
 
+#include <atomic>
 #include <utility>
 
 namespace pca {
@@ -234,6 +235,9 @@ struct Params {
     int ntg;            // workgroup ranks per (sequence, kv head) in the grid
     int pair;           // 1: a workgroup takes a heavy and a light task group of its unit
     int units;          // num_seqs * n_kv
+    int bt_cap;         // paged: block-table entries the LDS row holds (keys past bt_cap * 16 are not read)
+    int persist;        // 1: one workgroup per CU walks its XCD's compact list (see the kernel)
+    int tab_off;        // LDS byte offset of that list's counts and the slot -> sequence table
     // paged K/V (chunk over a cached prefix): k, v are the page pools
     // [page][slot][n_kv][hd]; key c of sequence b sits in page bt[b][c / 16],
     // slot c % 16; the sequence has ctx[b] keys, the last cu[b+1] - cu[b] of
@@ -400,15 +404,93 @@ void attn_fwd_kernel(Params p) {
     const bool lead = wave < kWaves / 2;                       // group A: matrix phase first
     const int r32 = lane & 31, half = lane >> 5;
 
+    // ---- batch slot -> sequence: slot b takes the b-th longest sequence (ties
+    // by index), so batches run as if packed longest first, which measured up
+    // to 1.2x faster than arbitrary orders of the same lengths.  Lane i ranks
+    // sequence i against all others, once per workgroup (every wave alike).
+    const bool ranked = p.cu != nullptr && p.num_seqs > 1 && p.num_seqs <= 64;
+    auto seq_len = [&](int i) __attribute__((always_inline)) {
+        const int64_t a0 = min<int64_t>(max<int64_t>(p.cu[i], 0), p.total);
+        return min<int64_t>(max<int64_t>(p.cu[i + 1], a0), p.total) - a0;
+    };
+    int rank_i = 64;
+    if (ranked && lane < p.num_seqs) {
+        const int64_t li = seq_len(lane);
+        rank_i = 0;
+        for (int j = 0; j < p.num_seqs; ++j) {
+            const int64_t lj = seq_len(j);
+            rank_i += (lj > li || (lj == li && j < lane)) ? 1 : 0;
+        }
+    }
+
+    // ---- persistent walk (p.persist; one workgroup per CU, a multiple of 8 of
+    // them).  The non-empty virtual workgroups of the units an XCD owns (units
+    // x, x + 8, ... for XCD x, heaviest first) form one compact list; the
+    // workgroups of the XCD take its entries in snake order (pass m: entry
+    // m * per + lp, or m * per + per - 1 - lp on odd passes).  No workgroup is
+    // dispatched after the first, so none waits behind the in-order dispatch of
+    // another XCD's workgroup.  tab[k] counts the non-empty virtual workgroups
+    // of the XCD's units before its k-th (tab[per_xcd]: all of them); a unit's
+    // non-empty ranks are its last ones.
+    __attribute__((address_space(3))) int32_t* tab = (__attribute__((address_space(3))) int32_t*)(lds + p.tab_off);
+    __attribute__((address_space(3))) int32_t* slot_to_seq = tab + (p.units / kNumXcd + 1);
+    const int xcd = blockIdx.x % kNumXcd, lp = blockIdx.x / kNumXcd, per = gridDim.x / kNumXcd;
+    const int per_xcd = p.units / kNumXcd;
+    int ncomp = 0;
+    if (p.persist) {
+        if (ranked && lane < p.num_seqs && wave == 0) slot_to_seq[rank_i] = lane;
+        __syncthreads();
+        if (wave == 0) {
+            int carry = 0;
+            for (int k0 = 0; k0 < per_xcd; k0 += 64) {
+                const int k = k0 + lane;
+                int ne = 0;
+                if (k < per_xcd) {
+                    const int slot = (k * kNumXcd + xcd) / p.n_kv;
+                    const int seq = ranked ? slot_to_seq[slot] : slot;
+                    const int64_t len = p.cu != nullptr ? seq_len(seq) : p.total;
+                    const int nt = (int)((p.group * ((len + BQ - 1) / BQ) + kWaves - 1) / kWaves);
+                    ne = min(p.pair ? (nt + 1) / 2 : nt, p.ntg);
+                }
+                // inclusive scan over the wave
+                int inc = ne;
+#pragma unroll
+                for (int d = 1; d < 64; d <<= 1) {
+                    const int up = __shfl_up(inc, d, 64);
+                    if (lane >= d) inc += up;
+                }
+                if (k < per_xcd) tab[k] = carry + inc - ne;
+                carry += __shfl(inc, 63, 64);
+            }
+            if (lane == 0) tab[per_xcd] = carry;
+        }
+        __syncthreads();
+        ncomp = __builtin_amdgcn_readfirstlane(tab[per_xcd]);
+    }
+
+    for (int pass = 0;; ++pass) {
     // ---- workgroup -> (unit = (sequence, kv head), task group), heaviest first
     int unit, rank;
-    {
+    if (p.persist) {
+        const int c = pass * per + ((pass & 1) ? per - 1 - lp : lp);
+        if (c >= ncomp) break;                                   // uniform per workgroup
+        // the unit holding entry c: the largest k with tab[k] <= c
+        int lo = 0, hi = per_xcd - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (tab[mid] <= c) lo = mid; else hi = mid - 1;
+        }
+        lo = __builtin_amdgcn_readfirstlane(lo);
+        const int t0 = __builtin_amdgcn_readfirstlane(tab[lo]), t1 = __builtin_amdgcn_readfirstlane(tab[lo + 1]);
+        unit = lo * kNumXcd + xcd;
+        rank = p.ntg - (t1 - t0) + (c - t0);
+    } else {
+        if (pass > 0) break;
         const int L = blockIdx.x;
         if (p.units % kNumXcd == 0) {
             // XCD x runs units x, x + 8, x + 16, ...: with n_kv a multiple of 8 that is
             // one kv head of every sequence, so the XCDs get equal shares of work
-            const int per_xcd = p.units / kNumXcd;
-            const int xcd = L % kNumXcd, local = L / kNumXcd;
+            const int local = L / kNumXcd;
             if (p.pair) {
                 // paired workgroups of one unit carry about equal work (its
                 // task-group count plus one), so heaviest first is unit-major:
@@ -426,26 +508,7 @@ void attn_fwd_kernel(Params p) {
     }
     const int g = unit % p.n_kv;
     int b = unit / p.n_kv;
-    if (p.cu != nullptr && p.num_seqs > 1 && p.num_seqs <= 64) {
-        // slot b takes the b-th longest sequence (ties by index): batches
-        // then run as if packed longest first, which measured up to 1.2x
-        // faster than arbitrary orders of the same lengths.  Lane i ranks
-        // sequence i against all others (every wave does it alike).
-        auto seq_len = [&](int i) __attribute__((always_inline)) {
-            const int64_t a0 = min<int64_t>(max<int64_t>(p.cu[i], 0), p.total);
-            return min<int64_t>(max<int64_t>(p.cu[i + 1], a0), p.total) - a0;
-        };
-        int rank_i = 64;
-        if (lane < p.num_seqs) {
-            const int64_t li = seq_len(lane);
-            rank_i = 0;
-            for (int j = 0; j < p.num_seqs; ++j) {
-                const int64_t lj = seq_len(j);
-                rank_i += (lj > li || (lj == li && j < lane)) ? 1 : 0;
-            }
-        }
-        b = (int)__builtin_ctzll(__builtin_amdgcn_ballot_w64(rank_i == b));
-    }
+    if (ranked) b = (int)__builtin_ctzll(__builtin_amdgcn_ballot_w64(rank_i == b));
     int64_t s0 = 0, s1 = p.total;
     if (p.cu != nullptr) {
         s0 = min<int64_t>(max<int64_t>(p.cu[b], 0), p.total);
@@ -459,7 +522,7 @@ void attn_fwd_kernel(Params p) {
     // keys: the chunk itself, or the cached prefix followed by the chunk; the
     // chunk's row r sits at key position pos0 + r
     int Lk = Lb;
-    if constexpr (kPaged) Lk = __builtin_amdgcn_readfirstlane(min(max(p.ctx[b], Lb), p.mp * 16));
+    if constexpr (kPaged) Lk = __builtin_amdgcn_readfirstlane(min(min(max(p.ctx[b], Lb), p.mp * 16), p.bt_cap * 16));
     const int pos0 = Lk - Lb;
     const int G = p.group;
     const int nqb = (Lb + BQ - 1) / BQ;
@@ -474,13 +537,13 @@ void attn_fwd_kernel(Params p) {
     if (p.pair) {
         const int i = p.ntg - 1 - rank;
         const int hi = ntg_b - 1 - i;
-        if (i > hi) return;                                    // uniform per workgroup
+        if (i > hi) continue;                                  // uniform per workgroup
         items[0] = hi;
         items[1] = i;
         nitems = i < hi ? 2 : 1;
     } else {
         items[0] = p.ntg - 1 - rank;
-        if (items[0] >= ntg_b) return;                         // uniform per workgroup
+        if (items[0] >= ntg_b) continue;                       // uniform per workgroup
         nitems = 1;
     }
 
@@ -967,10 +1030,26 @@ void attn_fwd_kernel(Params p) {
             }
         }
     }
+    }   // pass
 }
 
 // largest dynamic LDS a workgroup may take (gfx950: 160 KiB per CU)
 constexpr int kMaxLds = 160 * 1024;
+// persistent walk: at most this many units per XCD (their counts live in LDS)
+constexpr int kMaxPersistUnits = 4096;
+
+// compute units of the current device, looked up once per device
+int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = -1;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
 // unpaired grids at least this large (4 workgroups per CU) use pairing
 constexpr int64_t kPairMinWorkgroups = 1024;
 
@@ -1009,9 +1088,24 @@ hipError_t launch_cfg(const AttnArgs& a, hipStream_t s) {
     p.kex = a.kex;
     p.ldke = a.ldke;
     size_t lds = PAGED == 2 ? C::LDS_FP8 : C::LDS_BYTES;
-    if (PAGED == 1 || PAGED == 2) lds += (size_t)(((a.max_ctx + 15) / 16 + 3) / 4) * 16;   // the block-table row, int32
+    p.bt_cap = ((a.max_ctx + 15) / 16 + 3) / 4 * 4;
+    if (PAGED == 1 || PAGED == 2) lds += (size_t)p.bt_cap * 4;   // the block-table row, int32
     if (lds > (size_t)kMaxLds) return hipErrorInvalidValue;
-    const int64_t grid = (int64_t)p.ntg * p.units;
+    int64_t grid = (int64_t)p.ntg * p.units;
+    // deeper than one workgroup per CU, with the units spread evenly over the
+    // XCDs: one workgroup per CU walks its XCD's list (the kernel's persistent walk)
+    p.persist = 0;
+    p.tab_off = 0;
+    const int ncu = device_cus();
+    const int nwg = ncu >= kNumXcd ? (ncu / kNumXcd) * kNumXcd : 0;
+    const size_t lds_persist = ((lds + 15) & ~(size_t)15) + (size_t)(p.units / kNumXcd + 1 + 64) * 4;
+    if (nwg > 0 && p.units % kNumXcd == 0 && grid > nwg && p.units / kNumXcd <= kMaxPersistUnits &&
+        lds_persist <= (size_t)kMaxLds) {
+        p.persist = 1;
+        p.tab_off = (int)((lds + 15) & ~(size_t)15);
+        lds = lds_persist;
+        grid = nwg;
+    }
     hipLaunchKernelGGL((attn_fwd_kernel<HD, PAGED, WIN>), dim3((uint32_t)grid), dim3(kThreads), lds, s, p);
     return hipGetLastError();
 }

@@ -180,6 +180,33 @@ def test_varlen_equals_each_sequence_alone_bitwise():
         assert torch.equal(packed[cu[b]:cu[b + 1]], alone), f"sequence {b}"
 
 
+@pytest.mark.parametrize("lens,H,Hk", [
+    # deep enough for the one-workgroup-per-CU walk, with empty virtual
+    # workgroups (short sequences next to long ones): ranked batch slots
+    ([1500, 40, 700, 2100, 300, 1, 900, 64], 32, 8),
+    ([1200, 2600, 33, 800], 16, 4),
+    # more than 64 sequences: batch slots in packing order
+    ([97 * (1 + (i * 37) % 11) for i in range(72)], 16, 8),
+])
+def test_deep_varlen_batch_equals_each_sequence_alone_bitwise(lens, H, Hk):
+    require_gpu()
+    w = workloads.custom(49, lens, H, Hk, 128)
+    buf, *_ = workloads.qkv_inputs(w)
+    say(f"prefill_attention deep varlen: {len(lens)} seqs T={w.total_tokens} heads={H}/{Hk}")
+    packed = _gpu_attention(w, buf)
+    cu = workloads.cu_seqlens(w)
+    for b, L in enumerate(lens):
+        wb = workloads.custom(49, [L], H, Hk, 128)
+        alone = _gpu_attention(wb, buf[cu[b]:cu[b + 1]].clone())
+        assert torch.equal(packed[cu[b]:cu[b + 1]], alone), f"sequence {b} (length {L})"
+    # and the batch against the oracle on sampled rows
+    q, k, v = _oracle_inputs(w, buf)
+    rows = sample_rows(w.total_tokens, 64, seed=49)
+    want = A.varlen_causal_attention(q, k, v, cu, rows=rows)
+    got = packed[:, :H * 128].float().cpu().numpy().astype(np.float64)[rows]
+    assert_close(got, want, "deep varlen")
+
+
 def test_deterministic_bitwise():
     require_gpu()
     w, buf = _mk(1000, 8, 2, 128, 47)
