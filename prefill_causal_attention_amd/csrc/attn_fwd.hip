@@ -64,7 +64,6 @@
 #include "pca_device.hpp"
 #include "pca_internal.hpp"
 
-#include <atomic>
 #include <utility>
 
 namespace pca {
@@ -1038,18 +1037,6 @@ constexpr int kMaxLds = 160 * 1024;
 // persistent walk: at most this many units per XCD (their counts live in LDS)
 constexpr int kMaxPersistUnits = 4096;
 
-// compute units of the current device, looked up once per device
-int device_cus() {
-    static std::atomic<int> cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    int n = cache[dev].load(std::memory_order_relaxed);
-    if (n == 0) {
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = -1;
-        cache[dev].store(n, std::memory_order_relaxed);
-    }
-    return n;
-}
 // unpaired grids at least this large (4 workgroups per CU) use pairing
 constexpr int64_t kPairMinWorkgroups = 1024;
 

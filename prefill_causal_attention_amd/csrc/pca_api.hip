@@ -8,6 +8,24 @@
 #include "pca.h"
 #include "pca_internal.hpp"
 
+#include <atomic>
+
+namespace pca {
+
+int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = -1;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n > 0 ? n : 0;
+}
+
+}  // namespace pca
+
 namespace {
 
 thread_local char g_err[512] = "";

@@ -111,4 +111,9 @@ struct AttnArgs {
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 
+// Compute units of the current device (looked up once per device; 0 if
+// unknown).  Grids deeper than one workgroup per CU launch one per CU and
+// loop over their work.
+int device_cus();
+
 }  // namespace pca
