@@ -22,6 +22,7 @@ struct KvWriteArgs {
     float* k_scale;
     float* v_scale;
     int64_t num_pages;
+    int wave_lookup = 0;          // separate KV write only: slots looked up per wave (set by its launcher)
 };
 
 hipError_t launch_kv_write_bf16(const KvWriteArgs& a, hipStream_t s);
