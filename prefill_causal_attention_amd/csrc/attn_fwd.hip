@@ -1007,26 +1007,43 @@ void attn_fwd_kernel(Params p) {
         }
         if (lead) wg_barrier();
 
-        // ---- epilogue: O / l, bf16 RNE, 4 consecutive d per store (no early
-        // return: every wave runs every item's barriers)
-        if (active) {
-            float l_lo, l_hi;
-            both_halves(l_run, l_lo, l_hi);
-            const float l_tot = l_lo + l_hi;
-            const float inv = 1.0f / l_tot;
-            const int row = q0 + r32;
-            if (row < Lb) {
-                uint16_t* dst = p.o + (s0 + row) * p.ldo + head * HD;
+        // ---- epilogue: O / l, bf16 RNE.  Each wave stages its 32 rows in its
+        // eighth of the (now free) K/V buffers, 16-byte chunks XOR-swizzled by
+        // row, and writes them back as whole head rows, 16 bytes per lane (no
+        // early return: every wave runs every item's barriers)
+        {
+            lds_char_t* stg = lds + wave * (BQ * C::ROWB);
+            // the lane's swizzle and row terms pass through an empty asm here, so
+            // the addresses built from them are formed in the epilogue instead of
+            // being hoisted out of the item loop and held in registers throughout
+            int sw = r32 & (C::NC - 1), rl = lane / C::NC;
+            asm volatile("" : "+v"(sw), "+v"(rl));
+            if (active) {
+                float l_lo, l_hi;
+                both_halves(l_run, l_lo, l_hi);
+                const float inv = 1.0f / (l_lo + l_hi);
 #pragma unroll
                 for (int db = 0; db < C::DB; ++db)
 #pragma unroll
                     for (int gq = 0; gq < 4; ++gq) {
-                        const int d = db * 32 + gq * 8 + half * 4;
-                        u32x2_t w2 = {pack_bf16x2(oacc[db][gq * 4 + 0] * inv, oacc[db][gq * 4 + 1] * inv),
-                                      pack_bf16x2(oacc[db][gq * 4 + 2] * inv, oacc[db][gq * 4 + 3] * inv)};
-                        *reinterpret_cast<u32x2_t*>(dst + d) = w2;
+                        const int pc = (db * 4 + gq) ^ sw;
+                        const u32x2_t w2 = {pack_bf16x2(oacc[db][gq * 4 + 0] * inv, oacc[db][gq * 4 + 1] * inv),
+                                            pack_bf16x2(oacc[db][gq * 4 + 2] * inv, oacc[db][gq * 4 + 3] * inv)};
+                        *reinterpret_cast<__attribute__((address_space(3))) u32x2_t*>(stg + r32 * C::ROWB + pc * 16 + half * 8) = w2;
                     }
+                constexpr int RPI = 64 / C::NC;          // rows per store instruction
+                const int c = lane % C::NC;
+#pragma unroll
+                for (int k = 0; k < BQ / RPI; ++k) {
+                    const int rr = k * RPI + rl;
+                    const u32x4_t v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(
+                        stg + rr * C::ROWB + ((c ^ (rr & (C::NC - 1))) * 16));
+                    const int row = q0 + rr;
+                    if (row < Lb) *reinterpret_cast<u32x4_t*>(p.o + (s0 + row) * p.ldo + head * HD + c * 8) = v;
+                }
             }
+            // the staging areas are the next item's first K/V buffers
+            wg_barrier();
         }
     }
     }   // pass
