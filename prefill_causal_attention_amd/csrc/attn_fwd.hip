@@ -997,7 +997,11 @@ void attn_fwd_kernel(Params p) {
 
         retire();
         __syncthreads();
+        // group A's first scores go first (raised priority), so that group B's
+        // run on the matrix cores while A does the first softmax
+        if (lead) __builtin_amdgcn_s_setprio(1);
         if (wave_first == j0 && j0 < wave_ntiles) scores(K0{});
+        if (lead) __builtin_amdgcn_s_setprio(0);
         if (!lead) wg_barrier();
         // two tiles per trip so every buffer offset is a compile-time constant
         for (int j = j0; j < ntiles; j += 2) {
