@@ -12,10 +12,12 @@
 // for all kv heads is a contiguous run both in the fused projection row and in
 // its page slot, so the copy is a set of contiguous 16-byte chunks.  A block
 // takes 1024 consecutive chunks (4 per thread, lanes on consecutive chunks so
-// each wave instruction covers 1 KiB of contiguous memory): it issues all its
-// loads first, resolves the page slot of the few tokens it touches into LDS
-// while they are in flight, then stores.  Loads and stores are non-temporal:
-// the data is touched once.
+// each wave instruction covers 1 KiB of contiguous memory).  When every block
+// is resident at once, a block issues all its loads first, resolves the page
+// slot of the few tokens it touches into LDS while they are in flight, then
+// stores; deeper grids (and a wave's 64 chunks within one token) instead look
+// the slots up per wave with scalar loads ahead of the data loads.  Loads and
+// stores are non-temporal: the data is touched once.
 #include "kv_common.hpp"
 
 namespace pca {
