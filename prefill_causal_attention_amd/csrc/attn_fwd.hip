@@ -1013,8 +1013,10 @@ void attn_fwd_kernel(Params p) {
 
         // ---- epilogue: O / l, bf16 RNE.  Each wave stages its 32 rows in its
         // eighth of the (now free) K/V buffers, 16-byte chunks XOR-swizzled by
-        // row, and writes them back as whole head rows, 16 bytes per lane (no
-        // early return: every wave runs every item's barriers)
+        // row, and writes them back as whole head rows, 16 bytes per lane,
+        // non-temporal (O is not read again here, and its lines then do not
+        // push the shared K/V tiles out of L2).  No early return: every wave
+        // runs every item's barriers.
         {
             lds_char_t* stg = lds + wave * (BQ * C::ROWB);
             // the lane's swizzle and row terms pass through an empty asm here, so
@@ -1043,7 +1045,7 @@ void attn_fwd_kernel(Params p) {
                     const u32x4_t v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(
                         stg + rr * C::ROWB + ((c ^ (rr & (C::NC - 1))) * 16));
                     const int row = q0 + rr;
-                    if (row < Lb) *reinterpret_cast<u32x4_t*>(p.o + (s0 + row) * p.ldo + head * HD + c * 8) = v;
+                    if (row < Lb) __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p.o + (s0 + row) * p.ldo + head * HD + c * 8));
                 }
             }
             // the staging areas are the next item's first K/V buffers
