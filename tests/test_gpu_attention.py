@@ -207,6 +207,29 @@ def test_deep_varlen_batch_equals_each_sequence_alone_bitwise(lens, H, Hk):
     assert_close(got, want, "deep varlen")
 
 
+def test_growing_scores_move_the_reference_on_every_tile():
+    """Keys whose magnitude steps up every 64 positions raise a row's scores by
+    about 16 (in log2 units) from one kv tile to the next, far past the
+    2^12 tile-sum limit of the lazy softmax: every row moves its reference on
+    every new tile it sees, so O and l are rescaled mid-sequence many times
+    (with N(0,1) inputs a row's reference practically never moves after its
+    first tile).  The output must still match the oracle."""
+    require_gpu()
+    T, H, Hk, hd = 520, 4, 2, 128
+    w, buf = _mk(T, H, Hk, hd, 50)
+    rng = np.random.default_rng(50)
+    q = 0.25 + 0.05 * rng.standard_normal((T, H * hd))
+    # q.k grows by 128 * 0.25 * 4 = 128 per tile: 128 / sqrt(128) * log2(e) = 16.3
+    kmag = 4.0 * (np.arange(T) // 64)[:, None] + 0.1 * rng.standard_normal((T, Hk * hd))
+    buf[:, :H * hd] = torch.from_numpy(q.astype(np.float32)).to(torch.bfloat16)
+    buf[:, H * hd:(H + Hk) * hd] = torch.from_numpy(kmag.astype(np.float32)).to(torch.bfloat16)
+    say(f"prefill_attention growing scores T={T} heads={H}/{Hk} hd={hd} seed=50")
+    o = _gpu_attention(w, buf)
+    qq, kk, vv = _oracle_inputs(w, buf)
+    want = A.causal_attention(qq, kk, vv)
+    assert_close(o.float().cpu().numpy(), want, "growing scores")
+
+
 def test_deterministic_bitwise():
     require_gpu()
     w, buf = _mk(1000, 8, 2, 128, 47)
