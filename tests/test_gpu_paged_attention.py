@@ -120,6 +120,25 @@ def test_long_prefix_gqa_sampled():
     assert_close(got[rows], _oracle(c, rows=rows), "paged s=8192 chunk")
 
 
+def test_growing_scores_move_the_reference_on_every_tile():
+    """Paged keys whose magnitude steps up every 64 positions raise the chunk
+    rows' scores by about 16 (log2 units) per kv tile, so every row moves its
+    softmax reference on every tile of the prefix and of the chunk (O and l
+    rescaled many times); the output must still match the oracle."""
+    require_gpu()
+    H, Hk, hd = 4, 2, 128
+    c = _case(77, [100], [300], H, Hk, hd)
+    ctx = int(c["ctx"][0])
+    rng = np.random.default_rng(77)
+    kmag = 4.0 * (np.arange(ctx) // 64)[:, None] + 0.1 * rng.standard_normal((ctx, Hk * hd))
+    c["kb"] = bits(torch.from_numpy(kmag.astype(np.float32)).to(torch.bfloat16)).reshape(-1, Hk, hd)
+    c["kc"], c["vc"] = kvcache.paged_write_bf16(c["kb"], c["vb"], c["cu_k"], c["bt"], c["kc"].shape[0])
+    q = 0.25 + 0.05 * rng.standard_normal((100, H * hd))
+    c["q"] = torch.from_numpy(q.astype(np.float32)).to(torch.bfloat16)
+    say(f"prefill_attention_paged growing scores: chunk 100 over prefix 300, heads {H}/{Hk}, seed 77")
+    assert_close(_gpu(c).float().cpu().numpy(), _oracle(c), "paged growing scores")
+
+
 def _case_fp8(seed, chunks, prefixes, H, Hk, hd, spare=3):
     """As _case, with the keys quantised into fp8 pools (codes + scales) by the oracle."""
     c = _case(seed, chunks, prefixes, H, Hk, hd, spare)
