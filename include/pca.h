@@ -269,8 +269,10 @@ pca_status pca_prefill_attention_window(const pca_bf16* q, const pca_bf16* k, co
  *        and rounded to bf16 on chip before the matrix products; k_scale and
  *        v_scale must then be given (NULL for a bf16 cache).  Each pool must
  *        be smaller than 2 GiB.
- *        Block-table entries outside [0, num_pages) give unspecified output,
- *        never an access outside the pools.
+ *        A block-table entry outside [0, num_pages) makes its 16 keys (and,
+ *        for fp8, their scales) read as zeros: the output is then not that of
+ *        any real cache, but no access leaves the K, V or scale pools (each
+ *        is read through a buffer view of exactly its own size).
  *   head_dim 32, 64 or 128; causal must be 1.
  */
 pca_status pca_prefill_attention_paged(const pca_bf16* q, int64_t ldq, const int32_t* cu_seqlens_q, int num_seqs,

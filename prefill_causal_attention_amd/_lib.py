@@ -91,8 +91,33 @@ def _check(fn: str, status: int) -> None:
         raise PcaError(fn, status, load().pca_last_error().decode())
 
 
-def _ptr(t) -> Optional[int]:
-    return None if t is None else t.data_ptr()
+_DT = {}
+
+
+def _dtype(kind: str):
+    """torch dtype of an argument kind (torch is imported lazily: the host-only
+    calls need no torch)."""
+    if not _DT:
+        import torch
+        _DT.update(bf16=torch.bfloat16, u8=torch.uint8, f32=torch.float32, i32=torch.int32)
+    return _DT[kind]
+
+
+def _dev(t, name: str, kind: str):
+    """t must be a device tensor of the given element type; its pointer is
+    handed to a kernel, so a host tensor or another dtype is rejected here."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor (got {type(t).__name__})")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor (got device {t.device})")
+    if t.dtype != _dtype(kind):
+        raise ValueError(f"{name} must have dtype {_dtype(kind)} (got {t.dtype})")
+    return t
+
+
+def _ptr(t, name: str = "tensor", kind: str = "i32") -> Optional[int]:
+    return None if t is None else _dev(t, name, kind).data_ptr()
 
 
 def _stream(stream) -> Optional[int]:
@@ -102,11 +127,52 @@ def _stream(stream) -> Optional[int]:
     return torch.cuda.current_stream().cuda_stream
 
 
-def _rows(t, name: str):
-    """(pointer, row stride) of a 2-D row-major view with unit column stride."""
+def _rows(t, name: str, kind: str = "bf16"):
+    """(pointer, row stride) of a 2-D row-major device view with unit column
+    stride and the given element type."""
+    _dev(t, name, kind)
     if t.dim() != 2 or t.stride(1) != 1:
         raise ValueError(f"{name} must be a 2-D view with unit column stride")
     return t.data_ptr(), t.stride(0)
+
+
+def _flat(t, name: str, kind: str, n: int):
+    """Pointer of a contiguous device tensor of at least n elements."""
+    _dev(t, name, kind)
+    if not t.is_contiguous() or t.numel() < n:
+        raise ValueError(f"{name} must be contiguous with at least {n} elements (got {tuple(t.shape)})")
+    return t.data_ptr()
+
+
+def _table(t, name: str):
+    """Pointer and row length of a 2-D contiguous int32 device table."""
+    _dev(t, name, "i32")
+    if t.dim() != 2 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous 2-D int32 tensor [num_seqs, max_pages_per_seq]")
+    return t.data_ptr(), t.shape[1]
+
+
+def _cu(cu_seqlens, name: str = "cu_seqlens"):
+    """(pointer or None, num_seqs) of an optional int32 [num_seqs + 1] table."""
+    if cu_seqlens is None:
+        return None, 1
+    _flat(cu_seqlens, name, "i32", 1)
+    return cu_seqlens.data_ptr(), cu_seqlens.numel() - 1
+
+
+def _pool(t, name: str, cache_dtype: str):
+    """Pointer of a contiguous page pool: bf16 pools hold 16-bit patterns
+    (torch.bfloat16, or torch.int16 for the same bits), fp8 pools uint8 codes."""
+    import torch
+    if cache_dtype not in DTYPES:
+        raise ValueError(f"unknown cache dtype {cache_dtype!r} (bf16 or fp8_e4m3)")
+    if cache_dtype == "bf16" and isinstance(t, torch.Tensor) and t.dtype == torch.int16:
+        _dev(t.view(torch.bfloat16), name, "bf16")
+    else:
+        _dev(t, name, "bf16" if cache_dtype == "bf16" else "u8")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
 
 
 def version() -> str:
@@ -138,36 +204,37 @@ def quantize_rows_fp8(x, q, scales, stream=None):
     """Row-wise E4M3 codes of the bf16 2-D view x into the uint8 view q, with
     the per-row scales (float32, (M,))."""
     px, ldx = _rows(x, "x")
-    pq, ldq = _rows(q, "q")
+    pq, ldq = _rows(q, "q", "u8")
     M, K = x.shape
-    if tuple(q.shape) != (M, K) or scales.numel() < M:
+    if tuple(q.shape) != (M, K):
         raise ValueError(f"shape mismatch: x {tuple(x.shape)}, q {tuple(q.shape)}")
-    _check("pca_quantize_rows_fp8", load().pca_quantize_rows_fp8(px, ldx, M, K, pq, ldq, scales.data_ptr(),
-                                                                 _stream(stream)))
+    ps = _flat(scales, "scales", "f32", M)
+    _check("pca_quantize_rows_fp8", load().pca_quantize_rows_fp8(px, ldx, M, K, pq, ldq, ps, _stream(stream)))
     return q
 
 
 def e4m3_encode(x, codes, stream=None):
     """E4M3 codes (RNE, saturating at +-448) of the contiguous float32 tensor x
     into the contiguous uint8 tensor codes of the same number of elements."""
-    if not x.is_contiguous() or not codes.is_contiguous() or codes.numel() != x.numel():
-        raise ValueError("x and codes must be contiguous with the same number of elements")
-    if x.element_size() != 4 or codes.element_size() != 1:
-        raise ValueError("x must be float32 and codes uint8")
-    _check("pca_e4m3_encode", load().pca_e4m3_encode(x.data_ptr(), codes.data_ptr(), x.numel(), _stream(stream)))
+    px = _flat(x, "x", "f32", 0)
+    pc = _flat(codes, "codes", "u8", x.numel())
+    if codes.numel() != x.numel():
+        raise ValueError("x and codes must have the same number of elements")
+    _check("pca_e4m3_encode", load().pca_e4m3_encode(px, pc, x.numel(), _stream(stream)))
     return codes
 
 
 def qkv_proj_fp8(xq, sx, wq, sw, y, stream=None):
     """y = diag(sx) (dec(xq) @ dec(wq)^T) diag(sw) on fp8 matrix cores, bf16 out."""
-    pxq, ldxq = _rows(xq, "xq")
-    pwq, ldwq = _rows(wq, "wq")
+    pxq, ldxq = _rows(xq, "xq", "u8")
+    pwq, ldwq = _rows(wq, "wq", "u8")
     py, ldy = _rows(y, "y")
     M, K = xq.shape
     N = wq.shape[0]
-    if wq.shape[1] != K or tuple(y.shape) != (M, N) or sx.numel() < M or sw.numel() < N:
+    if wq.shape[1] != K or tuple(y.shape) != (M, N):
         raise ValueError(f"shape mismatch: xq {tuple(xq.shape)}, wq {tuple(wq.shape)}, y {tuple(y.shape)}")
-    _check("pca_qkv_proj_fp8", load().pca_qkv_proj_fp8(pxq, ldxq, sx.data_ptr(), pwq, ldwq, sw.data_ptr(), py, ldy,
+    psx, psw = _flat(sx, "sx", "f32", M), _flat(sw, "sw", "f32", N)
+    _check("pca_qkv_proj_fp8", load().pca_qkv_proj_fp8(pxq, ldxq, psx, pwq, ldwq, psw, py, ldy,
                                                        M, N, K, _stream(stream)))
     return y
 
@@ -181,9 +248,10 @@ def rms_norm_qkv_proj(x, w_t_g, y, inv_rms, eps: float = 1e-6, stream=None):
     py, ldy = _rows(y, "y")
     M, K = x.shape
     N = w_t_g.shape[0]
-    if w_t_g.shape[1] != K or tuple(y.shape) != (M, N) or inv_rms.numel() < M:
+    if w_t_g.shape[1] != K or tuple(y.shape) != (M, N):
         raise ValueError(f"shape mismatch: x {tuple(x.shape)}, w_t_g {tuple(w_t_g.shape)}, y {tuple(y.shape)}")
-    _check("pca_rms_norm_qkv_proj", load().pca_rms_norm_qkv_proj(px, ldx, pw, ldw, float(eps), inv_rms.data_ptr(),
+    pr = _flat(inv_rms, "inv_rms", "f32", M)
+    _check("pca_rms_norm_qkv_proj", load().pca_rms_norm_qkv_proj(px, ldx, pw, ldw, float(eps), pr,
                                                                  py, ldy, M, N, K, _stream(stream)))
     return y
 
@@ -217,15 +285,14 @@ def qkv_proj_kv_write(x, w_t, y, block_table, k_cache, v_cache, n_head: int, n_k
     N = (n_head + 2 * n_kv_head) * head_dim
     if tuple(w_t.shape) != (N, K) or tuple(y.shape) != (M, N):
         raise ValueError(f"shape mismatch: x {tuple(x.shape)}, w_t {tuple(w_t.shape)}, y {tuple(y.shape)}, N={N}")
-    num_seqs = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
-    if block_table.dim() != 2:
-        raise ValueError("block_table must be 2-D [num_seqs, max_pages_per_seq]")
-    elem = 2 if cache_dtype == "bf16" else 1
-    num_pages = k_cache.numel() * k_cache.element_size() // (page_size * n_kv_head * head_dim * elem)
+    pcu, num_seqs = _cu(cu_seqlens)
+    pbt, mp = _table(block_table, "block_table")
+    pk, pv = _pool(k_cache, "k_cache", cache_dtype), _pool(v_cache, "v_cache", cache_dtype)
+    num_pages = k_cache.numel() // (page_size * n_kv_head * head_dim)
     _check("pca_qkv_proj_kv_write", load().pca_qkv_proj_kv_write(
-        px, ldx, pw, ldw, py, ldy, M, K, n_head, n_kv_head, head_dim, _ptr(cu_seqlens), num_seqs,
-        block_table.data_ptr(), block_table.shape[1], page_size, DTYPES[cache_dtype],
-        k_cache.data_ptr(), v_cache.data_ptr(), _ptr(k_scale), _ptr(v_scale), num_pages, _stream(stream)))
+        px, ldx, pw, ldw, py, ldy, M, K, n_head, n_kv_head, head_dim, pcu, num_seqs,
+        pbt, mp, page_size, DTYPES[cache_dtype], pk, pv, _ptr(k_scale, "k_scale", "f32"),
+        _ptr(v_scale, "v_scale", "f32"), num_pages, _stream(stream)))
     return y
 
 
@@ -241,18 +308,20 @@ def prefill_attention(q, k, v, o, n_head: int, n_kv_head: int, head_dim: int,
     pv, ldv = _rows(v, "v")
     po, ldo = _rows(o, "o")
     T = q.shape[0] if total_tokens is None else int(total_tokens)
-    num_seqs = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
+    if min(k.shape[0], v.shape[0], o.shape[0]) < T:
+        raise ValueError(f"q, k, v and o need at least total_tokens = {T} rows")
+    pcu, num_seqs = _cu(cu_seqlens)
     if max_seqlen is None:
         max_seqlen = T
     if scale is None:
         scale = head_dim ** -0.5
     if window:
         _check("pca_prefill_attention_window", load().pca_prefill_attention_window(
-            pq, pk, pv, ldq, ldk, ldv, _ptr(cu_seqlens), num_seqs, int(max_seqlen), T,
+            pq, pk, pv, ldq, ldk, ldv, pcu, num_seqs, int(max_seqlen), T,
             n_head, n_kv_head, head_dim, float(scale), 1, int(window), po, ldo, _stream(stream)))
         return o
     _check("pca_prefill_attention", load().pca_prefill_attention(
-        pq, pk, pv, ldq, ldk, ldv, _ptr(cu_seqlens), num_seqs, int(max_seqlen), T,
+        pq, pk, pv, ldq, ldk, ldv, pcu, num_seqs, int(max_seqlen), T,
         n_head, n_kv_head, head_dim, float(scale), 1, po, ldo, _stream(stream)))
     return o
 
@@ -262,8 +331,8 @@ def quantize_heads_fp8(x, codes, exps, n_heads: int, head_dim: int, prescale: fl
     x: bf16 (T, >= n_heads*head_dim) view; codes: uint8 (T, >= n_heads*head_dim)
     view; exps: uint8 (T, >= n_heads) view (scale bytes e + 127)."""
     px, ldx = _rows(x, "x")
-    pc, ldc = _rows(codes, "codes")
-    pe, lde = _rows(exps, "exps")
+    pc, ldc = _rows(codes, "codes", "u8")
+    pe, lde = _rows(exps, "exps", "u8")
     T = x.shape[0]
     if codes.shape[0] != T or exps.shape[0] != T:
         raise ValueError("x, codes and exps must have the same number of rows")
@@ -279,18 +348,20 @@ def prefill_attention_fp8qk(q, k_codes, k_exps, v, o, n_head: int, n_kv_head: in
     after the scale * log2(e) factor), K as codes + scale bytes from
     quantize_heads_fp8, v bf16; o bf16 (T, n_head*head_dim)."""
     pq, ldq = _rows(q, "q")
-    pk, ldk = _rows(k_codes, "k_codes")
-    pe, lde = _rows(k_exps, "k_exps")
+    pk, ldk = _rows(k_codes, "k_codes", "u8")
+    pe, lde = _rows(k_exps, "k_exps", "u8")
     pv, ldv = _rows(v, "v")
     po, ldo = _rows(o, "o")
     T = q.shape[0] if total_tokens is None else int(total_tokens)
-    num_seqs = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
+    if min(k_codes.shape[0], k_exps.shape[0], v.shape[0], o.shape[0]) < T:
+        raise ValueError(f"q, k_codes, k_exps, v and o need at least total_tokens = {T} rows")
+    pcu, num_seqs = _cu(cu_seqlens)
     if max_seqlen is None:
         max_seqlen = T
     if scale is None:
         scale = head_dim ** -0.5
     _check("pca_prefill_attention_fp8qk", load().pca_prefill_attention_fp8qk(
-        pq, ldq, pk, ldk, pe, lde, pv, ldv, _ptr(cu_seqlens), num_seqs, int(max_seqlen), T,
+        pq, ldq, pk, ldk, pe, lde, pv, ldv, pcu, num_seqs, int(max_seqlen), T,
         n_head, n_kv_head, head_dim, float(scale), 1, po, ldo, _stream(stream)))
     return o
 
@@ -306,21 +377,23 @@ def prefill_attention_paged(q, o, k_cache, v_cache, block_table, ctx_lens, n_hea
     pq, ldq = _rows(q, "q")
     po, ldo = _rows(o, "o")
     T = q.shape[0] if total_tokens is None else int(total_tokens)
-    num_seqs = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
+    if o.shape[0] < T:
+        raise ValueError(f"q and o need at least total_tokens = {T} rows")
+    pcu, num_seqs = _cu(cu_seqlens, "cu_seqlens")
+    pctx = _flat(ctx_lens, "ctx_lens", "i32", num_seqs)
     if max_seqlen is None:
         max_seqlen = T
     if max_ctx is None:
         max_ctx = int(ctx_lens.max().item()) if ctx_lens.numel() else 0
     if scale is None:
         scale = head_dim ** -0.5
-    if block_table.dim() != 2:
-        raise ValueError("block_table must be 2-D [num_seqs, max_pages_per_seq]")
-    elem = 2 if cache_dtype == "bf16" else 1
-    num_pages = k_cache.numel() * k_cache.element_size() // (page_size * n_kv_head * head_dim * elem)
+    pbt, mp = _table(block_table, "block_table")
+    pk, pv = _pool(k_cache, "k_cache", cache_dtype), _pool(v_cache, "v_cache", cache_dtype)
+    num_pages = k_cache.numel() // (page_size * n_kv_head * head_dim)
     _check("pca_prefill_attention_paged", load().pca_prefill_attention_paged(
-        pq, ldq, _ptr(cu_seqlens), num_seqs, int(max_seqlen), T, ctx_lens.data_ptr(), int(max_ctx),
-        block_table.data_ptr(), block_table.shape[1], page_size, DTYPES[cache_dtype], k_cache.data_ptr(),
-        v_cache.data_ptr(), _ptr(k_scale), _ptr(v_scale), num_pages, n_head, n_kv_head, head_dim, float(scale), 1,
+        pq, ldq, pcu, num_seqs, int(max_seqlen), T, pctx, int(max_ctx),
+        pbt, mp, page_size, DTYPES[cache_dtype], pk, pv, _ptr(k_scale, "k_scale", "f32"),
+        _ptr(v_scale, "v_scale", "f32"), num_pages, n_head, n_kv_head, head_dim, float(scale), 1,
         po, ldo, _stream(stream)))
     return o
 
@@ -334,12 +407,13 @@ def kv_cache_write(k, v, block_table, k_cache, v_cache, n_kv_head: int, head_dim
     pk, ldk = _rows(k, "k")
     pv, ldv = _rows(v, "v")
     T = k.shape[0] if total_tokens is None else int(total_tokens)
-    num_seqs = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
-    if block_table.dim() != 2:
-        raise ValueError("block_table must be 2-D [num_seqs, max_pages_per_seq]")
-    elem = 2 if cache_dtype == "bf16" else 1
-    num_pages = k_cache.numel() * k_cache.element_size() // (page_size * n_kv_head * head_dim * elem)
+    if v.shape[0] < T:
+        raise ValueError(f"k and v need at least total_tokens = {T} rows")
+    pcu, num_seqs = _cu(cu_seqlens)
+    pbt, mp = _table(block_table, "block_table")
+    pkc, pvc = _pool(k_cache, "k_cache", cache_dtype), _pool(v_cache, "v_cache", cache_dtype)
+    num_pages = k_cache.numel() // (page_size * n_kv_head * head_dim)
     _check("pca_kv_cache_write", load().pca_kv_cache_write(
-        pk, pv, ldk, ldv, _ptr(cu_seqlens), num_seqs, T, block_table.data_ptr(), block_table.shape[1],
-        n_kv_head, head_dim, page_size, DTYPES[cache_dtype], k_cache.data_ptr(), v_cache.data_ptr(),
-        _ptr(k_scale), _ptr(v_scale), num_pages, _stream(stream)))
+        pk, pv, ldk, ldv, pcu, num_seqs, T, pbt, mp,
+        n_kv_head, head_dim, page_size, DTYPES[cache_dtype], pkc, pvc,
+        _ptr(k_scale, "k_scale", "f32"), _ptr(v_scale, "v_scale", "f32"), num_pages, _stream(stream)))

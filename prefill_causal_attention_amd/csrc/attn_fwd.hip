@@ -245,6 +245,7 @@ struct Params {
     int mp;             // block-table row length
     const int32_t* ctx;
     uint32_t pool_bytes;
+    int num_pages;      // paged: block-table entries outside [0, num_pages) read as zeros
     int window;         // > 0: sliding window, row r sees keys r - window < c <= r
     const float* k_scale;   // fp8 pages: per-(slot, kv head) scales [page][16][n_kv]
     const float* v_scale;
@@ -315,7 +316,7 @@ __device__ __forceinline__ void dma_tile_k8(const uint8_t* src, int64_t ld, cons
 // offset.  Same lane -> (row, swizzled chunk) map as dma_tile.
 template <int HD>
 __device__ __forceinline__ void dma_tile_paged(__amdgpu_buffer_rsrc_t r, int wave, int lane, int kbase, int Lk,
-                                               int n_kv, int g, lds_char_t* dst,
+                                               int n_kv, int g, int num_pages, lds_char_t* dst,
                                                const __attribute__((address_space(3))) int32_t* lbt) {
     using C = Cfg<HD>;
 #pragma unroll
@@ -326,8 +327,9 @@ __device__ __forceinline__ void dma_tile_paged(__amdgpu_buffer_rsrc_t r, int wav
             const int lch = (lane % C::NC) ^ swz<HD>(row);
             const int c = kbase + row;
             uint32_t off = kOob;
-            if (c < Lk) {
-                const int64_t slot = (int64_t)lbt[c >> 4] * 16 + (c & 15);
+            const int page = c < Lk ? lbt[c >> 4] : -1;
+            if ((uint32_t)page < (uint32_t)num_pages) {   // a table entry outside the pool reads 0
+                const int64_t slot = (int64_t)page * 16 + (c & 15);
                 off = (uint32_t)(((slot * n_kv + g) * HD + lch * 8) * 2);
             }
             __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(dst + blk * 1024), 16, off, 0, 0, 0);
@@ -338,23 +340,26 @@ __device__ __forceinline__ void dma_tile_paged(__amdgpu_buffer_rsrc_t r, int wav
 // DMA of one fp8 tile (E4M3 codes) from a page pool into the staging buffer
 // `dst8`: wave w < NB8 loads block w, lane l the 16 codes of row
 // w * RPI8 + l / (HD/16), column chunk l % (HD/16); it also loads that row's
-// scale (0 for keys at or past Lk).  Returns the scale.
+// scale through the scale pool's own buffer resource `rs` (0 for keys at or
+// past Lk and for block-table entries outside the pool).  Returns the scale.
 template <int HD>
-__device__ __forceinline__ float dma_tile_fp8(__amdgpu_buffer_rsrc_t r, const float* scales, int wave, int lane,
-                                              int kbase, int Lk, int n_kv, int g, lds_char_t* dst8,
+__device__ __forceinline__ float dma_tile_fp8(__amdgpu_buffer_rsrc_t r, __amdgpu_buffer_rsrc_t rs, int wave, int lane,
+                                              int kbase, int Lk, int n_kv, int g, int num_pages, lds_char_t* dst8,
                                               const __attribute__((address_space(3))) int32_t* lbt) {
     using C = Cfg<HD>;
     float sc = 0.0f;
     if (wave < C::NB8) {
         const int row = wave * C::RPI8 + lane / (HD / 16);
         const int c = kbase + row;
-        uint32_t off = kOob;
-        if (c < Lk) {
-            const int64_t slot = (int64_t)lbt[c >> 4] * 16 + (c & 15);
-            off = (uint32_t)((slot * n_kv + g) * HD + (lane % (HD / 16)) * 16);
-            sc = scales[slot * n_kv + g];
+        uint32_t off = kOob, soff = kOob;
+        const int page = c < Lk ? lbt[c >> 4] : -1;
+        if ((uint32_t)page < (uint32_t)num_pages) {
+            const int64_t srow = ((int64_t)page * 16 + (c & 15)) * n_kv + g;
+            off = (uint32_t)(srow * HD + (lane % (HD / 16)) * 16);
+            soff = (uint32_t)(srow * 4);
         }
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(dst8 + wave * 1024), 16, off, 0, 0, 0);
+        sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, soff, 0, 0));
     }
     return sc;
 }
@@ -586,10 +591,15 @@ void attn_fwd_kernel(Params p) {
     constexpr int kBtOff = PAGED == 2 ? C::LDS_FP8 : C::LDS_BYTES;
     const __attribute__((address_space(3))) int32_t* lbt =
         (const __attribute__((address_space(3))) int32_t*)(lds + kBtOff);
-    [[maybe_unused]] __amdgpu_buffer_rsrc_t rk, rv;
+    [[maybe_unused]] __amdgpu_buffer_rsrc_t rk, rv, rks, rvs;
     if constexpr (kPaged) {
         rk = make_rsrc(p.k, p.pool_bytes);
         rv = make_rsrc(p.v, p.pool_bytes);
+        if constexpr (PAGED == 2) {
+            // the scale pools hold one fp32 per (slot, kv head): pool_bytes / HD * 4 bytes
+            rks = make_rsrc(p.k_scale, p.pool_bytes / HD * 4);
+            rvs = make_rsrc(p.v_scale, p.pool_bytes / HD * 4);
+        }
         // the row was loaded into registers before the Q tile (both latencies overlap)
         __attribute__((address_space(3))) int32_t* wbt = (__attribute__((address_space(3))) int32_t*)(lds + kBtOff);
 #pragma unroll
@@ -609,10 +619,10 @@ void attn_fwd_kernel(Params p) {
         if constexpr (kF8S) {
             dma_tile_k8(p.k8, p.ldk8, p.kex, p.ldke, s0, Lb, wave, tile * BK, lds + buf, dma_k8, dma_ex);
         } else if constexpr (PAGED == 2) {
-            pend_ks = dma_tile_fp8<HD>(rk, p.k_scale, wave, lane, tile * BK, Lk, p.n_kv, g, lds + f8_of(buf), lbt);
+            pend_ks = dma_tile_fp8<HD>(rk, rks, wave, lane, tile * BK, Lk, p.n_kv, g, p.num_pages, lds + f8_of(buf), lbt);
             pend_k = buf;
         } else if constexpr (PAGED == 1) {
-            dma_tile_paged<HD>(rk, wave, lane, tile * BK, Lk, p.n_kv, g, lds + buf, lbt);
+            dma_tile_paged<HD>(rk, wave, lane, tile * BK, Lk, p.n_kv, g, p.num_pages, lds + buf, lbt);
         } else {
             dma_tile<HD>(p.k, p.ldk, s0, Lb, wave, tile * BK, lds + buf, dma_k);
         }
@@ -621,10 +631,10 @@ void attn_fwd_kernel(Params p) {
         if constexpr (kF8S) {
             dma_tile<HD>(p.v, p.ldv, s0, Lb, wave, tile * BK, lds + buf, dma_v);
         } else if constexpr (PAGED == 2) {
-            pend_vs = dma_tile_fp8<HD>(rv, p.v_scale, wave, lane, tile * BK, Lk, p.n_kv, g, lds + f8_of(buf), lbt);
+            pend_vs = dma_tile_fp8<HD>(rv, rvs, wave, lane, tile * BK, Lk, p.n_kv, g, p.num_pages, lds + f8_of(buf), lbt);
             pend_v = buf;
         } else if constexpr (PAGED == 1) {
-            dma_tile_paged<HD>(rv, wave, lane, tile * BK, Lk, p.n_kv, g, lds + buf, lbt);
+            dma_tile_paged<HD>(rv, wave, lane, tile * BK, Lk, p.n_kv, g, p.num_pages, lds + buf, lbt);
         } else {
             dma_tile<HD>(p.v, p.ldv, s0, Lb, wave, tile * BK, lds + buf, dma_v);
         }
@@ -1093,6 +1103,7 @@ hipError_t launch_cfg(const AttnArgs& a, hipStream_t s) {
     p.k_scale = a.k_scale;
     p.v_scale = a.v_scale;
     p.pool_bytes = (uint32_t)a.pool_bytes;
+    p.num_pages = (int)a.num_pages;
     p.k8 = a.k8;
     p.ldk8 = a.ldk8;
     p.kex = a.kex;

@@ -49,6 +49,19 @@ bool supported_head_dim(int hd) { return hd == 32 || hd == 64 || hd == 128; }
 
 constexpr int64_t kMaxBufferBytes = int64_t(1) << 31;   // buffer-resource offsets stay below 2^31
 
+// a * b * c for non-negative factors, or INT64_MAX when the product does not
+// fit in int64 (so a size check against any bound refuses it)
+int64_t sat_mul(int64_t a, int64_t b, int64_t c = 1) {
+    int64_t r;
+    if (a < 0 || b < 0 || c < 0) return INT64_MAX;
+    if (__builtin_mul_overflow(a, b, &r) || __builtin_mul_overflow(r, c, &r)) return INT64_MAX;
+    return r;
+}
+
+// true when a view of `rows` rows of stride `ld` elements of `elem` bytes
+// reaches 2 GiB (the reach of one buffer resource)
+bool view_too_big(int64_t rows, int64_t ld, int64_t elem) { return sat_mul(rows, ld, elem) >= kMaxBufferBytes; }
+
 pca_status hip_status(hipError_t e, const char* what) {
     if (e != hipSuccess) return fail(PCA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
     return ok();
@@ -79,7 +92,7 @@ pca_status check_gemm(const pca_bf16* x, int64_t ldx, const pca_bf16* w_t, int64
     if (ldx < K || ldw < K || ldy < N || ldx % 8 || ldw % 8 || ldy % 8)
         return fail(PCA_ERR_INVALID_ARG, "leading dimensions must be >= the row width and multiples of 8 "
                     "(ldx=%lld ldw=%lld ldy=%lld)", (long long)ldx, (long long)ldw, (long long)ldy);
-    if (256 * ldx * 2 >= kMaxBufferBytes || 256 * ldw * 2 >= kMaxBufferBytes)
+    if (view_too_big(256, ldx, 2) || view_too_big(256, ldw, 2))
         return fail(PCA_ERR_UNSUPPORTED, "row stride too large for a 256-row tile view");
     memset(&a, 0, sizeof(a));
     a.x = x; a.ldx = ldx; a.w = w_t; a.ldw = ldw; a.y = y; a.ldy = ldy;
@@ -114,7 +127,7 @@ pca_status check_kv_cache(const int32_t* cu_seqlens, int num_seqs, int64_t total
     } else {
         return fail(PCA_ERR_UNSUPPORTED, "unknown cache dtype %d", (int)cache_dtype);
     }
-    if (total_tokens * 2 * ((int64_t)n_kv_head * head_dim / 8) >= (int64_t(1) << 31))
+    if (n_kv_head <= 0 || sat_mul(total_tokens, 2, sat_mul(n_kv_head, head_dim) / 8) >= (int64_t(1) << 31))
         return fail(PCA_ERR_UNSUPPORTED, "batch too large (total_tokens * n_kv_head * head_dim)");
     return PCA_OK;
 }
@@ -195,7 +208,7 @@ pca_status pca_qkv_proj_fp8(const uint8_t* xq, int64_t ldxq, const float* sx, co
     if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return fail(PCA_ERR_INVALID_ARG, "M, N, K must fit in int32");
     if (ldxq < K || ldwq < K || ldy < N || ldxq % 16 || ldwq % 16 || ldy % 8)
         return fail(PCA_ERR_INVALID_ARG, "ldxq, ldwq >= K (multiples of 16), ldy >= N (multiple of 8) required");
-    if (256 * ldxq >= kMaxBufferBytes || 256 * ldwq >= kMaxBufferBytes)
+    if (view_too_big(256, ldxq, 1) || view_too_big(256, ldwq, 1))
         return fail(PCA_ERR_UNSUPPORTED, "row stride too large for a 256-row tile view");
     pca::Fp8GemmArgs a;
     a.x = xq; a.ldx = ldxq; a.sx = sx; a.w = wq; a.ldw = ldwq; a.sw = sw; a.y = y; a.ldy = ldy;
@@ -227,12 +240,17 @@ pca_status pca_out_proj_residual(const pca_bf16* o, int64_t ldo, const pca_bf16*
     if (!aligned16(res) || ldr < N || ldr % 8)
         return fail(PCA_ERR_INVALID_ARG, "res must be 16-byte aligned with ldr >= N and a multiple of 8");
     if (res != out) {
-        // res may be out itself (in-place residual update) but must not partly overlap it
-        const char* r0 = (const char*)res;
-        const char* r1 = r0 + ((M - 1) * ldr + N) * 2;
-        const char* o0 = (const char*)out;
-        const char* o1 = o0 + ((M - 1) * ldout + N) * 2;
-        if (r0 < o1 && o0 < r1) return fail(PCA_ERR_INVALID_ARG, "res overlaps out without being out");
+        // res may be out itself (in-place residual update) but must not partly overlap it;
+        // extents in bytes, refused when they do not fit (addresses compared as integers)
+        auto extent = [](int64_t rows, int64_t ld, int64_t width) -> int64_t {
+            const int64_t e = sat_mul(rows - 1, ld);
+            return e >= INT64_MAX / 4 ? INT64_MAX : (e + width) * 2;
+        };
+        const int64_t rb = extent(M, ldr, N), ob = extent(M, ldout, N);
+        if (rb == INT64_MAX || ob == INT64_MAX) return fail(PCA_ERR_INVALID_ARG, "res or out extent overflows");
+        const uintptr_t r0 = (uintptr_t)res, o0 = (uintptr_t)out;
+        if (r0 < o0 + (uint64_t)ob && o0 < r0 + (uint64_t)rb)
+            return fail(PCA_ERR_INVALID_ARG, "res overlaps out without being out");
     } else if (ldr != ldout) {
         return fail(PCA_ERR_INVALID_ARG, "in-place residual needs ldr == ldout");
     }
@@ -315,8 +333,7 @@ pca_status pca_prefill_attention_window(const pca_bf16* q, const pca_bf16* k, co
         return fail(PCA_ERR_INVALID_ARG, "max_seqlen must be >= 1 and cover the sequence (got %d)", max_seqlen);
     // each sequence is read through its own buffer view, which must stay below 2 GiB
     const int64_t longest = cu_seqlens ? (max_seqlen < total_tokens ? max_seqlen : total_tokens) : total_tokens;
-    if (longest * ldq * 2 >= kMaxBufferBytes || longest * ldk * 2 >= kMaxBufferBytes ||
-        longest * ldv * 2 >= kMaxBufferBytes)
+    if (view_too_big(longest, ldq, 2) || view_too_big(longest, ldk, 2) || view_too_big(longest, ldv, 2))
         return fail(PCA_ERR_UNSUPPORTED, "per-sequence q/k/v views beyond 2 GiB are not supported");
     pca::AttnArgs a;
     memset(&a, 0, sizeof(a));
@@ -355,8 +372,8 @@ pca_status pca_prefill_attention_fp8qk(const pca_bf16* q, int64_t ldq, const uin
     if (max_seqlen < 1 || (cu_seqlens == nullptr && max_seqlen < total_tokens))
         return fail(PCA_ERR_INVALID_ARG, "max_seqlen must be >= 1 and cover the sequence (got %d)", max_seqlen);
     const int64_t longest = cu_seqlens ? (max_seqlen < total_tokens ? max_seqlen : total_tokens) : total_tokens;
-    if (longest * ldq * 2 >= kMaxBufferBytes || longest * ldk >= kMaxBufferBytes || longest * lde >= kMaxBufferBytes ||
-        longest * ldv * 2 >= kMaxBufferBytes)
+    if (view_too_big(longest, ldq, 2) || view_too_big(longest, ldk, 1) || view_too_big(longest, lde, 1) ||
+        view_too_big(longest, ldv, 2))
         return fail(PCA_ERR_UNSUPPORTED, "per-sequence q/k/v views beyond 2 GiB are not supported");
     pca::AttnArgs a;
     memset(&a, 0, sizeof(a));
@@ -414,13 +431,13 @@ pca_status pca_prefill_attention_paged(const pca_bf16* q, int64_t ldq, const int
     if (max_ctx_len < max_seqlen_q || (int64_t)max_ctx_len > (int64_t)max_pages_per_seq * page_size)
         return fail(PCA_ERR_INVALID_ARG, "max_ctx_len (%d) must be >= max_seqlen_q and <= max_pages_per_seq * page_size",
                     max_ctx_len);
-    const int64_t pool_bytes = num_pages * page_size * (int64_t)n_kv_head * head_dim * elem;
+    const int64_t pool_bytes = sat_mul(num_pages, page_size, sat_mul(n_kv_head, head_dim, elem));
     if (pool_bytes >= kMaxBufferBytes) return fail(PCA_ERR_UNSUPPORTED, "page pools of 2 GiB or more are not supported");
     // LDS: 4 bf16 tiles (+ 4 fp8 staging tiles) + the staged block-table row
     const int64_t lds = 4 * 64 * (int64_t)head_dim * (elem == 1 ? 3 : 2) + (((int64_t)max_ctx_len + 15) / 16 + 3) / 4 * 16;
     if (lds > 160 * 1024) return fail(PCA_ERR_UNSUPPORTED, "max_ctx_len %d too long for the staged block table", max_ctx_len);
     const int64_t longest = cu_seqlens_q ? (max_seqlen_q < total_q ? max_seqlen_q : total_q) : total_q;
-    if (longest * ldq * 2 >= kMaxBufferBytes) return fail(PCA_ERR_UNSUPPORTED, "per-sequence q views beyond 2 GiB");
+    if (view_too_big(longest, ldq, 2)) return fail(PCA_ERR_UNSUPPORTED, "per-sequence q views beyond 2 GiB");
     pca::AttnArgs a;
     memset(&a, 0, sizeof(a));
     a.q = q; a.k = (const uint16_t*)k_cache; a.v = (const uint16_t*)v_cache; a.ldq = ldq;
@@ -428,7 +445,7 @@ pca_status pca_prefill_attention_paged(const pca_bf16* q, int64_t ldq, const int
     a.total_tokens = total_q; a.n_head = n_head; a.n_kv_head = n_kv_head; a.head_dim = head_dim;
     a.scale = scale; a.o = o; a.ldo = ldo;
     a.block_table = block_table; a.max_pages_per_seq = max_pages_per_seq; a.ctx_lens = ctx_lens;
-    a.max_ctx = max_ctx_len; a.pool_bytes = pool_bytes;
+    a.max_ctx = max_ctx_len; a.pool_bytes = pool_bytes; a.num_pages = num_pages;
     a.k_scale = elem == 1 ? k_scale : nullptr; a.v_scale = elem == 1 ? v_scale : nullptr;
     return hip_status(pca::launch_attention(a, (hipStream_t)stream), "prefill_attention_paged launch");
 }
@@ -476,7 +493,7 @@ pca_status pca_quantize_heads_fp8(const pca_bf16* x, int64_t ldx, int64_t T, int
     if (ldx < w || ldx % 8 || ldc < w || ldc % 8 || lde < n_heads)
         return fail(PCA_ERR_INVALID_ARG, "ldx, ldc >= n_heads*head_dim (multiples of 8) and lde >= n_heads required");
     if (!(prescale > 0.0f && prescale <= 3.40282347e38f)) return fail(PCA_ERR_INVALID_ARG, "prescale must be finite and > 0");
-    if (T * w / 8 >= (int64_t(1) << 40)) return fail(PCA_ERR_UNSUPPORTED, "input too large");
+    if (sat_mul(T, w) / 8 >= (int64_t(1) << 40)) return fail(PCA_ERR_UNSUPPORTED, "input too large");
     return hip_status(pca::launch_quantize_heads(x, ldx, T, n_heads, head_dim, prescale, codes, ldc, exps, lde,
                                                  (hipStream_t)stream),
                       "quantize_heads_fp8 launch");

@@ -98,6 +98,7 @@ struct AttnArgs {
     const int32_t* ctx_lens;      // [num_seqs] keys per sequence (prefix + chunk)
     int max_ctx;
     int64_t pool_bytes;           // bytes of the K (and of the V) pool, < 2^31
+    int64_t num_pages;            // pages per pool (block-table entries outside [0, num_pages) read zeros)
     int window;                   // > 0: sliding window of that many keys (row r sees r - window < c <= r)
     const float* k_scale;         // paged fp8 pools: per-(slot, kv head) scales; null for bf16 pools
     const float* v_scale;

@@ -16,6 +16,7 @@ from oracle import bf16 as obf16
 from oracle import fp8, fp8_attention
 
 from _gpu_helpers import assert_close, bits, dev, require_gpu, sample_rows, say
+from test_oracle_fp8_attention import FP8_SCORE_MAX_ABS, FP8_SCORE_MEAN_ABS
 
 pytestmark = pytest.mark.gpu
 
@@ -94,6 +95,21 @@ def test_parity_full_size_sampled():
     # row 0 sees only key 0: its output is V's row 0 exactly
     v0 = np.repeat(np.asarray(v)[0], w.n_head // w.n_kv_head, axis=0).reshape(-1)
     assert np.array_equal(bits(o[0].cpu()), v0)
+
+
+def test_full_size_within_quantisation_bound_of_plain_attention():
+    """Against the plain definition on the unquantised bf16 Q and K (fp64, no
+    fp8 anywhere): the fp8 score operands may only add the E4M3 quantisation
+    error, bounded as derived for the oracle's fp8-score attention."""
+    require_gpu()
+    w = workloads.WORKLOADS[2]                       # s=8192, 32 q / 8 kv heads, hd 128
+    rows = sample_rows(w.total_tokens, 48, 4243)
+    got, _, _, _ = _run(w, rows=rows)
+    buf, _, _, _ = workloads.qkv_inputs(w)
+    q, k, v = A.head_split(bits(buf), w.n_head, w.n_kv_head, w.head_dim)
+    plain = A.varlen_causal_attention(q, k, v, workloads.cu_seqlens(w), rows=rows)
+    assert_close(got, plain, "fp8qk vs plain bf16-operand attention", max_tol=FP8_SCORE_MAX_ABS,
+                 mean_tol=FP8_SCORE_MEAN_ABS)
 
 
 def test_zero_q_gives_prefix_mean():

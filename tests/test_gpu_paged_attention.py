@@ -194,3 +194,63 @@ def test_fp8_pages_long_prefix_sampled():
     got = _gpu_fp8(c).float().cpu().numpy()
     rows = sample_rows(512, 32, 79, must=(0, 1, 63, 64, 511))
     assert_close(got[rows], _oracle_fp8(c, rows=rows), "paged fp8 16k prefix")
+
+
+def _run_table(c, bt, fp8):
+    """The paged kernel with the given raw block table (entries passed as they are)."""
+    T = int(c["cu_q"][-1])
+    nq = c["H"] * c["hd"]
+    o = torch.full((T, nq + 8), float("nan"), dtype=torch.bfloat16, device="cuda")
+    cu = dev(torch.from_numpy(c["cu_q"])) if len(c["ctx"]) > 1 else None
+    kc = c["kc"] if fp8 else c["kc"].view(np.int16)
+    vc = c["vc"] if fp8 else c["vc"].view(np.int16)
+    extra = dict(cache_dtype="fp8_e4m3", k_scale=dev(torch.from_numpy(c["ks"])),
+                 v_scale=dev(torch.from_numpy(c["vs"]))) if fp8 else {}
+    pca.prefill_attention_paged(dev(c["q"]), o[:, :nq], dev(torch.from_numpy(kc)), dev(torch.from_numpy(vc)),
+                                dev(torch.from_numpy(bt.astype(np.int32))), dev(torch.from_numpy(c["ctx"])),
+                                c["H"], c["Hk"], c["hd"], cu_seqlens=cu, max_seqlen=int(np.diff(c["cu_q"]).max()),
+                                max_ctx=int(c["ctx"].max()), **extra)
+    torch.cuda.synchronize()
+    assert torch.isnan(o[:, nq:].float()).all(), "wrote outside the heads"
+    return o[:, :nq]
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_table_entries_outside_the_pool(fp8):
+    """Block-table entries outside [0, num_pages) read as zeros (keys, values
+    and, for fp8, scales) and never leave the pools.  Unused entries (past a
+    sequence's pages) set to -1 and num_pages + k change nothing, bit for bit;
+    used entries set out of range give the attention over a zero page."""
+    require_gpu()
+    H, Hk, hd = 8, 2, 128
+    c = (_case_fp8 if fp8 else _case)(91, [70, 33, 5], [300, 0, 650], H, Hk, hd, spare=2)
+    pages = c["kc"].shape[0]
+    clean = np.where(c["bt"] < 0, 0, c["bt"])
+    say(f"prefill_attention_paged fp8={fp8}: table entries outside the pool ({pages} pages), seed 91")
+    ref = _run_table(c, clean, fp8)
+    unused = c["bt"].copy()
+    holes = np.argwhere(unused < 0)
+    for n, (b, j) in enumerate(holes):
+        unused[b, j] = -1 if n % 2 == 0 else pages + 1000 * n
+    assert len(holes) > 0
+    assert np.array_equal(bits(_run_table(c, unused, fp8)), bits(ref))
+
+    # used entries out of range: sequence 0's page 3 -> -7, sequence 2's page 10 -> pages + 5
+    bad = clean.copy()
+    bad[0, 3] = -7
+    bad[2, 10] = pages + 5
+    got = _run_table(c, bad, fp8).float().cpu().numpy()
+    assert np.all(np.isfinite(got))
+    # expected: the same pools with one more, all-zero page that the bad entries point at
+    zc = dict(c)
+    zc["kc"] = np.concatenate([c["kc"], np.zeros_like(c["kc"][:1])])
+    zc["vc"] = np.concatenate([c["vc"], np.zeros_like(c["vc"][:1])])
+    if fp8:
+        zc["ks"] = np.concatenate([c["ks"], np.zeros_like(c["ks"][:1])])
+        zc["vs"] = np.concatenate([c["vs"], np.zeros_like(c["vs"][:1])])
+    zbt = c["bt"].copy()
+    zbt[0, 3] = pages
+    zbt[2, 10] = pages
+    zc["bt"] = zbt
+    want = _oracle_fp8(zc) if fp8 else _oracle(zc)
+    assert_close(got, want, f"paged {'fp8' if fp8 else 'bf16'} zero page")

@@ -157,3 +157,56 @@ def test_window_chunk_rows_equal_whole_rows():
     whole = PX.window_causal_attention(q, k, v, W)
     chunk = PX.window_causal_attention(q[P:], k, v, W, prefix_len=P)
     assert np.max(np.abs(chunk - whole[P:])) < 1e-12
+
+
+def brute_force_varlen_window(q, k, v, cu, W, scale, rows):
+    """Pure-Python loops over a packed batch: global row t of sequence b
+    (tokens cu[b] .. cu[b+1]-1) weighs the keys of its own sequence at global
+    positions max(cu[b], t - W + 1) .. t."""
+    H, D = len(q[0]), len(q[0][0])
+    G = H // len(k[0])
+    out = []
+    for t in rows:
+        b = max(i for i in range(len(cu) - 1) if cu[i] <= t)
+        keys = range(max(cu[b], t - W + 1), t + 1)
+        o = [0.0] * (H * D)
+        for i in range(H):
+            g = i // G
+            sc = [sum(q[t][i][d] * k[c][g][d] for d in range(D)) * scale for c in keys]
+            mx = max(sc)
+            w = [math.exp(x - mx) for x in sc]
+            tot = sum(w)
+            for d in range(D):
+                o[i * D + d] = sum(wi * v[c][g][d] for wi, c in zip(w, keys)) / tot
+        out.append(o)
+    return np.array(out)
+
+
+@pytest.mark.parametrize("lens,W", [([7, 1, 9], 3), ([5, 12], 4), ([3, 3, 3], 1), ([10, 2], 20)])
+def test_varlen_window_brute_force(lens, W):
+    """Packed sequences: the window never reaches into the previous sequence,
+    and the rows= selection (global indices) picks the right rows."""
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T, H, Hk, D = int(cu[-1]), 4, 2, 3
+    q, k, v = _rand(40, T, H, D), _rand(41, T, Hk, D), _rand(42, T, Hk, D)
+    rows = [0, T - 1] + [int(c) for c in cu[1:-1]] + [int(c) - 1 for c in cu[1:-1]] + [T // 2]
+    rows = sorted(set(rows))
+    ref = brute_force_varlen_window(q.tolist(), k.tolist(), v.tolist(), cu.tolist(), W, 1 / math.sqrt(D), rows)
+    assert np.max(np.abs(PX.varlen_window_attention(q, k, v, cu, W, rows=np.array(rows)) - ref)) < 1e-12
+    full = brute_force_varlen_window(q.tolist(), k.tolist(), v.tolist(), cu.tolist(), W, 1 / math.sqrt(D), range(T))
+    assert np.max(np.abs(PX.varlen_window_attention(q, k, v, cu, W) - full)) < 1e-12
+
+
+def test_varlen_window_limits():
+    """W at least the longest sequence is the plain packed causal attention;
+    W = 1 returns every row's own V."""
+    lens = [13, 1, 30, 8]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T = int(cu[-1])
+    q, k, v = _rand(43, T, 6, 8), _rand(44, T, 3, 8), _rand(45, T, 3, 8)
+    plain = A.varlen_causal_attention(q, k, v, cu)
+    assert np.max(np.abs(PX.varlen_window_attention(q, k, v, cu, 30) - plain)) < 1e-12
+    assert np.max(np.abs(PX.varlen_window_attention(q, k, v, cu, 10 ** 6) - plain)) < 1e-12
+    own = PX.varlen_window_attention(q, k, v, cu, 1)
+    for i in range(6):
+        assert np.array_equal(own[:, i * 8:(i + 1) * 8], v[:, i // 2, :])
