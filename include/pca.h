@@ -146,6 +146,26 @@ pca_status pca_rms_norm_qkv_proj(const pca_bf16* x, int64_t ldx, const pca_bf16*
                                  float* inv_rms, pca_bf16* y, int64_t ldy, int64_t M, int64_t N, int64_t K,
                                  void* stream);
 
+/* Rows the static workspace of pca_rms_norm_qkv_proj_noalloc holds (1 MiB of fp32). */
+#define PCA_NOALLOC_MAX_ROWS 262144
+
+/*
+ * pca_rms_norm_qkv_proj_noalloc -- pca_rms_norm_qkv_proj for callers that
+ *   cannot allocate device memory (code under HIP graph capture, tight
+ *   serving loops, harnesses that forbid hipMalloc): the same result, with
+ *   the per-row 1/rms workspace taken from a fixed device array inside the
+ *   library (PCA_NOALLOC_MAX_ROWS floats per GPU, held until the process
+ *   ends) instead of an inv_rms argument.  The call itself allocates and
+ *   frees nothing.  Arguments and errors as pca_rms_norm_qkv_proj; M beyond
+ *   PCA_NOALLOC_MAX_ROWS is PCA_ERR_UNSUPPORTED.  All calls on one GPU share
+ *   its array (it keeps the last call's 1/rms values): calls whose work
+ *   overlaps in time on one GPU (other streams or host threads) race and must
+ *   be serialised by the caller.
+ */
+pca_status pca_rms_norm_qkv_proj_noalloc(const pca_bf16* x, int64_t ldx, const pca_bf16* w_t, int64_t ldw,
+                                         float eps, pca_bf16* y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                                         void* stream);
+
 /*
  * pca_out_proj_residual -- the output projection and residual add that close
  *   the attention unit: out = res + o * w_t^T.  The data-flow article's §2.1

@@ -6,6 +6,7 @@ Calls (same names as the C ABI in include/pca.h, minus the ``pca_`` prefix):
   qkv_proj_kv_write  the same GEMM, its epilogue also writing K/V into the pages
   out_proj_residual  output projection W_o with the residual add (one rounding)
   rms_norm_qkv_proj  the input RMSNorm folded into the QKV GEMM (row scale in the epilogue)
+  rms_norm_qkv_proj_noalloc  the same with the library's static workspace (no allocation)
   quantize_rows_fp8  row-wise E4M3 quantisation of GEMM operands
   qkv_proj_fp8       the QKV GEMM on fp8 operands (fp8 matrix cores, fp32 accumulate)
   e4m3_encode        elementwise float32 -> E4M3 codes (the encoder of every fp8 result)
@@ -17,13 +18,14 @@ Calls (same names as the C ABI in include/pca.h, minus the ``pca_`` prefix):
 All compute runs in hand-written HIP kernels; PyTorch only provides device
 memory and the current stream.
 """
-from ._lib import (EXPORTED, PcaError, e4m3_encode, kv_cache_write, kv_layout, load,  # noqa: F401
+from ._lib import (EXPORTED, NOALLOC_MAX_ROWS, PcaError, e4m3_encode, kv_cache_write, kv_layout, load,  # noqa: F401
                    out_proj_residual, prefill_attention, prefill_attention_fp8qk, prefill_attention_paged,
                    qkv_proj, qkv_proj_fp8, qkv_proj_kv_write, quantize_heads_fp8, quantize_rows_fp8,
-                   rms_norm_qkv_proj, version)
+                   rms_norm_qkv_proj, rms_norm_qkv_proj_noalloc, version)
 
-__all__ = ["kv_layout", "qkv_proj", "qkv_proj_kv_write", "rms_norm_qkv_proj", "out_proj_residual", "quantize_rows_fp8",
+__all__ = ["kv_layout", "qkv_proj", "qkv_proj_kv_write", "rms_norm_qkv_proj", "rms_norm_qkv_proj_noalloc",
+           "out_proj_residual", "quantize_rows_fp8",
            "qkv_proj_fp8", "e4m3_encode", "quantize_heads_fp8", "prefill_attention", "prefill_attention_fp8qk",
            "prefill_attention_paged",
            "kv_cache_write", "load", "version",
-           "PcaError", "EXPORTED"]
+           "PcaError", "EXPORTED", "NOALLOC_MAX_ROWS"]

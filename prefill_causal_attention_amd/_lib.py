@@ -17,7 +17,10 @@ LIB_PATH = os.path.join(PKG, "libpca.so")
 PCA_OK, PCA_ERR_INVALID_ARG, PCA_ERR_UNSUPPORTED, PCA_ERR_HIP = 0, 1, 2, 3
 DTYPES = {"bf16": 0, "fp8_e4m3": 1}
 
-EXPORTED = ("pca_kv_layout", "pca_qkv_proj", "pca_qkv_proj_kv_write", "pca_rms_norm_qkv_proj", "pca_out_proj_residual",
+NOALLOC_MAX_ROWS = 262144      # PCA_NOALLOC_MAX_ROWS of include/pca.h
+
+EXPORTED = ("pca_kv_layout", "pca_qkv_proj", "pca_qkv_proj_kv_write", "pca_rms_norm_qkv_proj",
+            "pca_rms_norm_qkv_proj_noalloc", "pca_out_proj_residual",
             "pca_quantize_rows_fp8", "pca_qkv_proj_fp8", "pca_e4m3_encode",
             "pca_quantize_heads_fp8", "pca_prefill_attention_fp8qk",
             "pca_prefill_attention",
@@ -68,6 +71,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                                 f32, i32, vp, i64, vp]
     lib.pca_qkv_proj_fp8.argtypes = [vp, i64, vp, vp, i64, vp, vp, i64, i64, i64, i64, vp]
     lib.pca_rms_norm_qkv_proj.argtypes = [vp, i64, vp, i64, f32, vp, vp, i64, i64, i64, i64, vp]
+    lib.pca_rms_norm_qkv_proj_noalloc.argtypes = [vp, i64, vp, i64, f32, vp, i64, i64, i64, i64, vp]
     lib.pca_out_proj_residual.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, i64, i64, i64, vp]
     lib.pca_prefill_attention_window.argtypes = [vp, vp, vp, i64, i64, i64, vp, i32, i32, i64, i32, i32, i32,
                                                  f32, i32, i32, vp, i64, vp]
@@ -75,7 +79,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                                 vp, vp, i64, i32, i32, i32, f32, i32, vp, i64, vp]
     for fn in ("pca_kv_layout", "pca_qkv_proj", "pca_prefill_attention", "pca_kv_cache_write",
                "pca_qkv_proj_kv_write", "pca_prefill_attention_paged", "pca_prefill_attention_window",
-               "pca_out_proj_residual", "pca_rms_norm_qkv_proj", "pca_quantize_rows_fp8", "pca_qkv_proj_fp8",
+               "pca_out_proj_residual", "pca_rms_norm_qkv_proj", "pca_rms_norm_qkv_proj_noalloc",
+               "pca_quantize_rows_fp8", "pca_qkv_proj_fp8",
                "pca_e4m3_encode", "pca_quantize_heads_fp8", "pca_prefill_attention_fp8qk"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.pca_last_error.restype = ctypes.c_char_p
@@ -253,6 +258,22 @@ def rms_norm_qkv_proj(x, w_t_g, y, inv_rms, eps: float = 1e-6, stream=None):
     pr = _flat(inv_rms, "inv_rms", "f32", M)
     _check("pca_rms_norm_qkv_proj", load().pca_rms_norm_qkv_proj(px, ldx, pw, ldw, float(eps), pr,
                                                                  py, ldy, M, N, K, _stream(stream)))
+    return y
+
+
+def rms_norm_qkv_proj_noalloc(x, w_t_g, y, eps: float = 1e-6, stream=None):
+    """rms_norm_qkv_proj with the 1/rms workspace in the library's static
+    device array (no allocation by the call; M <= NOALLOC_MAX_ROWS; calls that
+    overlap in time on one GPU race on that array)."""
+    px, ldx = _rows(x, "x")
+    pw, ldw = _rows(w_t_g, "w_t_g")
+    py, ldy = _rows(y, "y")
+    M, K = x.shape
+    N = w_t_g.shape[0]
+    if w_t_g.shape[1] != K or tuple(y.shape) != (M, N):
+        raise ValueError(f"shape mismatch: x {tuple(x.shape)}, w_t_g {tuple(w_t_g.shape)}, y {tuple(y.shape)}")
+    _check("pca_rms_norm_qkv_proj_noalloc", load().pca_rms_norm_qkv_proj_noalloc(
+        px, ldx, pw, ldw, float(eps), py, ldy, M, N, K, _stream(stream)))
     return y
 
 

@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include "pca.h"
+#include "pca_abi.hpp"
 #include "pca_internal.hpp"
 
 #include <atomic>
@@ -30,10 +31,15 @@ namespace {
 
 thread_local char g_err[512] = "";
 
+pca_status vfail(pca_status st, const char* fmt, va_list ap) {
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    return st;
+}
+
 pca_status fail(pca_status st, const char* fmt, ...) {
     va_list ap;
     va_start(ap, fmt);
-    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    vfail(st, fmt, ap);
     va_end(ap);
     return st;
 }
@@ -134,6 +140,39 @@ pca_status check_kv_cache(const int32_t* cu_seqlens, int num_seqs, int64_t total
 
 }  // namespace
 
+namespace pca {
+
+pca_status abi_error(pca_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vfail(st, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+pca_status rms_norm_qkv_proj_check(const pca_bf16* x, int64_t ldx, const pca_bf16* w_t, int64_t ldw, float eps,
+                                   pca_bf16* y, int64_t ldy, int64_t M, int64_t N, int64_t K) {
+    GemmArgs a;
+    const pca_status st = check_gemm(x, ldx, w_t, ldw, y, ldy, M, N, K, a);
+    if (st != PCA_OK) return st;
+    if (!(eps >= 0.0f) || eps > 1e30f) return fail(PCA_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    return PCA_OK;
+}
+
+pca_status rms_norm_qkv_proj_launch(const pca_bf16* x, int64_t ldx, const pca_bf16* w_t, int64_t ldw, float eps,
+                                    float* inv_rms, pca_bf16* y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                                    void* stream) {
+    GemmArgs a;
+    pca_status st = check_gemm(x, ldx, w_t, ldw, y, ldy, M, N, K, a);
+    if (st != PCA_OK) return st;
+    a.row_scale = inv_rms;
+    st = hip_status(launch_rms_stats(x, ldx, (int)M, (int)K, eps, inv_rms, (hipStream_t)stream), "rms stats launch");
+    if (st != PCA_OK) return st;
+    return hip_status(launch_qkv_gemm(a, (hipStream_t)stream), "rms_norm_qkv_proj launch");
+}
+
+}  // namespace pca
+
 extern "C" {
 
 const char* pca_last_error(void) { return g_err; }
@@ -219,15 +258,10 @@ pca_status pca_qkv_proj_fp8(const uint8_t* xq, int64_t ldxq, const float* sx, co
 pca_status pca_rms_norm_qkv_proj(const pca_bf16* x, int64_t ldx, const pca_bf16* w_t, int64_t ldw, float eps,
                                  float* inv_rms, pca_bf16* y, int64_t ldy, int64_t M, int64_t N, int64_t K,
                                  void* stream) {
-    pca::GemmArgs a;
-    pca_status st = check_gemm(x, ldx, w_t, ldw, y, ldy, M, N, K, a);
+    pca_status st = pca::rms_norm_qkv_proj_check(x, ldx, w_t, ldw, eps, y, ldy, M, N, K);
     if (st != PCA_OK) return st;
     if (!inv_rms || ((uintptr_t)inv_rms & 3u)) return fail(PCA_ERR_INVALID_ARG, "inv_rms must be a 4-byte aligned device buffer");
-    if (!(eps >= 0.0f) || eps > 1e30f) return fail(PCA_ERR_INVALID_ARG, "eps must be finite and >= 0");
-    a.row_scale = inv_rms;
-    st = hip_status(pca::launch_rms_stats(x, ldx, (int)M, (int)K, eps, inv_rms, (hipStream_t)stream), "rms stats launch");
-    if (st != PCA_OK) return st;
-    return hip_status(pca::launch_qkv_gemm(a, (hipStream_t)stream), "rms_norm_qkv_proj launch");
+    return pca::rms_norm_qkv_proj_launch(x, ldx, w_t, ldw, eps, inv_rms, y, ldy, M, N, K, stream);
 }
 
 pca_status pca_out_proj_residual(const pca_bf16* o, int64_t ldo, const pca_bf16* w_t, int64_t ldw,

@@ -100,6 +100,23 @@ def test_rms_norm_qkv_proj_validation():
     _expect("pca_rms_norm_qkv_proj", base, order, bad, {"eps": C})
 
 
+def test_rms_norm_qkv_proj_noalloc_validation():
+    """Same checks as the workspace call (before any HIP call), plus the row
+    limit of the static workspace."""
+    order = ["x", "ldx", "w", "ldw", "eps", "y", "ldy", "M", "N", "K"]
+    base = dict(x=FAKE, ldx=64, w=FAKE, ldw=64, eps=1e-6, y=FAKE, ldy=128, M=16, N=128, K=64)
+    bad = dict(GEMM_BAD)
+    bad.update({("eps", -1.0): 1, ("eps", float("nan")): 1, ("M", pca.NOALLOC_MAX_ROWS + 1): 2})
+    _expect("pca_rms_norm_qkv_proj_noalloc", base, order, bad, {"eps": C})
+
+
+def test_noalloc_row_limit_matches_header():
+    import os
+    import re
+    text = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "pca.h")).read()
+    assert int(re.search(r"#define PCA_NOALLOC_MAX_ROWS (\d+)", text).group(1)) == pca.NOALLOC_MAX_ROWS
+
+
 def test_qkv_proj_fp8_validation():
     order = ["xq", "ldxq", "sx", "wq", "ldwq", "sw", "y", "ldy", "M", "N", "K"]
     base = dict(xq=FAKE, ldxq=64, sx=FAKE, wq=FAKE, ldwq=64, sw=FAKE, y=FAKE, ldy=128, M=16, N=128, K=64)
