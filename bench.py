@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--kv-cold-reps", type=int, default=20)
     ap.add_argument("--extra-reps", type=int, default=20,
                     help="reps of the extra measurements (fused GEMM + KV write, paged chunk attention); 0 skips")
+    ap.add_argument("--clock-seconds", type=float, default=0.3,
+                    help="seconds of back-to-back attention launches while the GPU clocks are sampled; 0 skips")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (to scale HBM byte counters)")
     return ap.parse_args()
@@ -67,6 +69,51 @@ def measured_traffic(workload):
     if t.get("attn_fwd_sha") != source_sha("attn_fwd.hip"):
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+def memory_clock_mhz():
+    """HBM clock as amdsmi reports it (MHz), or None."""
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        try:
+            h = amdsmi.amdsmi_get_processor_handles()[0]
+            return float(amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.MEM)["clk"])
+        finally:
+            amdsmi.amdsmi_shut_down()
+    except Exception:
+        return None
+
+
+def sample_clocks(pca, torch, launch, seconds):
+    """Average shader clock of each XCD while `launch` runs back to back for
+    about `seconds`, from the GPU's own counters (two pca.clock_stamp calls on
+    the same stream around the launches); the median over the XCDs is
+    sclk_mhz."""
+    if seconds <= 0:
+        return {"sclk_mhz": None, "note": "not sampled (--clock-seconds 0)"}
+    dev = torch.device("cuda:0")
+    a = torch.zeros(pca.CLOCK_STAMP_WORDS, dtype=torch.int64, device=dev)
+    b = torch.zeros_like(a)
+    launch()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    launch()
+    e1.record()
+    torch.cuda.synchronize()
+    n = max(1, int(seconds * 1e3 / max(e0.elapsed_time(e1), 1e-3)))
+    pca.clock_stamp(a)
+    for _ in range(n):
+        launch()
+    pca.clock_stamp(b)
+    torch.cuda.synchronize()
+    per_xcd = pca.shader_clock_mhz(a.cpu().numpy(), b.cpu().numpy())
+    vals = sorted(per_xcd.values())
+    return {"sclk_mhz": vals[len(vals) // 2] if vals else None, "sclk_per_xcd_mhz": per_xcd,
+            "mclk_mhz": memory_clock_mhz(),
+            "note": f"shader clock = s_memtime cycles / s_memrealtime (100 MHz) per XCD over {n} back-to-back "
+                    "attention launches after the timed steps (median over XCDs); mclk from amdsmi"}
 
 
 def cpu_baseline(w, target_s):
@@ -169,22 +216,9 @@ def main():
         if ev is not None:
             ev[3].record(stream)
 
-    print(f"[bench] workload={w.name} T={T} warmup={args.warmup} steps={args.steps}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        step()
+
+    step()                       # one pass first, so y holds real K/V for the side measurements
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
-    t_gemm = np.array([e[0].elapsed_time(e[1]) for e in events])
-    t_attn = np.array([e[1].elapsed_time(e[2]) for e in events])
-    t_kv = np.array([e[2].elapsed_time(e[3]) for e in events])
-    print(f"[bench] timed {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
 
     # cold KV write: KV_SETS independent (K/V source, page pool) sets written
     # back to back between two events, so a set's lines were last touched
@@ -217,6 +251,30 @@ def main():
         cold.append(e0.elapsed_time(e1) / KV_SETS)
     del sets
     t_kv_cold = np.array(cold)
+
+    # the same box's plain-copy ceiling for those bytes: KV_SETS (source,
+    # destination) pairs of the K+V byte count, copied back to back, cold in
+    # the same way; bytes moved = read + write
+    kv_payload = 2 * T * nk * 2
+    pairs = [(torch.ones(kv_payload // 8, dtype=torch.int64, device=dev),
+              torch.empty(kv_payload // 8, dtype=torch.int64, device=dev)) for _ in range(KV_SETS)]
+
+    def copy_round():
+        for src, dst in pairs:
+            dst.copy_(src)
+
+    copy_round()
+    torch.cuda.synchronize()
+    cold_copy = []
+    for _ in range(args.kv_cold_reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        copy_round()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cold_copy.append(e0.elapsed_time(e1) / KV_SETS)
+    del pairs
+    t_copy_cold = np.array(cold_copy)
 
     extras = {}
     if args.extra_reps > 0:
@@ -355,6 +413,38 @@ def main():
             "frac_hbm": b5 / (t5 * 1e-3) / 1e9 / PEAK_HBM_GBS}
         del sets5
 
+    # The headline steps run after the side measurements above, so they see the
+    # clock the chip holds under sustained load rather than its ramp from idle.
+    print(f"[bench] workload={w.name} T={T} warmup={args.warmup} steps={args.steps}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    stamp_a = torch.zeros(pca.CLOCK_STAMP_WORDS, dtype=torch.int64, device=dev)
+    stamp_b = torch.zeros_like(stamp_a)
+    pca.clock_stamp(stamp_a)           # outside the wall-clock window and the events
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pca.clock_stamp(stamp_b)
+    ms_step = wall * 1e3 / args.steps
+    t_gemm = np.array([e[0].elapsed_time(e[1]) for e in events])
+    t_attn = np.array([e[1].elapsed_time(e[2]) for e in events])
+    t_kv = np.array([e[2].elapsed_time(e[3]) for e in events])
+    print(f"[bench] timed {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
+
+    clocks = sample_clocks(pca, torch, lambda: pca.prefill_attention(q, k, v, o, w.n_head, w.n_kv_head, w.head_dim,
+                                                                      cu_seqlens=cu, max_seqlen=w.max_seqlen),
+                           args.clock_seconds)
+    steps_clock = pca.shader_clock_mhz(stamp_a.cpu().numpy(), stamp_b.cpu().numpy())
+    if steps_clock:
+        v_ = sorted(steps_clock.values())
+        clocks["sclk_mhz_timed_steps"] = v_[len(v_) // 2]
+
     att_flops = w.attention_flops()
     gemm_flops = w.gemm_flops()
     eb = 1 if fp8 else 2
@@ -378,12 +468,26 @@ def main():
                                cold_mean_ms=float(t_kv_cold.mean()),
                                cold_median_ms=float(np.median(t_kv_cold)),
                                gbs_cold=kv_bytes / (np.median(t_kv_cold) * 1e-3) / 1e9,
-                               frac_hbm_cold=kv_bytes / (np.median(t_kv_cold) * 1e-3) / 1e9 / PEAK_HBM_GBS),
+                               frac_hbm_cold=kv_bytes / (np.median(t_kv_cold) * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                               copy_ceiling_gbs_cold=2 * kv_payload / (np.median(t_copy_cold) * 1e-3) / 1e9,
+                               frac_of_copy_ceiling=(kv_bytes / np.median(t_kv_cold)) /
+                               (2 * kv_payload / np.median(t_copy_cold)),
+                               copy_ceiling_case=f"plain device copy of the same {kv_payload} K+V bytes "
+                                                 f"(torch copy_, {KV_SETS} rotating pairs, cold)"),
     }
     traffic = measured_traffic(w.name)
     roofline = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": tflops / PEAK_BF16_TFLOPS, "traffic": traffic, "kernel": f"attn_fwd_kernel<{w.head_dim}, 0, false>",
-                "flop_per_launch": att_flops, "avg_launch_ms": a_ms}
+                "flop_per_launch": att_flops, "avg_launch_ms": a_ms,
+                "traffic_source": (f"profiles/attn_fwd_{w.name}_traffic.json: rocprofv3 --pmc FETCH_SIZE and "
+                                   "WRITE_SIZE of this kernel source (sha-matched), scaled by a plain 1 GiB copy; "
+                                   "not measured in this run") if traffic is not None else None,
+                "clock": clocks}
+    if clocks.get("sclk_mhz"):
+        # the published peak assumes 2.4 GHz; at the observed shader clock the same units peak lower
+        peak_at_clock = PEAK_BF16_TFLOPS * clocks["sclk_mhz"] / 2400.0
+        roofline["peak_at_observed_sclk"] = peak_at_clock
+        roofline["frac_at_observed_sclk"] = tflops / peak_at_clock
     out = {
         "metric": METRIC,
         "value": tflops,

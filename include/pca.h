@@ -390,6 +390,17 @@ pca_status pca_prefill_attention_fp8qk(const pca_bf16* q, int64_t ldq, const uin
  */
 pca_status pca_e4m3_encode(const float* x, uint8_t* codes, int64_t n, void* stream);
 
+/*
+ * pca_clock_stamp -- measurement utility: enqueues on `stream` a small kernel
+ *   whose 64 one-wave blocks each write, at out[3*b .. 3*b+2], the XCD it ran
+ *   on (hardware XCC id), that XCD's shader-clock cycle counter (s_memtime)
+ *   and the 100 MHz real-time counter (s_memrealtime).  Two stamps around a
+ *   stretch of work give each XCD's average shader clock over it (cycles
+ *   over seconds), the clock the MFMA peak scales with (the published dense
+ *   peaks assume 2.4 GHz).  out: device uint64[192], 8-byte aligned.
+ */
+pca_status pca_clock_stamp(uint64_t* out, void* stream);
+
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char* pca_last_error(void);
 

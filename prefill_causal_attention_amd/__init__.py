@@ -18,7 +18,7 @@ Calls (same names as the C ABI in include/pca.h, minus the ``pca_`` prefix):
 All compute runs in hand-written HIP kernels; PyTorch only provides device
 memory and the current stream.
 """
-from ._lib import (EXPORTED, NOALLOC_MAX_ROWS, PcaError, e4m3_encode, kv_cache_write, kv_layout, load,  # noqa: F401
+from ._lib import (CLOCK_STAMP_WORDS, EXPORTED, NOALLOC_MAX_ROWS, PcaError, clock_stamp, shader_clock_mhz, e4m3_encode, kv_cache_write, kv_layout, load,  # noqa: F401
                    out_proj_residual, prefill_attention, prefill_attention_fp8qk, prefill_attention_paged,
                    qkv_proj, qkv_proj_fp8, qkv_proj_kv_write, quantize_heads_fp8, quantize_rows_fp8,
                    rms_norm_qkv_proj, rms_norm_qkv_proj_noalloc, version)
@@ -28,4 +28,4 @@ __all__ = ["kv_layout", "qkv_proj", "qkv_proj_kv_write", "rms_norm_qkv_proj", "r
            "qkv_proj_fp8", "e4m3_encode", "quantize_heads_fp8", "prefill_attention", "prefill_attention_fp8qk",
            "prefill_attention_paged",
            "kv_cache_write", "load", "version",
-           "PcaError", "EXPORTED", "NOALLOC_MAX_ROWS"]
+           "PcaError", "EXPORTED", "NOALLOC_MAX_ROWS", "clock_stamp", "shader_clock_mhz", "CLOCK_STAMP_WORDS"]

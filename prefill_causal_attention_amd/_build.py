@@ -12,7 +12,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpca.so")
 
-SOURCES = ["pca_api.hip", "noalloc.hip", "kv_write.hip", "qkv_gemm.hip", "gemm_fp8.hip", "attn_fwd.hip"]
+SOURCES = ["pca_api.hip", "noalloc.hip", "clock_stamp.hip", "kv_write.hip", "qkv_gemm.hip", "gemm_fp8.hip",
+           "attn_fwd.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

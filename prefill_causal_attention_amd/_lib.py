@@ -25,7 +25,7 @@ EXPORTED = ("pca_kv_layout", "pca_qkv_proj", "pca_qkv_proj_kv_write", "pca_rms_n
             "pca_quantize_heads_fp8", "pca_prefill_attention_fp8qk",
             "pca_prefill_attention",
             "pca_prefill_attention_window", "pca_prefill_attention_paged", "pca_kv_cache_write",
-            "pca_last_error", "pca_version")
+            "pca_clock_stamp", "pca_last_error", "pca_version")
 
 
 class PcaError(RuntimeError):
@@ -83,6 +83,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                "pca_quantize_rows_fp8", "pca_qkv_proj_fp8",
                "pca_e4m3_encode", "pca_quantize_heads_fp8", "pca_prefill_attention_fp8qk"):
         getattr(lib, fn).restype = ctypes.c_int
+    lib.pca_clock_stamp.argtypes = [vp, vp]
+    lib.pca_clock_stamp.restype = ctypes.c_int
     lib.pca_last_error.restype = ctypes.c_char_p
     lib.pca_last_error.argtypes = []
     lib.pca_version.restype = ctypes.c_char_p
@@ -104,7 +106,7 @@ def _dtype(kind: str):
     calls need no torch)."""
     if not _DT:
         import torch
-        _DT.update(bf16=torch.bfloat16, u8=torch.uint8, f32=torch.float32, i32=torch.int32)
+        _DT.update(bf16=torch.bfloat16, u8=torch.uint8, f32=torch.float32, i32=torch.int32, i64=torch.int64)
     return _DT[kind]
 
 
@@ -178,6 +180,31 @@ def _pool(t, name: str, cache_dtype: str):
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t.data_ptr()
+
+
+CLOCK_STAMP_WORDS = 192        # 64 blocks x (XCC id, shader-clock cycles, 100 MHz real time)
+
+
+def clock_stamp(out, stream=None):
+    """Enqueue a stamp of every XCD's shader-clock and real-time counters into
+    the int64 device tensor out (CLOCK_STAMP_WORDS elements)."""
+    _check("pca_clock_stamp", load().pca_clock_stamp(_flat(out, "out", "i64", CLOCK_STAMP_WORDS), _stream(stream)))
+    return out
+
+
+def shader_clock_mhz(before, after) -> dict:
+    """Average shader clock per XCD between two stamps (host int64 arrays of
+    CLOCK_STAMP_WORDS): cycles elapsed over real time elapsed, per XCD from the
+    medians of its blocks' counters."""
+    import numpy as np
+    a, b = np.asarray(before).reshape(-1, 3), np.asarray(after).reshape(-1, 3)
+    out = {}
+    for x in sorted(set(a[:, 0].tolist()) & set(b[:, 0].tolist())):
+        ca, ra = np.median(a[a[:, 0] == x, 1]), np.median(a[a[:, 0] == x, 2])
+        cb, rb = np.median(b[b[:, 0] == x, 1]), np.median(b[b[:, 0] == x, 2])
+        if rb > ra:
+            out[int(x)] = float((cb - ca) / ((rb - ra) / 100e6) / 1e6)
+    return out
 
 
 def version() -> str:

@@ -16,6 +16,8 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) char lds_char_t;
 
 constexpr int BM = 256, BN = 256;
+// wave shape of the fp8 GEMM (four waves, one per SIMD, 128 x 128 each); the
+// bf16 GEMM runs eight waves of 128 (n) x 64 (m) and keeps its own constants
 constexpr int kThreads = 256;
 constexpr int FN = 4, FM = 4;                 // 32x32 blocks per wave (n, m)
 constexpr int ROWB = 128;                     // bytes per tile row (one K step: 64 bf16 or 128 fp8)
@@ -23,7 +25,7 @@ constexpr int TILE_B = 256 * ROWB;            // 32 KiB: one operand tile
 constexpr int STAGE_B = 2 * TILE_B;           // W tile, then X tile
 constexpr int LDS_BYTES = 2 * STAGE_B;        // 128 KiB
 constexpr int DMA_PER_TILE = TILE_B / 1024;   // 32 one-KiB DMA blocks per operand tile
-constexpr int DMA_PER_WAVE = DMA_PER_TILE / 4;  // 8 per operand per wave
+constexpr int DMA_PER_WAVE = DMA_PER_TILE / 4;  // 8 per operand per wave (four waves)
 constexpr int kGroupM = 8;
 constexpr uint32_t kOob = 0x80000000u;        // an offset past every buffer: loads return 0
 

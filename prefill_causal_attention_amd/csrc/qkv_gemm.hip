@@ -7,13 +7,15 @@
 // along K (§5.1).
 //
 // gfx950 design.
-//  * Workgroup tile 256 x 256 (M x N), K step 64, four waves (one per SIMD),
-//    each a 128 x 128 sub-tile of 4 x 4 v_mfma_f32_32x32x16_bf16 blocks; the
-//    256 fp32 accumulators per lane live in AGPRs (one wave per SIMD gives
-//    each wave the whole 512-entry register file).  The wave computes the
-//    transposed product (MFMA rows = n, columns = m), so each lane's
-//    accumulator holds 4 consecutive n of one m: the epilogue writes 8-byte
-//    runs of a y row.
+//  * Workgroup tile 256 x 256 (M x N), K step 64, eight waves, two per SIMD
+//    (waves w and w + 4 share one), each a 64 (m) x 128 (n) sub-tile of
+//    2 x 4 v_mfma_f32_32x32x16_bf16 blocks with its 128 fp32 accumulators per
+//    lane in registers.  While one wave of a SIMD waits on its LDS operand
+//    reads, the workgroup barrier or its DMA, the other issues MFMAs (one wave
+//    per SIMD with a 128 x 128 sub-tile each measured 4-10% slower on every
+//    projection shape, although it reads a third fewer LDS bytes per MFMA).
+//    The wave computes the transposed product (MFMA rows = n, columns = m), so
+//    each lane's accumulator holds 4 consecutive n of one m.
 //  * Operand tiles go from HBM/L2 straight into LDS with buffer_load ... lds
 //    (no register staging, no LDS stores), double-buffered: the tiles of K
 //    step kt + 2 are requested as soon as step kt's tiles are no longer read,
@@ -21,9 +23,11 @@
 //    elements (8 chunks of 16 bytes) are stored with chunk c of row r at
 //    c ^ ((r >> 1) & 7): the 16 rows a 16-lane group of a ds_read_b128 touches
 //    then cover all 64 banks once.
-//  * The 64 MFMAs of a K step run as one fixed sequence; the 8 operand reads
-//    of each 16-key step are issued one step ahead as inline asm and retired
-//    by explicit lgkmcnt waits, and scheduling barriers keep the order.
+//  * The 32 MFMAs of a wave's K step run as one fixed sequence; the 6 operand
+//    reads of each 16-key step are issued one step ahead as inline asm and
+//    retired by explicit lgkmcnt waits, and scheduling barriers keep the
+//    order.  (Deeper DMA pipelines -- 4 or 5 stages of 32-wide K steps -- and
+//    operand reads two steps ahead measured slower or equal.)
 //  * Ragged M, N read zeros through the buffer-resource range check, a ragged
 //    K tail through an out-of-range offset.
 //  * Tile order: consecutive workgroup ids go round-robin to the 8 XCDs, so
@@ -42,20 +46,31 @@ namespace {
 using namespace gemm;
 
 constexpr int BKK = 64;                       // bf16 elements per K step (ROWB bytes)
+constexpr int kWavesG = 8;                    // two waves per SIMD
+constexpr int kThreadsG = kWavesG * 64;
+constexpr int FNg = 4, FMg = 2;               // 32 x 32 blocks per wave: 128 n x 64 m
+constexpr int DMA_PER_WAVE_G = DMA_PER_TILE / kWavesG;   // 1 KiB DMA blocks per operand per wave
+
+template <int N>
+__device__ __forceinline__ void lds_wait6(u32x4_t (&f)[6]) {
+    asm volatile("s_waitcnt lgkmcnt(%6)"
+                 : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(f[4]), "+v"(f[5])
+                 : "n"(N));
+}
 
 // KV = 0: plain GEMM; 1 / 2: the epilogue also writes y's K and V columns
 // into the bf16 / fp8 page pools.  RES: y = x w^T + res, the residual added
 // to the fp32 accumulators before the single bf16 rounding.  RS: the fp32
 // accumulators of row m are scaled by row_scale[m] before that rounding.
 template <int KV, bool RES, bool RS>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreadsG) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void qkv_gemm_kernel(GemmArgs a) {
     extern __shared__ __align__(16) uint16_t smem[];
     lds_char_t* lds = (lds_char_t*)smem;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave & 1, wn = wave >> 1;     // wave position in the 2 x 2 grid
+    const int wm = wave >> 1, wn = wave & 1;     // wave position: 4 (m) x 2 (n)
     const int r32 = lane & 31, half = lane >> 5;
 
     const int tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
@@ -68,11 +83,11 @@ void qkv_gemm_kernel(GemmArgs a) {
     // DMA lane offsets (bytes from the tile's first row at the current K step):
     // block b of a wave covers rows 8b .. 8b + 7; lane l writes physical chunk
     // l % 8 of row 8b + l / 8, i.e. fetches logical chunk (l % 8) ^ swz(row).
-    uint32_t offx[DMA_PER_WAVE], offw[DMA_PER_WAVE];
-    int lchunk[DMA_PER_WAVE];
+    uint32_t offx[DMA_PER_WAVE_G], offw[DMA_PER_WAVE_G];
+    int lchunk[DMA_PER_WAVE_G];
 #pragma unroll
-    for (int i = 0; i < DMA_PER_WAVE; ++i) {
-        const int row = (wave * DMA_PER_WAVE + i) * 8 + lane / 8;
+    for (int i = 0; i < DMA_PER_WAVE_G; ++i) {
+        const int row = (wave * DMA_PER_WAVE_G + i) * 8 + lane / 8;
         lchunk[i] = (lane % 8) ^ swz(row);
         offx[i] = (uint32_t)(((int64_t)row * a.ldx + lchunk[i] * 8) * 2);
         offw[i] = (uint32_t)(((int64_t)row * a.ldw + lchunk[i] * 8) * 2);
@@ -86,8 +101,8 @@ void qkv_gemm_kernel(GemmArgs a) {
             uniform_rsrc(a.x + (int64_t)m0 * a.ldx + k0, (int64_t)rows_x * a.ldx * 2 - (int64_t)k0 * 2);
         lds_char_t* dst = lds + stage * STAGE_B;
 #pragma unroll
-        for (int i = 0; i < DMA_PER_WAVE; ++i) {
-            const int blk = wave * DMA_PER_WAVE + i;
+        for (int i = 0; i < DMA_PER_WAVE_G; ++i) {
+            const int blk = wave * DMA_PER_WAVE_G + i;
             const bool oob = tail && (k0 + lchunk[i] * 8 >= a.K);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void_t*)(dst + blk * 1024), 16,
                                                      oob ? kOob : offw[i], 0, 0, 0);
@@ -104,35 +119,35 @@ void qkv_gemm_kernel(GemmArgs a) {
     for (int ks = 0; ks < 4; ++ks) {
         const uint32_t base = (uint32_t)(uintptr_t)lds + r32 * ROWB + (((ks * 2 + half) ^ swz(r32)) * 16);
         waddr[ks] = base + wn * 128 * ROWB;
-        xaddr[ks] = base + wm * 128 * ROWB;
+        xaddr[ks] = base + wm * 64 * ROWB;
     }
 
-    f32x16_t acc[FN][FM];
+    f32x16_t acc[FNg][FMg];
 #pragma unroll
-    for (int i = 0; i < FN; ++i)
+    for (int i = 0; i < FNg; ++i)
 #pragma unroll
-        for (int j = 0; j < FM; ++j)
+        for (int j = 0; j < FMg; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    // 8 operand fragments of 16-key step ks: W blocks i (rows wn*128 + i*32),
-    // X blocks j (rows wm*128 + j*32)
-    auto read_step = [&](uint32_t soff, auto KSc, u32x4_t (&f)[8]) __attribute__((always_inline)) {
+    // 6 operand fragments of 16-key step ks: W blocks i (rows wn*128 + i*32),
+    // X blocks j (rows wm*64 + j*32)
+    auto read_step = [&](uint32_t soff, auto KSc, u32x4_t (&f)[6]) __attribute__((always_inline)) {
         constexpr int ks = decltype(KSc)::value;
         const uint32_t wa = waddr[ks] + soff, xa = xaddr[ks] + soff;
-        static_for<FN>([&](auto Ic) {
+        static_for<FNg>([&](auto Ic) {
             constexpr int i = decltype(Ic)::value;
             f[i] = lds_read_b128<i * 32 * ROWB>(wa);
         });
-        static_for<FM>([&](auto Jc) {
+        static_for<FMg>([&](auto Jc) {
             constexpr int j = decltype(Jc)::value;
-            f[FN + j] = lds_read_b128<TILE_B + j * 32 * ROWB>(xa);
+            f[FNg + j] = lds_read_b128<TILE_B + j * 32 * ROWB>(xa);
         });
     };
-    auto mfmas = [&](const u32x4_t (&f)[8]) __attribute__((always_inline)) {
-        static_for<FN * FM>([&](auto Ic) {
-            constexpr int i = decltype(Ic)::value / FM, j = decltype(Ic)::value % FM;
-            acc[i][j] = mfma32x32x16(as_bf16x8(f[i]), as_bf16x8(f[FN + j]), acc[i][j]);
+    auto mfmas = [&](const u32x4_t (&f)[6]) __attribute__((always_inline)) {
+        static_for<FNg * FMg>([&](auto Ic) {
+            constexpr int i = decltype(Ic)::value / FMg, j = decltype(Ic)::value % FMg;
+            acc[i][j] = mfma32x32x16(as_bf16x8(f[i]), as_bf16x8(f[FNg + j]), acc[i][j]);
         });
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -140,16 +155,16 @@ void qkv_gemm_kernel(GemmArgs a) {
     // Software pipeline over K steps with two LDS stages and one barrier per
     // step.  The operands of 16-key step ks + 1 are read while ks runs on the
     // matrix cores.  The barrier of step kt sits after the wave's last LDS read
-    // of stage kt & 1 and before that step's last 16 MFMAs: past it, step
+    // of stage kt & 1 and before that step's last 8 MFMAs: past it, step
     // kt + 1's tiles are visible (every wave waited for its own loads first)
     // and stage kt & 1 is free, so the first operands of step kt + 1 are read
-    // and step kt + 2's tiles requested while those 16 MFMAs run.
+    // and step kt + 2's tiles requested while those 8 MFMAs run.
     issue(0, 0);
     if (1 < nk) issue(1, 1);
-    if (1 < nk) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DMA_PER_WAVE));   // step 0 only
+    if (1 < nk) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DMA_PER_WAVE_G));   // step 0 only
     else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     wg_barrier();
-    u32x4_t f[2][8];
+    u32x4_t f[2][6];
     read_step(0u, std::integral_constant<int, 0>{}, f[0]);
     for (int kt = 0; kt < nk; ++kt) {
         const int st = kt & 1;
@@ -157,10 +172,10 @@ void qkv_gemm_kernel(GemmArgs a) {
         static_for<3>([&](auto KSc) {
             constexpr int ks = decltype(KSc)::value;
             read_step(soff, std::integral_constant<int, ks + 1>{}, f[(ks + 1) & 1]);
-            lds_wait8<8>(f[ks & 1]);
+            lds_wait6<6>(f[ks & 1]);
             mfmas(f[ks & 1]);
         });
-        lds_wait8<0>(f[1]);
+        lds_wait6<0>(f[1]);
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // this wave's loads of step kt + 1
         wg_barrier();
         if (kt + 1 < nk) read_step(soff ^ (uint32_t)STAGE_B, std::integral_constant<int, 0>{}, f[0]);
@@ -170,21 +185,21 @@ void qkv_gemm_kernel(GemmArgs a) {
 
     // Epilogue.  The accumulators hold, per block (i, j), column m = r32 and
     // rows n = g*8 + half*4 + 0..3 -- 8-byte runs spread over 32 rows of y per
-    // store instruction.  Each wave instead stages its 128 x 128 bf16 tile in
+    // store instruction.  Each wave instead stages its 64 x 128 bf16 tile in
     // LDS (token-major, 16-byte chunks XOR-swizzled by row so neither the
     // 32-row writes nor the row reads collide on banks) and writes it back as
     // full rows: 16 lanes x 16 bytes = one 256-byte run of a y row per lane
     // group, four rows per store instruction.
     wg_barrier();                                        // every wave is done with the operand stages
-    lds_char_t* stg = lds + wave * (128 * 256);          // this wave's 32 KiB
+    lds_char_t* stg = lds + wave * (64 * 256);           // this wave's 16 KiB
     const int c = lane & 15;                             // the lane's 16-byte chunk of a row: columns c*8 .. c*8+7
     const int n = n0 + wn * 128 + c * 8;
-    const int m_lo = m0 + wm * 128;
+    const int m_lo = m0 + wm * 64;
     if constexpr (RES) {
         // the residual sub-tile goes into the staging area first, row by row
         // (coalesced 16-byte loads), and is added to the accumulators below
 #pragma unroll 8
-        for (int r = 0; r < 32; ++r) {
+        for (int r = 0; r < 16; ++r) {
             const int ml = r * 4 + (lane >> 4);
             const int m = m_lo + ml;
             u32x4_t rv = {0u, 0u, 0u, 0u};
@@ -204,14 +219,14 @@ void qkv_gemm_kernel(GemmArgs a) {
     // RMSNorm folded in: the row scale multiplies the fp32 accumulators (the
     // norm's gain is folded into the weight's K axis at load time)
 #pragma unroll
-    for (int j = 0; j < FM; ++j) {
+    for (int j = 0; j < FMg; ++j) {
         [[maybe_unused]] float rsc = 1.0f;
         if constexpr (RS) {
             const int m = m_lo + j * 32 + r32;
             if (m < a.M) rsc = a.row_scale[m];
         }
 #pragma unroll
-        for (int i = 0; i < FN; ++i)
+        for (int i = 0; i < FNg; ++i)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int ml = j * 32 + r32, ci = i * 4 + g;
@@ -238,7 +253,7 @@ void qkv_gemm_kernel(GemmArgs a) {
     // of y.
     [[maybe_unused]] const KvWriteArgs& kv = a.kv;
     [[maybe_unused]] int kv_sel = -1, kvh = 0, dcol = 0;   // 0: K, 1: V; kv head and first d of the chunk
-    [[maybe_unused]] int slot_lo = -1, slot_hi = -1;       // page slots of tokens m_lo + lane, m_lo + 64 + lane
+    [[maybe_unused]] int slot_lo = -1;                     // page slot of token m_lo + lane
     if constexpr (KV != 0) {
         const int hd = kv.head_dim, nkc = kv.n_kv_head * hd;
         int col = -1;
@@ -249,19 +264,19 @@ void qkv_gemm_kernel(GemmArgs a) {
         const int nw0 = n0 + wn * 128, nw1 = min(nw0 + 128, a.N);
         if ((nw0 < a.k_col0 + nkc && nw1 > a.k_col0) || (nw0 < a.v_col0 + nkc && nw1 > a.v_col0)) {
             if (m_lo + lane < a.M) slot_lo = (int)token_slot(kv, m_lo + lane);
-            if (m_lo + 64 + lane < a.M) slot_hi = (int)token_slot(kv, m_lo + 64 + lane);
+
         }
     }
 
 #pragma unroll 4
-    for (int r = 0; r < 32; ++r) {
+    for (int r = 0; r < 16; ++r) {
         const int ml = r * 4 + (lane >> 4);
         const u32x4_t v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(
             stg + ml * 256 + ((c ^ (ml & 15)) * 16));
         const int m = m_lo + ml;
         [[maybe_unused]] int slot = -1;
-        if constexpr (KV != 0)   // the slot of row ml sits in lane ml % 64 of slot_lo / slot_hi
-            slot = __builtin_amdgcn_ds_bpermute((ml & 63) * 4, r < 16 ? slot_lo : slot_hi);
+        if constexpr (KV != 0)   // the slot of row ml sits in lane ml of slot_lo
+            slot = __builtin_amdgcn_ds_bpermute((ml & 63) * 4, slot_lo);
         if (m >= a.M) continue;
         uint16_t* dst = a.y + (int64_t)m * a.ldy + n;
         if (n + 7 < a.N) {
@@ -344,7 +359,7 @@ hipError_t launch_kv(const GemmArgs& a, hipStream_t s) {
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
     if (attr != hipSuccess) return attr;
     const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-    hipLaunchKernelGGL((qkv_gemm_kernel<KV, RES, RS>), dim3(tiles), dim3(kThreads), LDS_BYTES, s, a);
+    hipLaunchKernelGGL((qkv_gemm_kernel<KV, RES, RS>), dim3(tiles), dim3(kThreadsG), LDS_BYTES, s, a);
     return hipGetLastError();
 }
 

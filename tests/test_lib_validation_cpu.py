@@ -117,6 +117,12 @@ def test_noalloc_row_limit_matches_header():
     assert int(re.search(r"#define PCA_NOALLOC_MAX_ROWS (\d+)", text).group(1)) == pca.NOALLOC_MAX_ROWS
 
 
+def test_clock_stamp_validation():
+    for ptr in (0, FAKE + 4):
+        st, msg = _status("pca_clock_stamp", ptr, None)
+        assert st == 1 and msg, ptr
+
+
 def test_qkv_proj_fp8_validation():
     order = ["xq", "ldxq", "sx", "wq", "ldwq", "sw", "y", "ldy", "M", "N", "K"]
     base = dict(xq=FAKE, ldxq=64, sx=FAKE, wq=FAKE, ldwq=64, sw=FAKE, y=FAKE, ldy=128, M=16, N=128, K=64)
