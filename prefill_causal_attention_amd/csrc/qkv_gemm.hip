@@ -15,7 +15,8 @@
 //    per SIMD with a 128 x 128 sub-tile each measured 4-10% slower on every
 //    projection shape, although it reads a third fewer LDS bytes per MFMA).
 //    The wave computes the transposed product (MFMA rows = n, columns = m), so
-//    each lane's accumulator holds 4 consecutive n of one m.
+//    each lane's accumulator holds 4 consecutive n of one m.  Grids too small
+//    to fill the CUs use 128 x 256 tiles instead (waves of 32 x 128).
 //  * Operand tiles go from HBM/L2 straight into LDS with buffer_load ... lds
 //    (no register staging, no LDS stores), double-buffered: the tiles of K
 //    step kt + 2 are requested as soon as step kt's tiles are no longer read,
@@ -48,23 +49,35 @@ using namespace gemm;
 constexpr int BKK = 64;                       // bf16 elements per K step (ROWB bytes)
 constexpr int kWavesG = 8;                    // two waves per SIMD
 constexpr int kThreadsG = kWavesG * 64;
-constexpr int FNg = 4, FMg = 2;               // 32 x 32 blocks per wave: 128 n x 64 m
-constexpr int DMA_PER_WAVE_G = DMA_PER_TILE / kWavesG;   // 1 KiB DMA blocks per operand per wave
+constexpr int FNg = 4;                        // 32 x 32 blocks per wave along n: 128 columns
+constexpr int DMA_W_PER_WAVE = DMA_PER_TILE / kWavesG;   // 1 KiB DMA blocks of the W tile per wave
 
+// Wait until at most N LDS reads are outstanding; the fragments pass through
+// the asm so their consumers stay after the wait (6 or 5 fragments per step).
 template <int N>
-__device__ __forceinline__ void lds_wait6(u32x4_t (&f)[6]) {
+__device__ __forceinline__ void lds_wait_f(u32x4_t (&f)[6]) {
     asm volatile("s_waitcnt lgkmcnt(%6)"
                  : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(f[4]), "+v"(f[5])
                  : "n"(N));
+}
+template <int N>
+__device__ __forceinline__ void lds_wait_f(u32x4_t (&f)[5]) {
+    asm volatile("s_waitcnt lgkmcnt(%5)" : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(f[4]) : "n"(N));
 }
 
 // KV = 0: plain GEMM; 1 / 2: the epilogue also writes y's K and V columns
 // into the bf16 / fp8 page pools.  RES: y = x w^T + res, the residual added
 // to the fp32 accumulators before the single bf16 rounding.  RS: the fp32
 // accumulators of row m are scaled by row_scale[m] before that rounding.
-template <int KV, bool RES, bool RS>
+// BMT: rows of x per tile, 256 (waves of 64 x 128) or 128 (waves of 32 x 128,
+// for grids whose 256-row tiles would leave the last round of CUs half idle).
+template <int KV, bool RES, bool RS, int BMT>
 __global__ __launch_bounds__(kThreadsG) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void qkv_gemm_kernel(GemmArgs a) {
+    constexpr int FMg = BMT / 128;                    // 32 x 32 blocks per wave along m
+    constexpr int WMR = 32 * FMg;                     // x rows per wave
+    constexpr int NF = FNg + FMg;                     // operand fragments per 16-key step
+    constexpr int DMA_X_PER_WAVE = BMT * ROWB / 1024 / kWavesG;   // 1 KiB DMA blocks of the x tile per wave
     extern __shared__ __align__(16) uint16_t smem[];
     lds_char_t* lds = (lds_char_t*)smem;
     const int tid = threadIdx.x;
@@ -73,24 +86,32 @@ void qkv_gemm_kernel(GemmArgs a) {
     const int wm = wave >> 1, wn = wave & 1;     // wave position: 4 (m) x 2 (n)
     const int r32 = lane & 31, half = lane >> 5;
 
-    const int tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
+    const int tiles_m = (a.M + BMT - 1) / BMT, tiles_n = (a.N + BN - 1) / BN;
     int tm, tn;
     tile_coords(tiles_m, tiles_n, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-    const int rows_x = min(BM, a.M - m0), rows_w = min(BN, a.N - n0);
+    const int m0 = tm * BMT, n0 = tn * BN;
+    const int rows_x = min(BMT, a.M - m0), rows_w = min(BN, a.N - n0);
     const int nk = (a.K + BKK - 1) / BKK;
 
     // DMA lane offsets (bytes from the tile's first row at the current K step):
     // block b of a wave covers rows 8b .. 8b + 7; lane l writes physical chunk
     // l % 8 of row 8b + l / 8, i.e. fetches logical chunk (l % 8) ^ swz(row).
-    uint32_t offx[DMA_PER_WAVE_G], offw[DMA_PER_WAVE_G];
-    int lchunk[DMA_PER_WAVE_G];
+    // (sized for the 256-row tile: a lambda capturing an array whose size
+    // depends on BMT leaves the host side without the kernel's stub)
+    uint32_t offx[DMA_W_PER_WAVE], offw[DMA_W_PER_WAVE];
+    int lchx[DMA_W_PER_WAVE], lchw[DMA_W_PER_WAVE];
+    static_assert(DMA_X_PER_WAVE <= DMA_W_PER_WAVE, "x tile has at most 256 rows");
 #pragma unroll
-    for (int i = 0; i < DMA_PER_WAVE_G; ++i) {
-        const int row = (wave * DMA_PER_WAVE_G + i) * 8 + lane / 8;
-        lchunk[i] = (lane % 8) ^ swz(row);
-        offx[i] = (uint32_t)(((int64_t)row * a.ldx + lchunk[i] * 8) * 2);
-        offw[i] = (uint32_t)(((int64_t)row * a.ldw + lchunk[i] * 8) * 2);
+    for (int i = 0; i < DMA_W_PER_WAVE; ++i) {
+        const int row = (wave * DMA_W_PER_WAVE + i) * 8 + lane / 8;
+        lchw[i] = (lane % 8) ^ swz(row);
+        offw[i] = (uint32_t)(((int64_t)row * a.ldw + lchw[i] * 8) * 2);
+    }
+#pragma unroll
+    for (int i = 0; i < DMA_X_PER_WAVE; ++i) {
+        const int row = (wave * DMA_X_PER_WAVE + i) * 8 + lane / 8;
+        lchx[i] = (lane % 8) ^ swz(row);
+        offx[i] = (uint32_t)(((int64_t)row * a.ldx + lchx[i] * 8) * 2);
     }
     auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
         const int k0 = kt * BKK;
@@ -101,11 +122,16 @@ void qkv_gemm_kernel(GemmArgs a) {
             uniform_rsrc(a.x + (int64_t)m0 * a.ldx + k0, (int64_t)rows_x * a.ldx * 2 - (int64_t)k0 * 2);
         lds_char_t* dst = lds + stage * STAGE_B;
 #pragma unroll
-        for (int i = 0; i < DMA_PER_WAVE_G; ++i) {
-            const int blk = wave * DMA_PER_WAVE_G + i;
-            const bool oob = tail && (k0 + lchunk[i] * 8 >= a.K);
+        for (int i = 0; i < DMA_W_PER_WAVE; ++i) {
+            const int blk = wave * DMA_W_PER_WAVE + i;
+            const bool oob = tail && (k0 + lchw[i] * 8 >= a.K);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void_t*)(dst + blk * 1024), 16,
                                                      oob ? kOob : offw[i], 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < DMA_X_PER_WAVE; ++i) {
+            const int blk = wave * DMA_X_PER_WAVE + i;
+            const bool oob = tail && (k0 + lchx[i] * 8 >= a.K);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(dst + TILE_B + blk * 1024), 16,
                                                      oob ? kOob : offx[i], 0, 0, 0);
         }
@@ -119,7 +145,7 @@ void qkv_gemm_kernel(GemmArgs a) {
     for (int ks = 0; ks < 4; ++ks) {
         const uint32_t base = (uint32_t)(uintptr_t)lds + r32 * ROWB + (((ks * 2 + half) ^ swz(r32)) * 16);
         waddr[ks] = base + wn * 128 * ROWB;
-        xaddr[ks] = base + wm * 64 * ROWB;
+        xaddr[ks] = base + wm * WMR * ROWB;
     }
 
     f32x16_t acc[FNg][FMg];
@@ -130,9 +156,9 @@ void qkv_gemm_kernel(GemmArgs a) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    // 6 operand fragments of 16-key step ks: W blocks i (rows wn*128 + i*32),
-    // X blocks j (rows wm*64 + j*32)
-    auto read_step = [&](uint32_t soff, auto KSc, u32x4_t (&f)[6]) __attribute__((always_inline)) {
+    // NF operand fragments of 16-key step ks: W blocks i (rows wn*128 + i*32),
+    // X blocks j (rows wm*WMR + j*32)
+    auto read_step = [&](uint32_t soff, auto KSc, u32x4_t (&f)[NF]) __attribute__((always_inline)) {
         constexpr int ks = decltype(KSc)::value;
         const uint32_t wa = waddr[ks] + soff, xa = xaddr[ks] + soff;
         static_for<FNg>([&](auto Ic) {
@@ -144,7 +170,7 @@ void qkv_gemm_kernel(GemmArgs a) {
             f[FNg + j] = lds_read_b128<TILE_B + j * 32 * ROWB>(xa);
         });
     };
-    auto mfmas = [&](const u32x4_t (&f)[6]) __attribute__((always_inline)) {
+    auto mfmas = [&](const u32x4_t (&f)[NF]) __attribute__((always_inline)) {
         static_for<FNg * FMg>([&](auto Ic) {
             constexpr int i = decltype(Ic)::value / FMg, j = decltype(Ic)::value % FMg;
             acc[i][j] = mfma32x32x16(as_bf16x8(f[i]), as_bf16x8(f[FNg + j]), acc[i][j]);
@@ -161,10 +187,10 @@ void qkv_gemm_kernel(GemmArgs a) {
     // and step kt + 2's tiles requested while those 8 MFMAs run.
     issue(0, 0);
     if (1 < nk) issue(1, 1);
-    if (1 < nk) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DMA_PER_WAVE_G));   // step 0 only
+    if (1 < nk) __builtin_amdgcn_s_waitcnt(vmcnt_imm(DMA_W_PER_WAVE + DMA_X_PER_WAVE));   // step 0 only
     else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     wg_barrier();
-    u32x4_t f[2][6];
+    u32x4_t f[2][NF];
     read_step(0u, std::integral_constant<int, 0>{}, f[0]);
     for (int kt = 0; kt < nk; ++kt) {
         const int st = kt & 1;
@@ -172,10 +198,10 @@ void qkv_gemm_kernel(GemmArgs a) {
         static_for<3>([&](auto KSc) {
             constexpr int ks = decltype(KSc)::value;
             read_step(soff, std::integral_constant<int, ks + 1>{}, f[(ks + 1) & 1]);
-            lds_wait6<6>(f[ks & 1]);
+            lds_wait_f<NF>(f[ks & 1]);
             mfmas(f[ks & 1]);
         });
-        lds_wait6<0>(f[1]);
+        lds_wait_f<0>(f[1]);
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // this wave's loads of step kt + 1
         wg_barrier();
         if (kt + 1 < nk) read_step(soff ^ (uint32_t)STAGE_B, std::integral_constant<int, 0>{}, f[0]);
@@ -185,21 +211,21 @@ void qkv_gemm_kernel(GemmArgs a) {
 
     // Epilogue.  The accumulators hold, per block (i, j), column m = r32 and
     // rows n = g*8 + half*4 + 0..3 -- 8-byte runs spread over 32 rows of y per
-    // store instruction.  Each wave instead stages its 64 x 128 bf16 tile in
+    // store instruction.  Each wave instead stages its WMR x 128 bf16 tile in
     // LDS (token-major, 16-byte chunks XOR-swizzled by row so neither the
     // 32-row writes nor the row reads collide on banks) and writes it back as
     // full rows: 16 lanes x 16 bytes = one 256-byte run of a y row per lane
     // group, four rows per store instruction.
     wg_barrier();                                        // every wave is done with the operand stages
-    lds_char_t* stg = lds + wave * (64 * 256);           // this wave's 16 KiB
+    lds_char_t* stg = lds + wave * (WMR * 256);          // this wave's staging rows
     const int c = lane & 15;                             // the lane's 16-byte chunk of a row: columns c*8 .. c*8+7
     const int n = n0 + wn * 128 + c * 8;
-    const int m_lo = m0 + wm * 64;
+    const int m_lo = m0 + wm * WMR;
     if constexpr (RES) {
         // the residual sub-tile goes into the staging area first, row by row
         // (coalesced 16-byte loads), and is added to the accumulators below
 #pragma unroll 8
-        for (int r = 0; r < 16; ++r) {
+        for (int r = 0; r < WMR / 4; ++r) {
             const int ml = r * 4 + (lane >> 4);
             const int m = m_lo + ml;
             u32x4_t rv = {0u, 0u, 0u, 0u};
@@ -263,13 +289,13 @@ void qkv_gemm_kernel(GemmArgs a) {
         // only waves whose columns touch K or V look up page slots
         const int nw0 = n0 + wn * 128, nw1 = min(nw0 + 128, a.N);
         if ((nw0 < a.k_col0 + nkc && nw1 > a.k_col0) || (nw0 < a.v_col0 + nkc && nw1 > a.v_col0)) {
-            if (m_lo + lane < a.M) slot_lo = (int)token_slot(kv, m_lo + lane);
+            if (lane < WMR && m_lo + lane < a.M) slot_lo = (int)token_slot(kv, m_lo + lane);
 
         }
     }
 
 #pragma unroll 4
-    for (int r = 0; r < 16; ++r) {
+    for (int r = 0; r < WMR / 4; ++r) {
         const int ml = r * 4 + (lane >> 4);
         const u32x4_t v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(
             stg + ml * 256 + ((c ^ (ml & 15)) * 16));
@@ -353,14 +379,36 @@ __global__ __launch_bounds__(256) void rms_stats_kernel(const uint16_t* x, int64
     if (lane == 0) inv_rms[m] = 1.0f / __builtin_sqrtf(acc / (float)K + eps);
 }
 
-template <int KV, bool RES, bool RS>
-hipError_t launch_kv(const GemmArgs& a, hipStream_t s) {
-    static const hipError_t attr = hipFuncSetAttribute((const void*)qkv_gemm_kernel<KV, RES, RS>,
+template <int KV, bool RES, bool RS, int BMT>
+hipError_t launch_tiles(const GemmArgs& a, hipStream_t s) {
+    static const hipError_t attr = hipFuncSetAttribute((const void*)qkv_gemm_kernel<KV, RES, RS, BMT>,
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
     if (attr != hipSuccess) return attr;
-    const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-    hipLaunchKernelGGL((qkv_gemm_kernel<KV, RES, RS>), dim3(tiles), dim3(kThreadsG), LDS_BYTES, s, a);
+    const int tiles = ((a.M + BMT - 1) / BMT) * ((a.N + BN - 1) / BN);
+    hipLaunchKernelGGL((qkv_gemm_kernel<KV, RES, RS, BMT>), dim3(tiles), dim3(kThreadsG), LDS_BYTES, s, a);
     return hipGetLastError();
+}
+
+// 128-row tiles are used only when the whole 128-row grid fits in one round
+// of the CUs (data-flow article §5.2's "wave" effect): 1024 x 6144 x 4096 has
+// 96 tiles of 256 rows, which leave 160 CUs idle, and runs 1.45x faster as 192
+// tiles of 128 rows.  A 128-row tile costs about 0.6 of a 256-row one (per-tile
+// start-up and epilogue, and half the operand reuse), and a partly filled last
+// round of 256-row tiles runs faster than a full one, so on every grid that
+// already takes more than one round 256-row tiles measured as fast or faster
+// (2048 x 12288 x 4096: 1070 against 1008 TFLOP/s; 8192 x 6144 x 4096: 1250
+// against 1044).
+bool half_tiles(const GemmArgs& a) {
+    const int ncu = device_cus();
+    if (ncu <= 0) return false;
+    const int64_t tn = (a.N + BN - 1) / BN;
+    const int64_t t256 = (a.M + 255) / 256 * tn, t128 = (a.M + 127) / 128 * tn;
+    return t256 < t128 && t128 <= ncu;
+}
+
+template <int KV, bool RES, bool RS>
+hipError_t launch_kv(const GemmArgs& a, hipStream_t s) {
+    return half_tiles(a) ? launch_tiles<KV, RES, RS, 128>(a, s) : launch_tiles<KV, RES, RS, 256>(a, s);
 }
 
 }  // namespace

@@ -78,3 +78,21 @@ def test_full_size_sampled(idx):
     rows = sample_rows(w.total_tokens, 64, 200 + idx, must=(0, 255, 256, w.total_tokens - 1))
     want = P.projection_rows(bits(x), bits(wq), rows)
     assert_close(y[rows].float().cpu().numpy(), want, f"{w.name} projection rows")
+
+
+def test_row_tile_heights_agree_bitwise():
+    """A grid that 256-row tiles would leave mostly idle (1000 x 6144: 96 tiles)
+    runs on 128-row tiles; each output still sums its K terms in the same order,
+    so the rows equal bitwise those of a tall call (8192 rows, 256-row tiles)."""
+    require_gpu()
+    M, N, K = 8192, 6144, 1032
+    x = workloads.normal_bf16(56, (M, K))
+    wq = workloads.normal_bf16(57, (K, N), std=float(1 / np.sqrt(K)))
+    say(f"qkv_proj tile heights M={M} and 1000, N={N} K={K}")
+    tall = _gpu_proj(x, wq)
+    short = _gpu_proj(x[:1000], wq, y_pad=8)
+    assert torch.equal(short[:, :N], tall[:1000]), "row tile heights disagree"
+    assert torch.isnan(short[:, N:].float()).all(), "wrote past N"
+    rows = sample_rows(1000, 48, 58, must=(0, 127, 128, 999))
+    want = P.projection_rows(bits(x[:1000]), bits(wq), rows)
+    assert_close(short[rows, :N].float().cpu().numpy(), want, "128-row tiles vs oracle rows")
