@@ -72,10 +72,14 @@ __device__ __forceinline__ void wg_barrier() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
-__device__ inline void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
-    int total = tiles_m * tiles_n;
-    int id = blockIdx.x;
-    if (total % kNumXcd == 0) id = (id % kNumXcd) * (total / kNumXcd) + id / kNumXcd;
+// Tile of grid position `id` in a tiles_m x tiles_n grid (see tile_coords).
+__device__ inline void tile_coords_id(int id, int tiles_m, int tiles_n, int& tm, int& tn) {
+    const int total = tiles_m * tiles_n;
+    // XCD x runs positions x, x + 8, ...: it gets the contiguous range of
+    // the total / 8 tiles (one more for the first total % 8 XCDs) from
+    // x * (total / 8) + min(x, total % 8)
+    const int per = total / kNumXcd, rem = total % kNumXcd, x = id % kNumXcd;
+    id = x * per + min(x, rem) + id / kNumXcd;
     int per_group = kGroupM * tiles_n;
     int group = id / per_group;
     int first_m = group * kGroupM;
@@ -83,6 +87,10 @@ __device__ inline void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
     int in_group = id - group * per_group;
     tm = first_m + in_group % gsize;
     tn = in_group / gsize;
+}
+
+__device__ inline void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
+    tile_coords_id((int)blockIdx.x, tiles_m, tiles_n, tm, tn);
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* p, int64_t bytes) {

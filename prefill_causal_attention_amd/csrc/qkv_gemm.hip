@@ -16,7 +16,8 @@
 //    projection shape, although it reads a third fewer LDS bytes per MFMA).
 //    The wave computes the transposed product (MFMA rows = n, columns = m), so
 //    each lane's accumulator holds 4 consecutive n of one m.  Grids too small
-//    to fill the CUs use 128 x 256 tiles instead (waves of 32 x 128).
+//    to fill the CUs, and the last round of short grids, use 128 x 256 tiles
+//    instead (waves of 32 x 128); see plan_tiles.
 //  * Operand tiles go from HBM/L2 straight into LDS with buffer_load ... lds
 //    (no register staging, no LDS stores), double-buffered: the tiles of K
 //    step kt + 2 are requested as soon as step kt's tiles are no longer read,
@@ -69,11 +70,10 @@ __device__ __forceinline__ void lds_wait_f(u32x4_t (&f)[5]) {
 // into the bf16 / fp8 page pools.  RES: y = x w^T + res, the residual added
 // to the fp32 accumulators before the single bf16 rounding.  RS: the fp32
 // accumulators of row m are scaled by row_scale[m] before that rounding.
-// BMT: rows of x per tile, 256 (waves of 64 x 128) or 128 (waves of 32 x 128,
-// for grids whose 256-row tiles would leave the last round of CUs half idle).
+// BMT: rows of x per tile, 256 (waves of 64 x 128) or 128 (waves of 32 x 128).
+// One workgroup computes output tile (tm, tn).
 template <int KV, bool RES, bool RS, int BMT>
-__global__ __launch_bounds__(kThreadsG) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void qkv_gemm_kernel(GemmArgs a) {
+__device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tm, int tn) {
     constexpr int FMg = BMT / 128;                    // 32 x 32 blocks per wave along m
     constexpr int WMR = 32 * FMg;                     // x rows per wave
     constexpr int NF = FNg + FMg;                     // operand fragments per 16-key step
@@ -86,9 +86,6 @@ void qkv_gemm_kernel(GemmArgs a) {
     const int wm = wave >> 1, wn = wave & 1;     // wave position: 4 (m) x 2 (n)
     const int r32 = lane & 31, half = lane >> 5;
 
-    const int tiles_m = (a.M + BMT - 1) / BMT, tiles_n = (a.N + BN - 1) / BN;
-    int tm, tn;
-    tile_coords(tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BMT, n0 = tn * BN;
     const int rows_x = min(BMT, a.M - m0), rows_w = min(BN, a.N - n0);
     const int nk = (a.K + BKK - 1) / BKK;
@@ -351,6 +348,29 @@ void qkv_gemm_kernel(GemmArgs a) {
     }
 }
 
+// The grid: BMT 256 or 128, tiles of that height over the whole output; BMT
+// 0, the first split_n column strips (BN wide) in 256-row tiles, then the
+// rest of N in 128-row tiles, the 256-row tiles first in dispatch order.
+template <int KV, bool RES, bool RS, int BMT>
+__global__ __launch_bounds__(kThreadsG) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void qkv_gemm_kernel(GemmArgs a, int split_n) {
+    const int tiles_n = (a.N + BN - 1) / BN;
+    int tm, tn;
+    if constexpr (BMT != 0) {
+        tile_coords_id((int)blockIdx.x, (a.M + BMT - 1) / BMT, tiles_n, tm, tn);
+        gemm_tile<KV, RES, RS, BMT>(a, tm, tn);
+    } else {
+        const int tm256 = (a.M + 255) / 256, big = tm256 * split_n;
+        if ((int)blockIdx.x < big) {
+            tile_coords_id((int)blockIdx.x, tm256, split_n, tm, tn);
+            gemm_tile<KV, RES, RS, 256>(a, tm, tn);
+        } else {
+            tile_coords_id((int)blockIdx.x - big, (a.M + 127) / 128, tiles_n - split_n, tm, tn);
+            gemm_tile<KV, RES, RS, 128>(a, tm, tn + split_n);
+        }
+    }
+}
+
 }  // namespace
 
 namespace {
@@ -380,35 +400,60 @@ __global__ __launch_bounds__(256) void rms_stats_kernel(const uint16_t* x, int64
 }
 
 template <int KV, bool RES, bool RS, int BMT>
-hipError_t launch_tiles(const GemmArgs& a, hipStream_t s) {
+hipError_t launch_tiles(const GemmArgs& a, int tiles, int split_n, hipStream_t s) {
     static const hipError_t attr = hipFuncSetAttribute((const void*)qkv_gemm_kernel<KV, RES, RS, BMT>,
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
     if (attr != hipSuccess) return attr;
-    const int tiles = ((a.M + BMT - 1) / BMT) * ((a.N + BN - 1) / BN);
-    hipLaunchKernelGGL((qkv_gemm_kernel<KV, RES, RS, BMT>), dim3(tiles), dim3(kThreadsG), LDS_BYTES, s, a);
+    hipLaunchKernelGGL((qkv_gemm_kernel<KV, RES, RS, BMT>), dim3(tiles), dim3(kThreadsG), LDS_BYTES, s, a, split_n);
     return hipGetLastError();
 }
 
-// 128-row tiles are used only when the whole 128-row grid fits in one round
-// of the CUs (data-flow article §5.2's "wave" effect): 1024 x 6144 x 4096 has
-// 96 tiles of 256 rows, which leave 160 CUs idle, and runs 1.45x faster as 192
-// tiles of 128 rows.  A 128-row tile costs about 0.6 of a 256-row one (per-tile
-// start-up and epilogue, and half the operand reuse), and a partly filled last
-// round of 256-row tiles runs faster than a full one, so on every grid that
-// already takes more than one round 256-row tiles measured as fast or faster
-// (2048 x 12288 x 4096: 1070 against 1008 TFLOP/s; 8192 x 6144 x 4096: 1250
-// against 1044).
-bool half_tiles(const GemmArgs& a) {
-    const int ncu = device_cus();
-    if (ncu <= 0) return false;
-    const int64_t tn = (a.N + BN - 1) / BN;
-    const int64_t t256 = (a.M + 255) / 256 * tn, t128 = (a.M + 127) / 128 * tn;
-    return t256 < t128 && t128 <= ncu;
+// Grid shape (the data-flow article's §5.2 "wave" effect: a grid of 384
+// tiles on 256 CUs takes two rounds for one and a half rounds of work).  A
+// 128-row tile costs about 0.6 of a 256-row one (per-tile start-up and
+// epilogue, half the operand reuse).
+//  * A grid whose 128-row tiles all fit in one round of the CUs runs on them:
+//    1024 x 6144 x 4096 has 96 tiles of 256 rows, which leave 160 CUs idle,
+//    and runs 1.37-1.45x faster as 192 tiles of 128 rows.
+//  * A grid of 256-row tiles whose last round is at most half full keeps the
+//    full rounds in 256-row tiles (whole column strips) and turns the rest
+//    into one round of 128-row tiles: 2048 x 12288 x 4096 is one round of 256
+//    tiles of 256 rows plus 256 tiles of 128 rows (1.10x faster than 384
+//    tiles of 256 rows, whose second round is half idle; 3000 x 6144 x 4096:
+//    1.19x).  Only for grids of at most kMaxMixedRounds full rounds: 27808 x
+//    6144 x 4096 (ten full rounds and a fifth) measured 2% slower mixed.
+//  * Otherwise 256-row tiles throughout (a grid of only 128-row tiles
+//    measured 16-22% slower than 256-row tiles on every multi-round shape).
+constexpr int64_t kMaxMixedRounds = 3;
+
+struct TilePlan {
+    int bmt;       // 256, 128, or 0: split_n strips of 256-row tiles, then 128-row tiles
+    int tiles;
+    int split_n;
+};
+
+TilePlan plan_tiles(const GemmArgs& a) {
+    const int64_t ncu = device_cus();
+    const int64_t tn = (a.N + BN - 1) / BN, tm256 = (a.M + 255) / 256, tm128 = (a.M + 127) / 128;
+    const int64_t t256 = tm256 * tn, t128 = tm128 * tn;
+    if (ncu > 0) {
+        if (t256 < t128 && t128 <= ncu) return {128, (int)t128, 0};
+        const int64_t full = t256 / ncu * ncu;               // tiles of the full rounds
+        if (full > 0 && full < t256 && full <= kMaxMixedRounds * ncu) {
+            const int64_t n1 = full / tm256;                 // strips of 256-row tiles within them
+            const int64_t small = tm128 * (tn - n1);
+            if (n1 >= 1 && n1 < tn && small <= ncu) return {0, (int)(tm256 * n1 + small), (int)n1};
+        }
+    }
+    return {256, (int)t256, 0};
 }
 
 template <int KV, bool RES, bool RS>
 hipError_t launch_kv(const GemmArgs& a, hipStream_t s) {
-    return half_tiles(a) ? launch_tiles<KV, RES, RS, 128>(a, s) : launch_tiles<KV, RES, RS, 256>(a, s);
+    const TilePlan t = plan_tiles(a);
+    if (t.bmt == 128) return launch_tiles<KV, RES, RS, 128>(a, t.tiles, 0, s);
+    if (t.bmt == 0) return launch_tiles<KV, RES, RS, 0>(a, t.tiles, t.split_n, s);
+    return launch_tiles<KV, RES, RS, 256>(a, t.tiles, 0, s);
 }
 
 }  // namespace

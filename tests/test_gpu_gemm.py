@@ -80,19 +80,23 @@ def test_full_size_sampled(idx):
     assert_close(y[rows].float().cpu().numpy(), want, f"{w.name} projection rows")
 
 
-def test_row_tile_heights_agree_bitwise():
-    """A grid that 256-row tiles would leave mostly idle (1000 x 6144: 96 tiles)
-    runs on 128-row tiles; each output still sums its K terms in the same order,
-    so the rows equal bitwise those of a tall call (8192 rows, 256-row tiles)."""
+@pytest.mark.parametrize("short_m,tall_m,N", [(1000, 8192, 6144), (2048, 8192, 12288), (3000, 5120, 6216)])
+def test_row_tile_heights_agree_bitwise(short_m, tall_m, N):
+    """Every grid plan sums each output's K terms in the same order, so rows
+    of a short call equal bitwise those of a tall call.  On 256 CUs the short
+    calls run on 128-row tiles (1000 x 6144: 96 tiles of 256 rows would leave
+    most CUs idle) or on the mixed grid (2048 x 12288: one round of 256-row
+    tiles, then the last 16 column strips as 128-row tiles; 3000 x 6216, also
+    ragged in M and N), the tall calls on 256-row tiles throughout."""
     require_gpu()
-    M, N, K = 8192, 6144, 1032
-    x = workloads.normal_bf16(56, (M, K))
+    K = 1032
+    x = workloads.normal_bf16(56, (tall_m, K))
     wq = workloads.normal_bf16(57, (K, N), std=float(1 / np.sqrt(K)))
-    say(f"qkv_proj tile heights M={M} and 1000, N={N} K={K}")
+    say(f"qkv_proj tile plans M={tall_m} and {short_m}, N={N} K={K}")
     tall = _gpu_proj(x, wq)
-    short = _gpu_proj(x[:1000], wq, y_pad=8)
-    assert torch.equal(short[:, :N], tall[:1000]), "row tile heights disagree"
+    short = _gpu_proj(x[:short_m], wq, y_pad=8)
+    assert torch.equal(short[:, :N], tall[:short_m]), "grid plans disagree"
     assert torch.isnan(short[:, N:].float()).all(), "wrote past N"
-    rows = sample_rows(1000, 48, 58, must=(0, 127, 128, 999))
-    want = P.projection_rows(bits(x[:1000]), bits(wq), rows)
-    assert_close(short[rows, :N].float().cpu().numpy(), want, "128-row tiles vs oracle rows")
+    rows = sample_rows(short_m, 48, 58, must=(0, 127, 128, 255, 256, short_m - 1))
+    want = P.projection_rows(bits(x[:short_m]), bits(wq), rows)
+    assert_close(short[rows, :N].float().cpu().numpy(), want, "short call vs oracle rows")
