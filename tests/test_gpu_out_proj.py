@@ -57,6 +57,7 @@ def test_zero_weight_returns_residual():
 @pytest.mark.parametrize("M,N,K,in_place", [(100, 200, 64, False), (257, 384, 4096, True), (513, 1000, 1032, False),
                                             (2048, 4096, 4096, True)])
 def test_normal_inputs_tolerance(M, N, K, in_place):
+    """(2048, 4096) runs on 128-row tiles on 256 CUs, the others on 256-row tiles."""
     require_gpu()
     o = workloads.normal_bf16(94, (M, K))
     w = workloads.normal_bf16(95, (K, N), std=float(1 / np.sqrt(K)))
@@ -78,3 +79,25 @@ def test_full_size_sampled():
     rows = sample_rows(M, 48, 100, must=(0, 255, 256, M - 1))
     want = LY.out_projection_residual(bits(o), bits(w), bits(res), rows=rows)
     assert_close(got[rows].float().cpu().numpy(), want, "out_proj s=8192")
+
+
+def test_mixed_grid_rows_equal_a_tall_call_bitwise():
+    """2304 x 8192 runs on the mixed grid on 256 CUs (one round of 256-row
+    tiles, the last four column strips in 128-row tiles); 8192 x 8192 on
+    256-row tiles throughout.  Each output sums its K terms and adds its
+    residual in the same order either way, so the first 2304 rows agree bit
+    for bit; sampled rows are also checked against the oracle.  The residual
+    is drawn at half scale: y is then about N(0, 1.25), and no output reaches
+    8, where bf16 rounding alone would exceed the 2e-2 bound."""
+    require_gpu()
+    M, N, K = 2304, 8192, 1032
+    o = workloads.normal_bf16(91, (8192, K))
+    w = workloads.normal_bf16(92, (K, N), std=float(1 / np.sqrt(K)))
+    res = workloads.normal_bf16(93, (8192, N), std=0.5)
+    say(f"out_proj_residual mixed grid M={M} and 8192, N={N} K={K}")
+    tall = _run(o, w, res, in_place=False)
+    short = _run(o[:M], w, res[:M], in_place=False)
+    assert torch.equal(short, tall[:M]), "grid plans disagree"
+    rows = sample_rows(M, 48, 90, must=(0, 127, 128, 255, 256, M - 1))
+    want = LY.out_projection_residual(bits(o[:M]), bits(w), bits(res[:M]), rows=rows)
+    assert_close(short[rows].float().cpu().numpy(), want, "out_proj mixed grid rows")

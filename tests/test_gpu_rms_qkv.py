@@ -42,8 +42,10 @@ def _gpu(x, wtg, eps, pad=8):
     return y[:, :N], inv[:M]
 
 
-@pytest.mark.parametrize("M,K,N,eps", [(100, 256, 200, 1e-6), (257, 4096, 384, 1e-5), (513, 1032, 1000, 0.0)])
+@pytest.mark.parametrize("M,K,N,eps", [(100, 256, 200, 1e-6), (257, 4096, 384, 1e-5), (513, 1032, 1000, 0.0),
+                                       (2304, 1032, 8192, 1e-6)])
 def test_parity(M, K, N, eps):
+    """(2304, 8192) runs on the mixed grid of 256- and 128-row tiles on 256 CUs."""
     require_gpu()
     x, g, w = _inputs(101, M, K, N)
     say(f"rms_norm_qkv_proj M={M} K={K} N={N} eps={eps}")
