@@ -392,12 +392,15 @@ pca_status pca_e4m3_encode(const float* x, uint8_t* codes, int64_t n, void* stre
 
 /*
  * pca_clock_stamp -- measurement utility: enqueues on `stream` a small kernel
- *   whose 64 one-wave blocks each write, at out[3*b .. 3*b+2], the XCD it ran
- *   on (hardware XCC id), that XCD's shader-clock cycle counter (s_memtime)
- *   and the 100 MHz real-time counter (s_memrealtime).  Two stamps around a
- *   stretch of work give each XCD's average shader clock over it (cycles
- *   over seconds), the clock the MFMA peak scales with (the published dense
- *   peaks assume 2.4 GHz).  out: device uint64[192], 8-byte aligned.
+ *   whose 1024 one-wave blocks each write, at out[4*b .. 4*b+3], the XCD it
+ *   ran on (hardware XCC id), its HW_ID register (shader engine, array and CU
+ *   in bits 8-15), the shader-clock cycle counter it reads (s_memtime) and
+ *   the 100 MHz real-time counter (s_memrealtime).  Two stamps around a
+ *   stretch of work give, per CU present in both, the average shader clock
+ *   over it (cycles over seconds), the clock the MFMA peak scales with (the
+ *   published dense peaks assume 2.4 GHz).  Cycle counters of different
+ *   shader engines do not agree, so only stamps of one CU may be paired.
+ *   out: device uint64[4096], 8-byte aligned.
  */
 pca_status pca_clock_stamp(uint64_t* out, void* stream);
 

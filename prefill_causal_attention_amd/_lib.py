@@ -182,11 +182,11 @@ def _pool(t, name: str, cache_dtype: str):
     return t.data_ptr()
 
 
-CLOCK_STAMP_WORDS = 192        # 64 blocks x (XCC id, shader-clock cycles, 100 MHz real time)
+CLOCK_STAMP_WORDS = 4096       # 1024 blocks x (XCC id, HW_ID, shader-clock cycles, 100 MHz real time)
 
 
 def clock_stamp(out, stream=None):
-    """Enqueue a stamp of every XCD's shader-clock and real-time counters into
+    """Enqueue pca_clock_stamp: the GPU's clock counters, read on the device, into
     the int64 device tensor out (CLOCK_STAMP_WORDS elements)."""
     _check("pca_clock_stamp", load().pca_clock_stamp(_flat(out, "out", "i64", CLOCK_STAMP_WORDS), _stream(stream)))
     return out
@@ -194,17 +194,25 @@ def clock_stamp(out, stream=None):
 
 def shader_clock_mhz(before, after) -> dict:
     """Average shader clock per XCD between two stamps (host int64 arrays of
-    CLOCK_STAMP_WORDS): cycles elapsed over real time elapsed, per XCD from the
-    medians of its blocks' counters."""
+    CLOCK_STAMP_WORDS): for every CU that stamped both times (XCC id and the
+    shader engine, array and CU bits of HW_ID), cycles elapsed over real time
+    elapsed on that CU's own counters; per XCD the median over its CUs."""
     import numpy as np
-    a, b = np.asarray(before).reshape(-1, 3), np.asarray(after).reshape(-1, 3)
-    out = {}
-    for x in sorted(set(a[:, 0].tolist()) & set(b[:, 0].tolist())):
-        ca, ra = np.median(a[a[:, 0] == x, 1]), np.median(a[a[:, 0] == x, 2])
-        cb, rb = np.median(b[b[:, 0] == x, 1]), np.median(b[b[:, 0] == x, 2])
-        if rb > ra:
-            out[int(x)] = float((cb - ca) / ((rb - ra) / 100e6) / 1e6)
-    return out
+    a, b = np.asarray(before).reshape(-1, 4), np.asarray(after).reshape(-1, 4)
+
+    def by_cu(s):
+        out = {}
+        for x, hw, cyc, rt in s.tolist():
+            out.setdefault((int(x), int(hw) & 0xFF00), []).append((cyc, rt))
+        return {k: (np.median([c for c, _ in v]), np.median([r for _, r in v])) for k, v in out.items()}
+
+    ca, cb = by_cu(a), by_cu(b)
+    per_xcd = {}
+    for k in set(ca) & set(cb):
+        (c0, r0), (c1, r1) = ca[k], cb[k]
+        if r1 > r0 and c1 > c0:
+            per_xcd.setdefault(k[0], []).append((c1 - c0) / ((r1 - r0) / 100e6) / 1e6)
+    return {x: float(np.median(v)) for x, v in sorted(per_xcd.items())}
 
 
 def version() -> str:

@@ -44,6 +44,7 @@ def _oracle(w, buf, window, rows=None):
     ([300], 4, 2, 128, 64),
     ([257, 90, 1], 8, 2, 128, 37),        # varlen, a 1-token sequence
     ([500], 8, 8, 64, 1),
+    ([130, 70], 4, 2, 32, 50),             # head_dim 32, varlen
     ([200, 333], 4, 1, 32, 150),
     ([700], 10, 2, 128, 300),              # G = 5
 ])
