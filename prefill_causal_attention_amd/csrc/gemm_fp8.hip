@@ -138,6 +138,11 @@ void gemm_fp8_kernel(Fp8GemmArgs a) {
             constexpr int i = h * 2 + decltype(Ic)::value / FM, j = decltype(Ic)::value % FM;
             acc[i][j] = mfma_f8(f[2 * i], f[2 * i + 1], f[8 + 2 * j], f[8 + 2 * j + 1], acc[i][j]);
         });
+        // the products' next use is past the barrier and the loop's branches;
+        // an asm that reads them keeps the compiler from sinking these MFMAs
+        // down to it (they would then no longer overlap the operand reads)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) asm volatile("" ::"a"(acc[h * 2 + q / FM][q % FM]));
         __builtin_amdgcn_sched_barrier(0);
     };
     using KS0 = std::integral_constant<int, 0>;
