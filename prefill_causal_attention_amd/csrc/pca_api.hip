@@ -100,6 +100,9 @@ pca_status check_gemm(const pca_bf16* x, int64_t ldx, const pca_bf16* w_t, int64
                     "(ldx=%lld ldw=%lld ldy=%lld)", (long long)ldx, (long long)ldw, (long long)ldy);
     if (view_too_big(256, ldx, 2) || view_too_big(256, ldw, 2))
         return fail(PCA_ERR_UNSUPPORTED, "row stride too large for a 256-row tile view");
+    // the grid holds one workgroup per 128 x 256 tile at most
+    if ((M + 127) / 128 * ((N + 255) / 256) > INT32_MAX)
+        return fail(PCA_ERR_UNSUPPORTED, "M x N too large for one launch (M=%lld N=%lld)", (long long)M, (long long)N);
     memset(&a, 0, sizeof(a));
     a.x = x; a.ldx = ldx; a.w = w_t; a.ldw = ldw; a.y = y; a.ldy = ldy;
     a.M = (int)M; a.N = (int)N; a.K = (int)K;
@@ -249,6 +252,8 @@ pca_status pca_qkv_proj_fp8(const uint8_t* xq, int64_t ldxq, const float* sx, co
         return fail(PCA_ERR_INVALID_ARG, "ldxq, ldwq >= K (multiples of 16), ldy >= N (multiple of 8) required");
     if (view_too_big(256, ldxq, 1) || view_too_big(256, ldwq, 1))
         return fail(PCA_ERR_UNSUPPORTED, "row stride too large for a 256-row tile view");
+    if ((M + 255) / 256 * ((N + 255) / 256) > INT32_MAX)
+        return fail(PCA_ERR_UNSUPPORTED, "M x N too large for one launch (M=%lld N=%lld)", (long long)M, (long long)N);
     pca::Fp8GemmArgs a;
     a.x = xq; a.ldx = ldxq; a.sx = sx; a.w = wq; a.ldw = ldwq; a.sw = sw; a.y = y; a.ldy = ldy;
     a.M = (int)M; a.N = (int)N; a.K = (int)K;

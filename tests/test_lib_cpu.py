@@ -177,3 +177,15 @@ def test_fp8qk_attention_validation():
     st, _ = _status("pca_prefill_attention_fp8qk", None, 4096, None, 1024, None, 8, None, 1024, None, 1, 0, 0, 32, 8,
                     128, ctypes.c_float(0.088), 1, None, 4096, None)
     assert st == 0                                                       # empty batch
+
+
+def test_gemm_grids_too_large_for_one_launch_rejected():
+    """M x N whose tile count exceeds int32 is refused before any launch (the
+    product and the fp8 product), not wrapped into a wrong grid."""
+    big = 1 << 30
+    st, msg = _status("pca_qkv_proj", FAKE, 64, FAKE, 64, FAKE, big, big, big, 64, None)
+    assert st == 2 and "too large" in msg, (st, msg)
+    lib = pca.load()
+    st = lib.pca_qkv_proj_fp8(FAKE, 64, FAKE, FAKE, 64, FAKE, FAKE, big, big, big, 64, None)
+    msg = lib.pca_last_error().decode()
+    assert st == 2 and "too large" in msg, (st, msg)
