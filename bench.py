@@ -112,8 +112,9 @@ def sample_clocks(pca, torch, launch, seconds):
     vals = sorted(per_xcd.values())
     return {"sclk_mhz": vals[len(vals) // 2] if vals else None, "sclk_per_xcd_mhz": per_xcd,
             "mclk_mhz": memory_clock_mhz(),
-            "note": f"shader clock = s_memtime cycles / s_memrealtime (100 MHz) per XCD over {n} back-to-back "
-                    "attention launches after the timed steps (median over XCDs); mclk from amdsmi"}
+            "note": f"shader clock = s_memtime cycles / s_memrealtime (100 MHz) on each CU's own counters over {n} "
+                    "back-to-back attention launches after the timed steps, per XCD the median over its CUs, "
+                    "sclk_mhz the median over XCDs; mclk from amdsmi"}
 
 
 def cpu_baseline(w, target_s):
