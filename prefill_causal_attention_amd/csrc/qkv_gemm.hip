@@ -21,7 +21,13 @@
 //  * Operand tiles go from HBM/L2 straight into LDS with buffer_load ... lds
 //    (no register staging, no LDS stores), double-buffered: the tiles of K
 //    step kt + 2 are requested as soon as step kt's tiles are no longer read,
-//    so each load has a whole K step of matrix work to land.  Rows of 64
+//    so each load has a whole K step of matrix work to land.  Only waves 0-3
+//    (one per SIMD) request tiles: the CU accepts these requests at about 64
+//    bytes per clock, so the 64 KiB of a K step keeps a requesting wave waiting
+//    at its DMA instructions for ~600-1000 cycles.  Requested by every wave,
+//    right after the barrier, that wait held both waves of each SIMD off the
+//    matrix cores at once; now the other wave of the SIMD issues MFMAs through
+//    it (+4-7% on the projection shapes, the same bits).  Rows of 64
 //    elements (8 chunks of 16 bytes) are stored with chunk c of row r at
 //    c ^ ((r >> 1) & 7): the 16 rows a 16-lane group of a ds_read_b128 touches
 //    then cover all 64 banks once.
@@ -51,7 +57,8 @@ constexpr int BKK = 64;                       // bf16 elements per K step (ROWB 
 constexpr int kWavesG = 8;                    // two waves per SIMD
 constexpr int kThreadsG = kWavesG * 64;
 constexpr int FNg = 4;                        // 32 x 32 blocks per wave along n: 128 columns
-constexpr int DMA_W_PER_WAVE = DMA_PER_TILE / kWavesG;   // 1 KiB DMA blocks of the W tile per wave
+constexpr int kDmaWaves = 4;                  // waves 0..3 request every operand tile
+constexpr int DMA_W_PER_WAVE = DMA_PER_TILE / kDmaWaves;   // 1 KiB DMA blocks of the W tile per requesting wave
 
 // Wait until at most N LDS reads are outstanding; the fragments pass through
 // the asm so their consumers stay after the wait (6 or 5 fragments per step).
@@ -77,7 +84,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tm, int tn) {
     constexpr int FMg = BMT / 128;                    // 32 x 32 blocks per wave along m
     constexpr int WMR = 32 * FMg;                     // x rows per wave
     constexpr int NF = FNg + FMg;                     // operand fragments per 16-key step
-    constexpr int DMA_X_PER_WAVE = BMT * ROWB / 1024 / kWavesG;   // 1 KiB DMA blocks of the x tile per wave
+    constexpr int DMA_X_PER_WAVE = BMT * ROWB / 1024 / kDmaWaves;   // 1 KiB DMA blocks of the x tile per requesting wave
     extern __shared__ __align__(16) uint16_t smem[];
     lds_char_t* lds = (lds_char_t*)smem;
     const int tid = threadIdx.x;
@@ -90,7 +97,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tm, int tn) {
     const int rows_x = min(BMT, a.M - m0), rows_w = min(BN, a.N - n0);
     const int nk = (a.K + BKK - 1) / BKK;
 
-    // DMA lane offsets (bytes from the tile's first row at the current K step):
+    // DMA lane offsets (bytes from the tile's first row at the current K step)
+    // of the requesting waves 0..3 (the others compute them too, unused):
     // block b of a wave covers rows 8b .. 8b + 7; lane l writes physical chunk
     // l % 8 of row 8b + l / 8, i.e. fetches logical chunk (l % 8) ^ swz(row).
     // (sized for the 256-row tile: a lambda capturing an array whose size
@@ -100,13 +108,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tm, int tn) {
     static_assert(DMA_X_PER_WAVE <= DMA_W_PER_WAVE, "x tile has at most 256 rows");
 #pragma unroll
     for (int i = 0; i < DMA_W_PER_WAVE; ++i) {
-        const int row = (wave * DMA_W_PER_WAVE + i) * 8 + lane / 8;
+        const int row = ((wave & (kDmaWaves - 1)) * DMA_W_PER_WAVE + i) * 8 + lane / 8;
         lchw[i] = (lane % 8) ^ swz(row);
         offw[i] = (uint32_t)(((int64_t)row * a.ldw + lchw[i] * 8) * 2);
     }
 #pragma unroll
     for (int i = 0; i < DMA_X_PER_WAVE; ++i) {
-        const int row = (wave * DMA_X_PER_WAVE + i) * 8 + lane / 8;
+        const int row = ((wave & (kDmaWaves - 1)) * DMA_X_PER_WAVE + i) * 8 + lane / 8;
         lchx[i] = (lane % 8) ^ swz(row);
         offx[i] = (uint32_t)(((int64_t)row * a.ldx + lchx[i] * 8) * 2);
     }
@@ -118,6 +126,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tm, int tn) {
         const __amdgpu_buffer_rsrc_t rx =
             uniform_rsrc(a.x + (int64_t)m0 * a.ldx + k0, (int64_t)rows_x * a.ldx * 2 - (int64_t)k0 * 2);
         lds_char_t* dst = lds + stage * STAGE_B;
+        if (wave >= kDmaWaves) return;                    // uniform per wave
 #pragma unroll
         for (int i = 0; i < DMA_W_PER_WAVE; ++i) {
             const int blk = wave * DMA_W_PER_WAVE + i;
