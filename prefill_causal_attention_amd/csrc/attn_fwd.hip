@@ -262,8 +262,9 @@ constexpr int kBtPerThread = 4;         // block-table entries per thread loaded
 
 // DMA of one K or V tile (keys [kbase, kbase + BK) of one sequence) into the
 // LDS buffer `dst`: the buffer view starts at the tile, so keys at or past the
-// sequence end read 0.  Wave w fills the 1 KiB blocks w, w + 8, ...
-template <int HD>
+// sequence end read 0.  With NW waves issuing, issuing wave w fills the 1 KiB
+// blocks w, w + NW, ...
+template <int HD, int NW = kWaves>
 __device__ __forceinline__ void dma_tile(const uint16_t* src, int64_t ld, int64_t s0, int Lb, int wave, int kbase,
                                          lds_char_t* dst, const uint32_t* off) {
     using C = Cfg<HD>;
@@ -276,9 +277,9 @@ __device__ __forceinline__ void dma_tile(const uint16_t* src, int64_t ld, int64_
     const uint32_t bytes = (uint32_t)__builtin_amdgcn_readfirstlane((int)((int64_t)(Lb - kbase) * ld * 2));
     const __amdgpu_buffer_rsrc_t r = make_rsrc((const void*)ubase, bytes);
 #pragma unroll
-    for (int i = 0; i < C::DMA_ITERS; ++i) {
-        const int blk = wave + i * kWaves;
-        if (C::NBLK % kWaves == 0 || blk < C::NBLK)
+    for (int i = 0; i < (C::NBLK + NW - 1) / NW; ++i) {
+        const int blk = wave + i * NW;
+        if (C::NBLK % NW == 0 || blk < C::NBLK)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(dst + blk * 1024), 16, off[i], 0, 0, 0);
     }
 }
@@ -577,11 +578,19 @@ void attn_fwd_kernel(Params p) {
 
     // ---- DMA lane offsets: lane l writes bytes [16 l, 16 l + 16) of a 1 KiB block,
     // i.e. row l / NC, physical chunk l % NC, so it fetches the logical chunk the
-    // swizzle puts there.
-    uint32_t dma_k[C::DMA_ITERS], dma_v[C::DMA_ITERS];
+    // swizzle puts there.  Plain kernels: only group B's four waves request
+    // K/V tiles (a wave waits at its DMA instructions until the CU accepts
+    // them, at about 64 bytes per clock; group A's waves request theirs right
+    // before their matrix phase, so that wait delayed their MFMAs; group B
+    // requests at the start of its softmax; +1-2.5%).  The other kernels: all
+    // eight waves.
+    constexpr int kDmaWaves = PAGED == 0 ? kWaves / 2 : kWaves;
+    constexpr int kDmaIters = (C::NBLK + kDmaWaves - 1) / kDmaWaves;
+    const int dwave = wave % kDmaWaves;                     // index among the requesting waves
+    uint32_t dma_k[kDmaIters], dma_v[kDmaIters];
 #pragma unroll
-    for (int i = 0; i < C::DMA_ITERS; ++i) {
-        const int row = (wave + i * kWaves) * C::RPI + lane / C::NC;
+    for (int i = 0; i < kDmaIters; ++i) {
+        const int row = (dwave + i * kDmaWaves) * C::RPI + lane / C::NC;
         const int lch = (lane % C::NC) ^ swz<HD>(row);
         dma_k[i] = (uint32_t)(((int64_t)row * p.ldk + g * HD + lch * 8) * 2);
         dma_v[i] = (uint32_t)(((int64_t)row * p.ldv + g * HD + lch * 8) * 2);
@@ -624,7 +633,7 @@ void attn_fwd_kernel(Params p) {
         } else if constexpr (PAGED == 1) {
             dma_tile_paged<HD>(rk, wave, lane, tile * BK, Lk, p.n_kv, g, p.num_pages, lds + buf, lbt);
         } else {
-            dma_tile<HD>(p.k, p.ldk, s0, Lb, wave, tile * BK, lds + buf, dma_k);
+            if (!lead) dma_tile<HD, kDmaWaves>(p.k, p.ldk, s0, Lb, dwave, tile * BK, lds + buf, dma_k);
         }
     };
     auto issue_v = [&](int tile, int buf) __attribute__((always_inline)) {
@@ -636,7 +645,7 @@ void attn_fwd_kernel(Params p) {
         } else if constexpr (PAGED == 1) {
             dma_tile_paged<HD>(rv, wave, lane, tile * BK, Lk, p.n_kv, g, p.num_pages, lds + buf, lbt);
         } else {
-            dma_tile<HD>(p.v, p.ldv, s0, Lb, wave, tile * BK, lds + buf, dma_v);
+            if (!lead) dma_tile<HD, kDmaWaves>(p.v, p.ldv, s0, Lb, dwave, tile * BK, lds + buf, dma_v);
         }
     };
     // wait for this wave's loads; for fp8 pages also convert what it loaded
@@ -920,7 +929,8 @@ void attn_fwd_kernel(Params p) {
         // barriers; B starts with one extra barrier and A ends with one.
         //
         // DMA: in half-step 2m + 1 (A's matrix phase of tile m, B's softmax of
-        // tile m) every wave issues its share of K_{m+2} (into K_m's buffer) and
+        // tile m) the requesting waves (group B for plain kernels, every wave
+        // otherwise) issue their shares of K_{m+2} (into K_m's buffer) and
         // V_{m+1} (into V_{m-1}'s); both were last read in half-step 2m.  They are
         // waited for at the end of half-step 2m + 2 and first read in 2m + 3.
         // KC/KN: K buffers of tiles j and j + 1; VC/VN: V buffers of j and j + 1.
