@@ -264,6 +264,54 @@ pca_status pca_prefill_attention_window(const pca_bf16* q, const pca_bf16* k, co
                                         void* stream);
 
 /*
+ * pca_prefill_attention_splitkv -- pca_prefill_attention for shallow grids,
+ *   with the key range of long query blocks split over two workgroups (the
+ *   data-flow article §5.2: a grid that fills the compute units about once
+ *   leaves many idle while the longest tiles finish).  When the launch has at
+ *   most one task group (8 waves of 32 query rows sharing a kv head) per
+ *   workgroup slot of the device, and its units (sequence, kv head) spread
+ *   evenly over the 8 XCDs, task groups with more than three quarters of the
+ *   longest sequence's 64-key tiles (at least 8 tiles in it) run as two
+ *   chunks, tiles [0, n/2) and [n/2, n).  Each chunk stores its partial result (fp32 accumulators,
+ *   reference and row sums) in the workspace; the chunk that finishes second
+ *   merges the two in chunk order and writes o.  Otherwise the call runs
+ *   pca_prefill_attention unchanged (bitwise the same output).
+ *   The output is deterministic, but a split row sums its keys in a
+ *   different order than pca_prefill_attention, so the two differ by
+ *   rounding; it also depends on the launch (a sequence alone and inside a
+ *   batch may differ by rounding).
+ *   workspace: device memory of at least
+ *        pca_prefill_attention_splitkv_workspace(...) bytes, 256-byte aligned,
+ *        owned by the caller, ZEROED ONCE before its first use; every call
+ *        leaves its counters zero again.  Calls that share a workspace must
+ *        not overlap (one stream, or ordered).
+ *   Every other argument as for pca_prefill_attention.  Errors: a null or
+ *   misaligned workspace, or workspace_bytes below the needed size, is
+ *   PCA_ERR_INVALID_ARG (before any launch).
+ */
+pca_status pca_prefill_attention_splitkv(const pca_bf16* q, const pca_bf16* k, const pca_bf16* v,
+                                         int64_t ldq, int64_t ldk, int64_t ldv,
+                                         const int32_t* cu_seqlens, int num_seqs, int max_seqlen,
+                                         int64_t total_tokens, int n_head, int n_kv_head, int head_dim,
+                                         float scale, int causal, pca_bf16* o, int64_t ldo,
+                                         void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * pca_prefill_attention_splitkv_workspace -- bytes of the workspace for
+ *   pca_prefill_attention_splitkv with these sizes: 4 KiB of arrival
+ *   counters (at the same place for every size, so one workspace serves calls
+ *   of different sizes), then, per task group slot (num_seqs * n_kv_head *
+ *   ceil(G * ceil(max_seqlen / 32) / 8) of them, G = n_head / n_kv_head, at
+ *   most 1024: larger launches are never split), two chunks' partial results
+ *   of 32 * (32 * head_dim + 128) bytes each (264 KiB per slot at head_dim
+ *   128).  Returns -1 for invalid sizes (num_seqs or
+ *   max_seqlen < 1, n_head not a multiple of n_kv_head, head_dim not 32, 64
+ *   or 128), with the reason in pca_last_error().
+ */
+int64_t pca_prefill_attention_splitkv_workspace(int num_seqs, int max_seqlen, int n_head, int n_kv_head,
+                                                int head_dim);
+
+/*
  * pca_prefill_attention_paged -- causal GQA attention of a prefill chunk over
  *   its sequence's cached prefix.  Chunked prefill ("Prefill vs decode tuning
  *   notes" (hncyxsy.com/news/227904) §2.1; "Decoding LLM inference latency"

@@ -24,7 +24,8 @@ EXPORTED = ("pca_kv_layout", "pca_qkv_proj", "pca_qkv_proj_kv_write", "pca_rms_n
             "pca_quantize_rows_fp8", "pca_qkv_proj_fp8", "pca_e4m3_encode",
             "pca_quantize_heads_fp8", "pca_prefill_attention_fp8qk",
             "pca_prefill_attention",
-            "pca_prefill_attention_window", "pca_prefill_attention_paged", "pca_kv_cache_write",
+            "pca_prefill_attention_window", "pca_prefill_attention_splitkv",
+            "pca_prefill_attention_splitkv_workspace", "pca_prefill_attention_paged", "pca_kv_cache_write",
             "pca_clock_stamp", "pca_last_error", "pca_version")
 
 
@@ -75,10 +76,15 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pca_out_proj_residual.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, i64, i64, i64, vp]
     lib.pca_prefill_attention_window.argtypes = [vp, vp, vp, i64, i64, i64, vp, i32, i32, i64, i32, i32, i32,
                                                  f32, i32, i32, vp, i64, vp]
+    lib.pca_prefill_attention_splitkv.argtypes = [vp, vp, vp, i64, i64, i64, vp, i32, i32, i64, i32, i32, i32,
+                                                  f32, i32, vp, i64, vp, i64, vp]
+    lib.pca_prefill_attention_splitkv_workspace.argtypes = [i32, i32, i32, i32, i32]
+    lib.pca_prefill_attention_splitkv_workspace.restype = ctypes.c_int64
     lib.pca_prefill_attention_paged.argtypes = [vp, i64, vp, i32, i32, i64, vp, i32, vp, i32, i32, i32, vp, vp,
                                                 vp, vp, i64, i32, i32, i32, f32, i32, vp, i64, vp]
     for fn in ("pca_kv_layout", "pca_qkv_proj", "pca_prefill_attention", "pca_kv_cache_write",
                "pca_qkv_proj_kv_write", "pca_prefill_attention_paged", "pca_prefill_attention_window",
+               "pca_prefill_attention_splitkv",
                "pca_out_proj_residual", "pca_rms_norm_qkv_proj", "pca_rms_norm_qkv_proj_noalloc",
                "pca_quantize_rows_fp8", "pca_qkv_proj_fp8",
                "pca_e4m3_encode", "pca_quantize_heads_fp8", "pca_prefill_attention_fp8qk"):
@@ -379,6 +385,45 @@ def prefill_attention(q, k, v, o, n_head: int, n_kv_head: int, head_dim: int,
     _check("pca_prefill_attention", load().pca_prefill_attention(
         pq, pk, pv, ldq, ldk, ldv, pcu, num_seqs, int(max_seqlen), T,
         n_head, n_kv_head, head_dim, float(scale), 1, po, ldo, _stream(stream)))
+    return o
+
+
+def prefill_attention_splitkv_workspace(num_seqs: int, max_seqlen: int, n_head: int, n_kv_head: int,
+                                        head_dim: int) -> int:
+    """Bytes of the workspace prefill_attention_splitkv needs for these sizes."""
+    n = load().pca_prefill_attention_splitkv_workspace(int(num_seqs), int(max_seqlen), int(n_head), int(n_kv_head),
+                                                       int(head_dim))
+    if n < 0:
+        raise PcaError("pca_prefill_attention_splitkv_workspace", -1, load().pca_last_error().decode())
+    return int(n)
+
+
+def prefill_attention_splitkv(q, k, v, o, workspace, n_head: int, n_kv_head: int, head_dim: int,
+                              cu_seqlens=None, max_seqlen: Optional[int] = None, scale: Optional[float] = None,
+                              total_tokens: Optional[int] = None, stream=None):
+    """prefill_attention with split key ranges on shallow grids.  workspace: a
+    contiguous uint8 device tensor of at least prefill_attention_splitkv_workspace
+    bytes, 256-byte aligned, zeroed once before its first use (each call leaves
+    its counters zero); calls sharing it must not overlap."""
+    pq, ldq = _rows(q, "q")
+    pk, ldk = _rows(k, "k")
+    pv, ldv = _rows(v, "v")
+    po, ldo = _rows(o, "o")
+    _dev(workspace, "workspace", "u8")
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    T = q.shape[0] if total_tokens is None else int(total_tokens)
+    if min(k.shape[0], v.shape[0], o.shape[0]) < T:
+        raise ValueError(f"q, k, v and o need at least total_tokens = {T} rows")
+    pcu, num_seqs = _cu(cu_seqlens)
+    if max_seqlen is None:
+        max_seqlen = T
+    if scale is None:
+        scale = head_dim ** -0.5
+    _check("pca_prefill_attention_splitkv", load().pca_prefill_attention_splitkv(
+        pq, pk, pv, ldq, ldk, ldv, pcu, num_seqs, int(max_seqlen), T,
+        n_head, n_kv_head, head_dim, float(scale), 1, po, ldo, workspace.data_ptr(), workspace.numel(),
+        _stream(stream)))
     return o
 
 

@@ -64,6 +64,8 @@
 #include "pca_device.hpp"
 #include "pca_internal.hpp"
 
+#include <cstring>
+
 #include <utility>
 
 namespace pca {
@@ -255,6 +257,14 @@ struct Params {
     int64_t ldk8;
     const uint8_t* kex;
     int64_t ldke;
+    // split key ranges (shallow grids, its own entry point): a task group with
+    // more than split_t kv tiles runs as two chunks, tiles [0, nt / 2) and
+    // [nt / 2, nt), on different workgroups; each chunk stores its partial
+    // result in ws and the chunk that arrives second merges the two
+    int split_t;
+    float* ws;              // [slot][chunk][wave][DB * 4][lane][4] accumulators, then [slot][chunk][wave][lane][2]
+    uint32_t* ws_cnt;       // [slot] chunks arrived; zero between calls
+    int ws_slots;           // units * ntg
 };
 
 constexpr uint32_t kOob = 0x80000000u;  // a buffer offset past every pool: loads return 0
@@ -394,13 +404,14 @@ __device__ __forceinline__ void convert_fp8(int wave, int lane, const lds_char_t
 // 2 = fp8 (E4M3 + per-row scale) page pools, 3 = token-major rows with fp8
 // score operands (K as E4M3 codes with power-of-two row scales, Q quantised
 // here; V bf16).
-template <int HD, int PAGED, bool WIN>
+template <int HD, int PAGED, bool WIN, bool SPLIT = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(Params p) {
     using C = Cfg<HD>;
     constexpr bool kPaged = PAGED == 1 || PAGED == 2;
     constexpr bool kF8S = PAGED == 3;
     static_assert(!kF8S || HD == 128, "fp8 score operands: two 64-wide head_dim slices");
+    static_assert(!SPLIT || (PAGED == 0 && !WIN), "split key ranges: plain causal kernels");
     extern __shared__ __align__(16) uint16_t smem[];
     lds_char_t* lds = (lds_char_t*)smem;
     const int tid = threadIdx.x;
@@ -438,11 +449,69 @@ void attn_fwd_kernel(Params p) {
     // of the XCD's units before its k-th (tab[per_xcd]: all of them); a unit's
     // non-empty ranks are its last ones.
     __attribute__((address_space(3))) int32_t* tab = (__attribute__((address_space(3))) int32_t*)(lds + p.tab_off);
-    __attribute__((address_space(3))) int32_t* slot_to_seq = tab + (p.units / kNumXcd + 1);
+    // (split: tab[0 .. 63] is the XCD's sorted entry list, tab[64] its length,
+    // then the slot -> sequence table and one broadcast word)
+    __attribute__((address_space(3))) int32_t* slot_to_seq = tab + (SPLIT ? 65 : p.units / kNumXcd + 1);
+    [[maybe_unused]] __attribute__((address_space(3))) int32_t* bcast = tab + 129;
     const int xcd = blockIdx.x % kNumXcd, lp = blockIdx.x / kNumXcd, per = gridDim.x / kNumXcd;
     const int per_xcd = p.units / kNumXcd;
     int ncomp = 0;
-    if (p.persist) {
+    if constexpr (SPLIT) {
+        // The XCD's entries: every task group of its units once, a split one
+        // as its two chunks (weight = kv tiles), sorted heaviest first and
+        // taken in snake order.  Lane i is task group i % ntg of the XCD's unit
+        // i / ntg (the host keeps per_xcd * ntg <= 64).  Key: weight << 23 |
+        // unit index << 16 | task group << 2 | chunk (0 whole, 1 first, 2 second).
+        if (ranked && lane < p.num_seqs && wave == 0) slot_to_seq[rank_i] = lane;
+        __syncthreads();
+        if (wave == 0) {
+            const int k = lane / p.ntg, t = lane % p.ntg;
+            int key0 = 0, key1 = 0, cnt = 0;
+            if (k < per_xcd) {
+                const int slot = (k * kNumXcd + xcd) / p.n_kv;
+                const int seq = ranked ? slot_to_seq[slot] : slot;
+                const int64_t len = p.cu != nullptr ? seq_len(seq) : p.total;
+                const int ntasks_u = (int)(p.group * ((len + BQ - 1) / BQ));
+                if (t * kWaves < ntasks_u) {
+                    const int last = min(t * kWaves + kWaves - 1, ntasks_u - 1);
+                    const int nt = (int)((min<int64_t>(len, (int64_t)(last / p.group + 1) * BQ) + BK - 1) / BK);
+                    if (nt > p.split_t) {
+                        const int h = nt / 2;
+                        key0 = ((nt - h) << 23) | (k << 16) | (t << 2) | 2;
+                        key1 = (h << 23) | (k << 16) | (t << 2) | 1;
+                        cnt = 2;
+                    } else {
+                        key0 = (nt << 23) | (k << 16) | (t << 2);
+                        cnt = 1;
+                    }
+                }
+            }
+            int inc = cnt;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int up = __shfl_up(inc, d, 64);
+                if (lane >= d) inc += up;
+            }
+            const int total = __shfl(inc, 63, 64);
+            // (the host keeps the entries of an XCD within 64)
+            if (cnt >= 1) tab[inc - cnt] = key0;
+            if (cnt == 2) tab[inc - 1] = key1;
+            int v = lane < total ? tab[lane] : 0;
+            // bitonic sort, descending, one key per lane
+#pragma unroll
+            for (int size = 2; size <= 64; size <<= 1)
+#pragma unroll
+                for (int stride = size / 2; stride > 0; stride >>= 1) {
+                    const int o = __shfl_xor(v, stride, 64);
+                    const bool keep_max = ((lane & size) == 0) == ((lane & stride) == 0);
+                    v = keep_max ? max(v, o) : min(v, o);
+                }
+            tab[lane] = v;
+            if (lane == 0) tab[64] = total;
+        }
+        __syncthreads();
+        ncomp = __builtin_amdgcn_readfirstlane(tab[64]);
+    } else if (p.persist) {
         if (ranked && lane < p.num_seqs && wave == 0) slot_to_seq[rank_i] = lane;
         __syncthreads();
         if (wave == 0) {
@@ -476,7 +545,15 @@ void attn_fwd_kernel(Params p) {
     for (int pass = 0;; ++pass) {
     // ---- workgroup -> (unit = (sequence, kv head), task group), heaviest first
     int unit, rank;
-    if (p.persist) {
+    [[maybe_unused]] int chunk = 0;                              // split: 0 whole, 1 first, 2 second
+    if constexpr (SPLIT) {
+        const int c = pass * per + ((pass & 1) ? per - 1 - lp : lp);
+        if (c >= ncomp) break;                                   // uniform per workgroup
+        const int key = __builtin_amdgcn_readfirstlane(tab[c]);
+        unit = ((key >> 16) & 127) * kNumXcd + xcd;
+        rank = p.ntg - 1 - ((key >> 2) & 16383);
+        chunk = key & 3;
+    } else if (p.persist) {
         const int c = pass * per + ((pass & 1) ? per - 1 - lp : lp);
         if (c >= ncomp) break;                                   // uniform per workgroup
         // the unit holding entry c: the largest k with tab[k] <= c
@@ -701,15 +778,26 @@ void attn_fwd_kernel(Params p) {
         const int q0 = qblk * BQ;                                  // first query row (in sequence)
         const int last_task = min(tg * kWaves + kWaves - 1, ntasks - 1);
         const int kv_end = pos0 + min(Lb, (last_task / G + 1) * BQ);
-        const int ntiles = (kv_end + BK - 1) / BK;                 // tiles the workgroup visits
+        int ntiles = (kv_end + BK - 1) / BK;                       // tiles the workgroup visits
         const int wave_last_q = pos0 + min(q0 + BQ, Lb) - 1;       // key position of the wave's last query
-        const int wave_ntiles = active ? wave_last_q / BK + 1 : 0; // tiles this wave computes
+        int wave_ntiles = active ? wave_last_q / BK + 1 : 0;       // tiles this wave computes
         // sliding window: the first tile holding a key that the wave's (the
         // workgroup's) first row sees; tiles before it are skipped
         int wave_first = 0, j0 = 0;
         if constexpr (WIN) {
             wave_first = max(0, pos0 + q0 - p.window + 1) / BK;
             j0 = __builtin_amdgcn_readfirstlane(max(0, pos0 + (tg * kWaves / G) * BQ - p.window + 1) / BK);
+        }
+        // split: the chunk's tiles (a wave may have none in the second chunk)
+        if constexpr (SPLIT) {
+            const int hsplit = ntiles / 2;
+            if (chunk == 1) {
+                ntiles = hsplit;
+                wave_ntiles = min(wave_ntiles, hsplit);
+            } else if (chunk == 2) {
+                j0 = hsplit;
+                wave_first = hsplit;
+            }
         }
 
         f32x16_t oacc[C::DB];
@@ -1031,6 +1119,83 @@ void attn_fwd_kernel(Params p) {
         }
         if (lead) wg_barrier();
 
+        // ---- split chunk: the chunk stores its partial -- accumulators
+        // relative to its reference R, R, and the lane's half-row sum -- and
+        // counts its arrival.  The chunk that arrives second merges the two in
+        // chunk order (so the result does not depend on which came first) and
+        // goes on to the epilogue; the first skips the epilogue's stores.  A
+        // row with no visible key in a chunk (sum 0) takes no weight from it.
+        [[maybe_unused]] bool write_o = true;
+        if constexpr (SPLIT) {
+            if (chunk != 0) {
+                // The partials go past the caches (sc0 sc1: written through to
+                // memory, read from it), so the count needs only this wave's
+                // stores to have completed, not a cache write-back: a fence
+                // at device scope wrote back each XCD's whole L2 and cost more
+                // than the split saved.
+                constexpr int kCoherent = 1 | 16;
+                const int slot = unit * p.ntg + tg;
+                constexpr uint32_t kAccW = (uint32_t)C::DB * 4 * 64 * 4;    // floats per wave
+                const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.ws, (uint32_t)p.ws_slots * 2u * kWaves * (kAccW + 128u) * 4u);
+                auto acc_off = [&](int ci) __attribute__((always_inline)) {
+                    return ((((uint32_t)slot * 2u + ci) * kWaves + wave) * kAccW + (uint32_t)lane * 4u) * 4u;
+                };
+                auto rl_off = [&](int ci) __attribute__((always_inline)) {
+                    return ((uint32_t)p.ws_slots * 2u * kWaves * kAccW + (((uint32_t)slot * 2u + ci) * kWaves + wave) * 128u +
+                            (uint32_t)lane * 2u) * 4u;
+                };
+                const uint32_t mine = acc_off(chunk - 1);
+#pragma unroll
+                for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        // (whole vectors are bit-cast: a bit-cast of one vector
+                        // element read element 0)
+                        const u32x4_t w4 = __builtin_bit_cast(
+                            u32x4_t, f32x4_t{oacc[db][q4 * 4], oacc[db][q4 * 4 + 1], oacc[db][q4 * 4 + 2], oacc[db][q4 * 4 + 3]});
+                        __builtin_amdgcn_raw_buffer_store_b128(w4, wr, mine + (uint32_t)((db * 4 + q4) * 64 * 16), 0, kCoherent);
+                    }
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, f32x2_t{R, l_run}),
+                                                      wr, rl_off(chunk - 1), 0, kCoherent);
+                __builtin_amdgcn_s_waitcnt(kVmcnt0);   // this wave's partial is in memory
+                __syncthreads();
+                if (tid == 0) bcast[0] = (int)atomicAdd(&p.ws_cnt[slot], 1u);
+                __syncthreads();
+                write_o = __builtin_amdgcn_readfirstlane(bcast[0]) != 0;
+                if (write_o) {
+                    const uint32_t theirs = acc_off(2 - chunk);
+                    const u32x2_t orl = __builtin_amdgcn_raw_buffer_load_b64(wr, rl_off(2 - chunk), 0, kCoherent);
+                    // chunk 1's values first, then chunk 2's
+                    const f32x2_t orf = __builtin_bit_cast(f32x2_t, orl);
+                    const float oR = orf[0], oh = orf[1];
+                    const float R1 = chunk == 1 ? R : oR, R2 = chunk == 1 ? oR : R;
+                    const float h1 = chunk == 1 ? l_run : oh, h2 = chunk == 1 ? oh : l_run;
+                    float a1, b1, a2, b2;
+                    both_halves(h1, a1, b1);
+                    both_halves(h2, a2, b2);
+                    const bool v1 = a1 + b1 > 0.0f, v2 = a2 + b2 > 0.0f;
+                    const float Rm = v1 && v2 ? __builtin_fmaxf(R1, R2) : (v1 ? R1 : R2);
+                    const float w1 = v1 ? fast_exp2(R1 - Rm) : 0.0f, w2 = v2 ? fast_exp2(R2 - Rm) : 0.0f;
+                    l_run = h1 * w1 + h2 * w2;
+#pragma unroll
+                    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+                        for (int q4 = 0; q4 < 4; ++q4) {
+                            const u32x4_t ov = __builtin_amdgcn_raw_buffer_load_b128(wr, theirs + (uint32_t)((db * 4 + q4) * 64 * 16), 0, kCoherent);
+                            const f32x4_t ovf = __builtin_bit_cast(f32x4_t, ov);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const float m = oacc[db][q4 * 4 + e], o = ovf[e];
+                                const float o1 = chunk == 1 ? m : o, o2 = chunk == 1 ? o : m;
+                                oacc[db][q4 * 4 + e] = o1 * w1 + o2 * w2;
+                            }
+                        }
+                    // both chunks have arrived: ready for the next call
+                    if (tid == 0) __hip_atomic_store(&p.ws_cnt[slot], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+        }
+
         // ---- epilogue: O / l, bf16 RNE.  Each wave stages its 32 rows in its
         // eighth of the (now free) K/V buffers, 16-byte chunks XOR-swizzled by
         // row, and writes them back as whole head rows, 16 bytes per lane,
@@ -1044,7 +1209,7 @@ void attn_fwd_kernel(Params p) {
             // being hoisted out of the item loop and held in registers throughout
             int sw = r32 & (C::NC - 1), rl = lane / C::NC;
             asm volatile("" : "+v"(sw), "+v"(rl));
-            if (active) {
+            if (active && write_o) {
                 float l_lo, l_hi;
                 both_halves(l_run, l_lo, l_hi);
                 const float inv = 1.0f / (l_lo + l_hi);
@@ -1141,6 +1306,57 @@ hipError_t launch_cfg(const AttnArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Split key ranges (shallow grids): at most one task group per workgroup
+// slot, the units spread evenly over the XCDs, at least 8 kv tiles.  Task
+// groups with more than three quarters of the longest sequence's kv tiles
+// run as two chunks.  Every item costs a fixed ~10 us here (first tiles in
+// flight, pipeline fill and drain, epilogue) on top of its tiles, so only
+// the heaviest task groups pay for being split: a quarter or a half split
+// more of them and ran slower than no split.  Otherwise, and for deeper
+// grids, the plain kernel runs.
+static_assert(BQ == 32 && kWaves == 8, "the split workspace layout of pca_internal.hpp");
+
+template <int HD>
+hipError_t launch_split(const AttnArgs& a, hipStream_t s) {
+    using C = Cfg<HD>;
+    const int G = a.n_head / a.n_kv_head;
+    const int ntg = (G * ((a.max_seqlen + BQ - 1) / BQ) + kWaves - 1) / kWaves;
+    const int64_t units = (int64_t)a.num_seqs * a.n_kv_head;
+    const int ncu = device_cus();
+    const int nwg = ncu >= kNumXcd ? (ncu / kNumXcd) * kNumXcd : 0;
+    const int max_nt = (a.max_seqlen + BK - 1) / BK;
+    const bool use = nwg > 0 && units % kNumXcd == 0 && units * ntg <= nwg && units * ntg <= kSplitMaxSlots &&
+                     (units / kNumXcd) * ntg <= 32 && max_nt >= 8;
+    if (!use) return launch_cfg<HD, 0, false>(a, s);
+    static const hipError_t attr = hipFuncSetAttribute((const void*)attn_fwd_kernel<HD, 0, false, true>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+    if (attr != hipSuccess) return attr;
+    Params p;
+    memset(&p, 0, sizeof(p));
+    p.q = a.q; p.k = a.k; p.v = a.v;
+    p.ldq = a.ldq; p.ldk = a.ldk; p.ldv = a.ldv;
+    p.cu = a.cu_seqlens;
+    p.num_seqs = a.num_seqs;
+    p.total = a.total_tokens;
+    p.n_kv = a.n_kv_head;
+    p.group = G;
+    p.c = a.scale * 1.4426950408889634f;
+    p.o = a.o;
+    p.ldo = a.ldo;
+    p.units = (int)units;
+    p.pair = 0;
+    p.ntg = ntg;
+    p.split_t = max(4, max_nt * 3 / 4);
+    p.ws_cnt = (uint32_t*)a.split_ws;
+    p.ws = (float*)((char*)a.split_ws + kSplitCounterBytes);
+    p.ws_slots = (int)(units * ntg);
+    p.persist = 1;
+    p.tab_off = (C::LDS_BYTES + 15) & ~15;
+    const size_t lds = (size_t)p.tab_off + 130 * 4;     // entry list, its length, slot -> sequence, broadcast
+    hipLaunchKernelGGL((attn_fwd_kernel<HD, 0, false, true>), dim3((uint32_t)nwg), dim3(kThreads), lds, s, p);
+    return hipGetLastError();
+}
+
 template <int PAGED, bool WIN>
 hipError_t launch_hd(const AttnArgs& a, hipStream_t s) {
     switch (a.head_dim) {
@@ -1154,6 +1370,14 @@ hipError_t launch_hd(const AttnArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
+    if (a.split_ws != nullptr && a.k8 == nullptr && a.block_table == nullptr && a.window == 0) {
+        switch (a.head_dim) {
+            case 32: return launch_split<32>(a, s);
+            case 64: return launch_split<64>(a, s);
+            case 128: return launch_split<128>(a, s);
+            default: return hipErrorInvalidValue;
+        }
+    }
     if (a.k8 != nullptr) return a.head_dim == 128 ? launch_cfg<128, 3, false>(a, s) : hipErrorInvalidValue;
     if (a.block_table != nullptr) return a.k_scale != nullptr ? launch_hd<2, false>(a, s) : launch_hd<1, false>(a, s);
     return a.window > 0 ? launch_hd<0, true>(a, s) : launch_hd<0, false>(a, s);

@@ -342,12 +342,14 @@ pca_status pca_prefill_attention(const pca_bf16* q, const pca_bf16* k, const pca
                                         n_head, n_kv_head, head_dim, scale, causal, 0, o, ldo, stream);
 }
 
-pca_status pca_prefill_attention_window(const pca_bf16* q, const pca_bf16* k, const pca_bf16* v,
-                                        int64_t ldq, int64_t ldk, int64_t ldv,
-                                        const int32_t* cu_seqlens, int num_seqs, int max_seqlen,
-                                        int64_t total_tokens, int n_head, int n_kv_head, int head_dim,
-                                        float scale, int causal, int window, pca_bf16* o, int64_t ldo,
-                                        void* stream) {
+namespace {
+// the token-major attention calls: plain, sliding window, split key ranges
+pca_status prefill_attention_impl(const pca_bf16* q, const pca_bf16* k, const pca_bf16* v,
+                                  int64_t ldq, int64_t ldk, int64_t ldv,
+                                  const int32_t* cu_seqlens, int num_seqs, int max_seqlen,
+                                  int64_t total_tokens, int n_head, int n_kv_head, int head_dim,
+                                  float scale, int causal, int window, void* split_ws, int64_t split_ws_bytes,
+                                  pca_bf16* o, int64_t ldo, void* stream) {
     if (window < 0) return fail(PCA_ERR_INVALID_ARG, "window must be >= 0 (0: no window), got %d", window);
     if (total_tokens == 0 && num_seqs >= 1 && causal == 1) return ok();   // empty batch: nothing to read or write
     if (!q || !k || !v || !o) return fail(PCA_ERR_INVALID_ARG, "null q, k, v or o");
@@ -381,7 +383,50 @@ pca_status pca_prefill_attention_window(const pca_bf16* q, const pca_bf16* k, co
     a.total_tokens = total_tokens; a.n_head = n_head; a.n_kv_head = n_kv_head; a.head_dim = head_dim;
     a.scale = scale; a.o = o; a.ldo = ldo;
     a.window = window;
+    if (split_ws_bytes >= 0) {
+        if (!split_ws) return fail(PCA_ERR_INVALID_ARG, "null workspace");
+        if ((uintptr_t)split_ws & 255u) return fail(PCA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+        const int64_t need = pca::attention_split_workspace(num_seqs, max_seqlen, n_head, n_kv_head, head_dim);
+        if (split_ws_bytes < need)
+            return fail(PCA_ERR_INVALID_ARG, "workspace of %lld bytes, %lld needed", (long long)split_ws_bytes,
+                        (long long)need);
+        a.split_ws = split_ws;
+    }
     return hip_status(pca::launch_attention(a, (hipStream_t)stream), "prefill_attention launch");
+}
+}  // namespace
+
+pca_status pca_prefill_attention_window(const pca_bf16* q, const pca_bf16* k, const pca_bf16* v,
+                                        int64_t ldq, int64_t ldk, int64_t ldv,
+                                        const int32_t* cu_seqlens, int num_seqs, int max_seqlen,
+                                        int64_t total_tokens, int n_head, int n_kv_head, int head_dim,
+                                        float scale, int causal, int window, pca_bf16* o, int64_t ldo,
+                                        void* stream) {
+    return prefill_attention_impl(q, k, v, ldq, ldk, ldv, cu_seqlens, num_seqs, max_seqlen, total_tokens, n_head,
+                                  n_kv_head, head_dim, scale, causal, window, nullptr, -1, o, ldo, stream);
+}
+
+int64_t pca_prefill_attention_splitkv_workspace(int num_seqs, int max_seqlen, int n_head, int n_kv_head,
+                                                int head_dim) {
+    if (num_seqs < 1 || max_seqlen < 1 || n_head <= 0 || n_kv_head <= 0 || n_head % n_kv_head != 0 ||
+        !supported_head_dim(head_dim)) {
+        fail(PCA_ERR_INVALID_ARG, "need num_seqs, max_seqlen >= 1, n_head %% n_kv_head == 0 and head_dim "
+             "32, 64 or 128 (%d, %d, %d, %d, %d)", num_seqs, max_seqlen, n_head, n_kv_head, head_dim);
+        return -1;
+    }
+    return pca::attention_split_workspace(num_seqs, max_seqlen, n_head, n_kv_head, head_dim);
+}
+
+pca_status pca_prefill_attention_splitkv(const pca_bf16* q, const pca_bf16* k, const pca_bf16* v,
+                                         int64_t ldq, int64_t ldk, int64_t ldv,
+                                         const int32_t* cu_seqlens, int num_seqs, int max_seqlen,
+                                         int64_t total_tokens, int n_head, int n_kv_head, int head_dim,
+                                         float scale, int causal, pca_bf16* o, int64_t ldo,
+                                         void* workspace, int64_t workspace_bytes, void* stream) {
+    if (workspace_bytes < 0) return fail(PCA_ERR_INVALID_ARG, "workspace_bytes must be >= 0");
+    return prefill_attention_impl(q, k, v, ldq, ldk, ldv, cu_seqlens, num_seqs, max_seqlen, total_tokens, n_head,
+                                  n_kv_head, head_dim, scale, causal, 0, workspace, workspace_bytes, o, ldo,
+                                  stream);
 }
 
 pca_status pca_prefill_attention_fp8qk(const pca_bf16* q, int64_t ldq, const uint8_t* k_codes, int64_t ldk,

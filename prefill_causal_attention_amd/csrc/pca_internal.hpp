@@ -109,9 +109,32 @@ struct AttnArgs {
     int64_t ldk8;
     const uint8_t* kex;
     int64_t ldke;
+    // split key ranges for shallow grids: a zeroed-once workspace of at least
+    // attention_split_workspace(...) bytes (null: never split)
+    void* split_ws;
 };
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+
+// Split-key-range workspace.  One slot per task group (8 waves of 32 query
+// rows that share a kv head), at most kSplitMaxSlots of them when the split
+// runs: first the slots' 4-byte arrival counters, in a block of fixed size
+// (so calls of different sizes on one workspace never write partial results
+// where another size keeps counters), then per slot two chunks' partials of
+// 8 waves x 64 lanes x (head_dim / 2 accumulators + reference + half-row sum)
+// fp32.
+constexpr int64_t kSplitMaxSlots = 1024;
+constexpr int64_t kSplitCounterBytes = kSplitMaxSlots * 4;
+inline int64_t attention_split_slots(int num_seqs, int max_seqlen, int n_head, int n_kv_head) {
+    const int64_t G = n_head / n_kv_head;
+    const int64_t ntg = (G * ((max_seqlen + 31) / 32) + 7) / 8;
+    return (int64_t)num_seqs * n_kv_head * ntg;
+}
+inline int64_t attention_split_workspace(int num_seqs, int max_seqlen, int n_head, int n_kv_head, int head_dim) {
+    int64_t slots = attention_split_slots(num_seqs, max_seqlen, n_head, n_kv_head);
+    if (slots > kSplitMaxSlots) slots = kSplitMaxSlots;   // more never split
+    return kSplitCounterBytes + slots * 2 * 8 * 64 * (head_dim / 2 + 2) * 4;
+}
 
 // Compute units of the current device (looked up once per device; 0 if
 // unknown).  Grids deeper than one workgroup per CU launch one per CU and

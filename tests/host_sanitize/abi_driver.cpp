@@ -139,6 +139,30 @@ static void attention_checks() {
     CALL(PCA_OK, 1, pca_prefill_attention_window(B(A1), B(A2), B(A3), 6144, 6144, 6144, cu, 16, 4096, 27808, 32, 8, 128,
                                                  0.088f, 1, 1024, B(A4), 4096, nullptr));
     EXPECT(pca::g_attn.window == 1024 && pca::g_attn.num_seqs == 16, "window args");
+    // split key ranges: the workspace is checked before any launch
+    const int64_t wsb = pca_prefill_attention_splitkv_workspace(1, 2048, 32, 32, 128);
+    EXPECT(wsb == 4096 + 256LL * 2 * 8 * 64 * 66 * 4, "split workspace bytes %lld", (long long)wsb);
+    EXPECT(pca_prefill_attention_splitkv_workspace(1, 2048, 32, 7, 128) == -1 && pca_last_error()[0] != '\0',
+           "split workspace of invalid sizes");
+    EXPECT(pca_prefill_attention_splitkv_workspace(0, 2048, 32, 8, 128) == -1, "split workspace, no sequences");
+    CALL(PCA_OK, 1, pca_prefill_attention_splitkv(B(A1), B(A2), B(A3), 12288, 12288, 12288, nullptr, 1, 2048, 2048, 32,
+                                                  32, 128, 0.088f, 1, B(A4), 4096, (void*)0x10000000, wsb, nullptr));
+    EXPECT(pca::g_attn.split_ws == (void*)0x10000000 && pca::g_attn.window == 0, "split args");
+    CALL(PCA_ERR_INVALID_ARG, 0, pca_prefill_attention_splitkv(B(A1), B(A2), B(A3), 12288, 12288, 12288, nullptr, 1,
+                                                               2048, 2048, 32, 32, 128, 0.088f, 1, B(A4), 4096,
+                                                               nullptr, wsb, nullptr));
+    CALL(PCA_ERR_INVALID_ARG, 0, pca_prefill_attention_splitkv(B(A1), B(A2), B(A3), 12288, 12288, 12288, nullptr, 1,
+                                                               2048, 2048, 32, 32, 128, 0.088f, 1, B(A4), 4096,
+                                                               (void*)0x10000080, wsb, nullptr));
+    CALL(PCA_ERR_INVALID_ARG, 0, pca_prefill_attention_splitkv(B(A1), B(A2), B(A3), 12288, 12288, 12288, nullptr, 1,
+                                                               2048, 2048, 32, 32, 128, 0.088f, 1, B(A4), 4096,
+                                                               (void*)0x10000000, wsb - 1, nullptr));
+    CALL(PCA_ERR_INVALID_ARG, 0, pca_prefill_attention_splitkv(B(A1), B(A2), B(A3), 12288, 12288, 12288, nullptr, 1,
+                                                               2048, 2048, 32, 32, 128, 0.088f, 1, B(A4), 4096,
+                                                               (void*)0x10000000, -1, nullptr));
+    CALL(PCA_OK, 1, pca_prefill_attention(B(A1), B(A2), B(A3), 6144, 6144, 6144, nullptr, 1, 8192, 8192, 32, 8, 128,
+                                          0.088f, 1, B(A4), 4096, nullptr));
+    EXPECT(pca::g_attn.split_ws == nullptr, "plain attention: no split workspace");
     CALL(PCA_OK, 0, pca_prefill_attention(nullptr, nullptr, nullptr, 64, 64, 64, nullptr, 1, 0, 0, 1, 1, 64, 0.1f, 1,
                                           nullptr, 64, nullptr));
     CALL(PCA_ERR_INVALID_ARG, 0, pca_prefill_attention(B(A1), B(A2), B(A3), 6144, 6144, 6144, nullptr, 1, INT_MAX,

@@ -20,7 +20,7 @@ MISALIGNED = 0x10008
 
 def _declared():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:pca_status|const char\*)\s+(pca_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:pca_status|const char\*|int64_t)\s+(pca_\w+)\s*\(", text, re.M)))
 
 
 def test_library_loads_and_exports_header_symbols():
