@@ -332,6 +332,28 @@ def main():
             "flop_count": "exact causal pairs, 4*hd*n_head per (query, visible key)"}
         del pk, pv, pq, po
 
+        # split key ranges on shallow grids: one 2048-token sequence (MHA and
+        # GQA, hd 128), one pass against the split entry point
+        split = {}
+        for sH, sHk in ((32, 32), (32, 8)):
+            sS, shd = 2048, 128
+            gen.manual_seed(9005)
+            sq = torch.randn((sS, sH * shd), generator=gen, device=dev).to(torch.bfloat16)
+            skv = torch.randn((sS, 2 * sHk * shd), generator=gen, device=dev).to(torch.bfloat16)
+            sk, sv = skv[:, :sHk * shd], skv[:, sHk * shd:]
+            so = torch.empty_like(sq)
+            sws = torch.zeros(pca.prefill_attention_splitkv_workspace(1, sS, sH, sHk, shd), dtype=torch.uint8,
+                              device=dev)
+            t_one = timed(lambda: pca.prefill_attention(sq, sk, sv, so, sH, sHk, shd), args.extra_reps * 5)
+            t_spl = timed(lambda: pca.prefill_attention_splitkv(sq, sk, sv, so, sws, sH, sHk, shd),
+                          args.extra_reps * 5)
+            sflop = 2.0 * 2.0 * sS * sS * shd * sH / 2
+            split[f"s2048_h{sH}_kv{sHk}"] = {"one_pass_ms": t_one, "split_ms": t_spl,
+                                             "tflops_one_pass": sflop / (t_one * 1e-3) / 1e12,
+                                             "tflops_split": sflop / (t_spl * 1e-3) / 1e12}
+            del sq, skv, sk, sv, so, sws
+        extras["prefill_attention_splitkv"] = split
+
         # the two ends of the attention unit: RMSNorm folded into the QKV GEMM
         # (row statistics + scaled epilogue), and W_o with the residual add
         inv_rms = torch.empty((T,), dtype=torch.float32, device=dev)
@@ -478,7 +500,7 @@ def main():
     }
     traffic = measured_traffic(w.name)
     roofline = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": tflops / PEAK_BF16_TFLOPS, "traffic": traffic, "kernel": f"attn_fwd_kernel<{w.head_dim}, 0, false>",
+                "frac": tflops / PEAK_BF16_TFLOPS, "traffic": traffic, "kernel": f"attn_fwd_kernel<{w.head_dim}, 0, false, false>",
                 "flop_per_launch": att_flops, "avg_launch_ms": a_ms,
                 "traffic_source": (f"profiles/attn_fwd_{w.name}_traffic.json: rocprofv3 --pmc FETCH_SIZE and "
                                    "WRITE_SIZE of this kernel source (sha-matched), scaled by a plain 1 GiB copy; "
