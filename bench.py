@@ -45,8 +45,12 @@ def parse():
     ap.add_argument("--kv-cold-reps", type=int, default=20)
     ap.add_argument("--extra-reps", type=int, default=20,
                     help="reps of the extra measurements (fused GEMM + KV write, paged chunk attention); 0 skips")
+    ap.add_argument("--split-reps", type=int, default=100,
+                    help="reps of the split-key-range side measurement (s=2048, one pass against split); 0 skips")
     ap.add_argument("--clock-seconds", type=float, default=0.3,
                     help="seconds of back-to-back attention launches while the GPU clocks are sampled; 0 skips")
+    ap.add_argument("--splitkv-only", action="store_true",
+                    help="only run the split-key-range side measurement (--split-reps launches of each kernel)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (to scale HBM byte counters)")
     return ap.parse_args()
@@ -152,6 +156,42 @@ def cpu_baseline(w, target_s):
                       f"causal FLOPs of those rows / {dt:.1f} s; BLAS threads={threads}, host cpus={os.cpu_count()}"}
 
 
+def splitkv_side(pca, torch, dev, reps):
+    """One 2048-token sequence, hd 128, MHA (32/32) then GQA (32/8): the
+    one-pass attention kernel against the split entry point, each `reps`
+    launches after 3 untimed ones, HIP events on the current stream."""
+    stream = torch.cuda.current_stream()
+    gen = torch.Generator(device=dev)
+    out = {}
+    for H, Hk in ((32, 32), (32, 8)):
+        S, hd = 2048, 128
+        gen.manual_seed(9005)
+        q = torch.randn((S, H * hd), generator=gen, device=dev).to(torch.bfloat16)
+        kv = torch.randn((S, 2 * Hk * hd), generator=gen, device=dev).to(torch.bfloat16)
+        k, v = kv[:, :Hk * hd], kv[:, Hk * hd:]
+        o = torch.empty_like(q)
+        ws = torch.zeros(pca.prefill_attention_splitkv_workspace(1, S, H, Hk, hd), dtype=torch.uint8, device=dev)
+        times = []
+        for fn in (lambda: pca.prefill_attention(q, k, v, o, H, Hk, hd),
+                   lambda: pca.prefill_attention_splitkv(q, k, v, o, ws, H, Hk, hd)):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) / reps)
+        flop = 2.0 * 2.0 * S * S * hd * H / 2
+        out[f"s2048_h{H}_kv{Hk}"] = {"one_pass_ms": times[0], "split_ms": times[1],
+                                     "tflops_one_pass": flop / (times[0] * 1e-3) / 1e12,
+                                     "tflops_split": flop / (times[1] * 1e-3) / 1e12}
+        del q, kv, k, v, o, ws
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -175,6 +215,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": 1 << 30, "copy_bytes_written": 1 << 30, "reps": 5}), flush=True)
+        return
+    if args.splitkv_only:
+        print(json.dumps({"prefill_attention_splitkv": splitkv_side(pca, torch, torch.device("cuda:0"),
+                                                                   max(1, args.split_reps))}), flush=True)
         return
     w = workloads.BY_NAME[args.workload]
     dev = torch.device("cuda:0")
@@ -332,27 +376,8 @@ def main():
             "flop_count": "exact causal pairs, 4*hd*n_head per (query, visible key)"}
         del pk, pv, pq, po
 
-        # split key ranges on shallow grids: one 2048-token sequence (MHA and
-        # GQA, hd 128), one pass against the split entry point
-        split = {}
-        for sH, sHk in ((32, 32), (32, 8)):
-            sS, shd = 2048, 128
-            gen.manual_seed(9005)
-            sq = torch.randn((sS, sH * shd), generator=gen, device=dev).to(torch.bfloat16)
-            skv = torch.randn((sS, 2 * sHk * shd), generator=gen, device=dev).to(torch.bfloat16)
-            sk, sv = skv[:, :sHk * shd], skv[:, sHk * shd:]
-            so = torch.empty_like(sq)
-            sws = torch.zeros(pca.prefill_attention_splitkv_workspace(1, sS, sH, sHk, shd), dtype=torch.uint8,
-                              device=dev)
-            t_one = timed(lambda: pca.prefill_attention(sq, sk, sv, so, sH, sHk, shd), args.extra_reps * 5)
-            t_spl = timed(lambda: pca.prefill_attention_splitkv(sq, sk, sv, so, sws, sH, sHk, shd),
-                          args.extra_reps * 5)
-            sflop = 2.0 * 2.0 * sS * sS * shd * sH / 2
-            split[f"s2048_h{sH}_kv{sHk}"] = {"one_pass_ms": t_one, "split_ms": t_spl,
-                                             "tflops_one_pass": sflop / (t_one * 1e-3) / 1e12,
-                                             "tflops_split": sflop / (t_spl * 1e-3) / 1e12}
-            del sq, skv, sk, sv, so, sws
-        extras["prefill_attention_splitkv"] = split
+        if args.split_reps > 0:
+            extras["prefill_attention_splitkv"] = splitkv_side(pca, torch, dev, args.split_reps)
 
         # the two ends of the attention unit: RMSNorm folded into the QKV GEMM
         # (row statistics + scaled epilogue), and W_o with the residual add
