@@ -73,6 +73,40 @@ def test_window_attention_validation():
     _expect("pca_prefill_attention_window", WIN_BASE, WIN_ORDER, bad, {"scale": C})
 
 
+SPLIT_ORDER = WIN_ORDER[:15] + ["o", "ldo", "ws", "wsb"]
+
+
+def _split_ws(ns, mx, nh, nkv, hd):
+    return pca.load().pca_prefill_attention_splitkv_workspace(ns, mx, nh, nkv, hd)
+
+
+def test_splitkv_workspace_size():
+    """4 KiB of counters, then two chunks x 8 waves x 64 lanes x (hd/2 + 2)
+    floats per task-group slot, slots = sequences x kv heads x
+    ceil(G * ceil(L / 32) / 8), at most 1024."""
+    def want(ns, mx, nh, nkv, hd):
+        g = nh // nkv
+        slots = min(1024, ns * nkv * -(-(g * -(-mx // 32)) // 8))
+        return 4096 + slots * 2 * 8 * 64 * (hd // 2 + 2) * 4
+    for args in [(1, 2048, 32, 32, 128), (1, 2048, 32, 8, 128), (3, 500, 16, 8, 128), (1, 600, 8, 8, 64),
+                 (1, 777, 8, 8, 32), (1, 1, 2, 1, 32), (1, 8192, 32, 8, 128), (1, 32768, 40, 8, 128)]:
+        assert _split_ws(*args) == want(*args), args
+    assert _split_ws(1, 2048, 32, 32, 128) == 4096 + 256 * 270336         # 264 KiB per slot at hd 128
+    assert _split_ws(1, 32768, 40, 8, 128) == 4096 + 1024 * 270336         # capped: never split
+    for bad in [(0, 2048, 32, 8, 128), (1, 0, 32, 8, 128), (1, 2048, 30, 8, 128), (1, 2048, 32, 8, 96),
+                (1, 2048, 0, 8, 128), (1, 2048, 32, 0, 128)]:
+        assert _split_ws(*bad) == -1 and pca.load().pca_last_error(), bad
+
+
+def test_splitkv_validation():
+    need = _split_ws(1, 64, 32, 8, 128)
+    base = dict(WIN_BASE, ws=FAKE, wsb=need)
+    bad = {("ws", None): 1, ("ws", FAKE + 64): 1, ("wsb", need - 1): 1, ("wsb", -1): 1, ("wsb", 0): 1,
+           ("q", 0): 1, ("causal", 0): 1, ("nkv", 5): 1, ("hd", 48): 2, ("mx", 10): 1, ("ns", 0): 1,
+           ("scale", float("nan")): 1}
+    _expect("pca_prefill_attention_splitkv", base, SPLIT_ORDER, bad, {"scale": C})
+
+
 GEMM_ORDER = ["x", "ldx", "w", "ldw", "y", "ldy", "M", "N", "K"]
 GEMM_BAD = {("x", 0): 1, ("w", 0): 1, ("y", 0): 1, ("x", MISALIGNED): 1, ("M", 0): 1, ("N", 0): 1, ("K", 4): 1,
             ("K", 68): 1, ("ldx", 32): 1, ("ldw", 60): 1, ("ldy", 100): 1, ("M", 1 << 31): 1,
