@@ -47,8 +47,9 @@ def parse():
                     help="reps of the extra measurements (fused GEMM + KV write, paged chunk attention); 0 skips")
     ap.add_argument("--split-reps", type=int, default=100,
                     help="reps of the split-key-range side measurement (s=2048, one pass against split); 0 skips")
-    ap.add_argument("--clock-seconds", type=float, default=0.3,
-                    help="seconds of back-to-back attention launches while the GPU clocks are sampled; 0 skips")
+    ap.add_argument("--clock-seconds", type=float, default=1.0,
+                    help="seconds of back-to-back attention launches while the GPU clocks and socket power are "
+                         "sampled; 0 skips")
     ap.add_argument("--splitkv-only", action="store_true",
                     help="only run the split-key-range side measurement (--split-reps launches of each kernel)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -89,6 +90,57 @@ def memory_clock_mhz():
         return None
 
 
+class PowerSampler:
+    """Socket power (W) and its cap from amdsmi, sampled every 20 ms in a
+    thread while GPU work runs; the first 0.5 s are left out (the reading
+    trails the load by about that much).  Silent (None) where amdsmi is
+    missing or refuses."""
+
+    def __init__(self):
+        import threading
+        self.samples, self.cap, self._h = [], None, None
+        self._stop = threading.Event()
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._smi = amdsmi
+            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+            cap = amdsmi.amdsmi_get_power_cap_info(self._h).get("power_cap")
+            self.cap = cap / 1e6 if isinstance(cap, (int, float)) else None   # reported in microwatts
+        except Exception:
+            self._h = None
+        self._t = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        t0 = time.time()
+        while not self._stop.is_set():
+            try:
+                pw = self._smi.amdsmi_get_power_info(self._h).get("current_socket_power")
+                if isinstance(pw, (int, float)) and time.time() - t0 >= 0.5:
+                    self.samples.append(float(pw))
+            except Exception:
+                pass
+            time.sleep(0.02)
+
+    def __enter__(self):
+        if self._h is not None:
+            self._t.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._h is not None:
+            self._stop.set()
+            self._t.join()
+            try:
+                self._smi.amdsmi_shut_down()
+            except Exception:
+                pass
+
+    def result(self):
+        return {"socket_power_w": sum(self.samples) / len(self.samples) if self.samples else None,
+                "power_cap_w": self.cap, "power_samples": len(self.samples)}
+
+
 def sample_clocks(pca, torch, launch, seconds):
     """Average shader clock of each XCD while `launch` runs back to back for
     about `seconds`, from the GPU's own counters (two pca.clock_stamp calls on
@@ -107,18 +159,20 @@ def sample_clocks(pca, torch, launch, seconds):
     e1.record()
     torch.cuda.synchronize()
     n = max(1, int(seconds * 1e3 / max(e0.elapsed_time(e1), 1e-3)))
-    pca.clock_stamp(a)
-    for _ in range(n):
-        launch()
-    pca.clock_stamp(b)
-    torch.cuda.synchronize()
+    with PowerSampler() as pw:
+        pca.clock_stamp(a)
+        for _ in range(n):
+            launch()
+        pca.clock_stamp(b)
+        torch.cuda.synchronize()
     per_xcd = pca.shader_clock_mhz(a.cpu().numpy(), b.cpu().numpy())
     vals = sorted(per_xcd.values())
     return {"sclk_mhz": vals[len(vals) // 2] if vals else None, "sclk_per_xcd_mhz": per_xcd,
-            "mclk_mhz": memory_clock_mhz(),
+            "mclk_mhz": memory_clock_mhz(), **pw.result(),
             "note": f"shader clock = s_memtime cycles / s_memrealtime (100 MHz) on each CU's own counters over {n} "
                     "back-to-back attention launches after the timed steps, per XCD the median over its CUs, "
-                    "sclk_mhz the median over XCDs; mclk from amdsmi"}
+                    "sclk_mhz the median over XCDs; mclk from amdsmi; socket_power_w: amdsmi's socket power "
+                    "averaged over those launches after their first 0.5 s, power_cap_w the board's cap"}
 
 
 def cpu_baseline(w, target_s):
