@@ -1,5 +1,5 @@
 // Shared pieces of the two MFMA GEMMs (bf16 and fp8 operands): tile
-// geometry, the LDS swizzle, inline-asm LDS reads and waits, the barrier, the
+// geometry, the LDS swizzle, inline-asm LDS reads, the barrier, the
 // XCD-aware tile order and wave-uniform buffer resources.  Both kernels keep
 // K steps of 128 bytes per operand row (64 bf16 or 128 fp8 elements), so
 // their DMA and LDS layouts are byte-identical.
@@ -16,16 +16,13 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) char lds_char_t;
 
 constexpr int BM = 256, BN = 256;
-// wave shape of the fp8 GEMM (four waves, one per SIMD, 128 x 128 each); the
-// bf16 GEMM runs eight waves of 128 (n) x 64 (m) and keeps its own constants
-constexpr int kThreads = 256;
-constexpr int FN = 4, FM = 4;                 // 32x32 blocks per wave (n, m)
+// (both GEMMs run eight waves of 128 (n) x 64 (m) and keep their wave
+// constants in their own files)
 constexpr int ROWB = 128;                     // bytes per tile row (one K step: 64 bf16 or 128 fp8)
 constexpr int TILE_B = 256 * ROWB;            // 32 KiB: one operand tile
 constexpr int STAGE_B = 2 * TILE_B;           // W tile, then X tile
 constexpr int LDS_BYTES = 2 * STAGE_B;        // 128 KiB
 constexpr int DMA_PER_TILE = TILE_B / 1024;   // 32 one-KiB DMA blocks per operand tile
-constexpr int DMA_PER_WAVE = DMA_PER_TILE / 4;  // 8 per operand per wave (four waves)
 constexpr int kGroupM = 8;
 constexpr uint32_t kOob = 0x80000000u;        // an offset past every buffer: loads return 0
 
@@ -51,15 +48,6 @@ __device__ __forceinline__ u32x4_t lds_read_b128(uint32_t addr) {
     u32x4_t r;
     asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
     return r;
-}
-
-// Wait until at most N LDS operations are outstanding (LDS returns in order);
-// the fragments pass through the asm so their consumers stay after the wait.
-template <int N>
-__device__ __forceinline__ void lds_wait8(u32x4_t (&f)[8]) {
-    asm volatile("s_waitcnt lgkmcnt(%8)"
-                 : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(f[4]), "+v"(f[5]), "+v"(f[6]), "+v"(f[7])
-                 : "n"(N));
 }
 
 // Workgroup barrier with no implied waits: the operand DMA of the next K step

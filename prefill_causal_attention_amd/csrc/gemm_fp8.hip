@@ -8,16 +8,18 @@
 // code = E4M3_RNE_saturate(v * (448 / amax)); then
 //   y[m, n] = RNE_bf16(sx[m] * sw[n] * sum_k dec(xq[m, k]) * dec(wq[n, k])).
 //
-// gfx950 design: the bf16 GEMM's tiles, DMA and LDS layout unchanged in bytes
-// (a K step is 128 fp8 = 128 bytes per row), with
-// v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales): 2x the bf16 MFMA rate
-// per cycle, half the LDS bytes per flop.  A 64-wide MFMA K slice is two
-// 16-byte chunks per lane (lane half h takes bytes 32h .. 32h+31 of the
-// slice in both operands, so the products pair up), 16 reads per slice for
-// the 4 x 4 blocks, which exceeds the 15 LDS operations a wave can track: the
-// next slice's reads go out in two groups of 8 between the current slice's
-// two groups of 8 MFMAs.  The row scales multiply the fp32 accumulators in
-// the staged epilogue, before the single rounding.
+// gfx950 design: the bf16 GEMM's tiling, DMA and LDS layout byte for byte
+// (a K step is 128 fp8 = 128 bytes per row, two 64-wide slices), with
+// v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales): 2x the bf16 MFMA
+// rate per cycle, half the LDS bytes per flop.  Eight waves, two per SIMD,
+// each 64 (m) x 128 (n) as 2 x 4 blocks with its 128 fp32 accumulators in
+// AGPRs and its operands in VGPRs.  A slice is two 16-byte parts per lane
+// and block (lane half h takes bytes 32h .. 32h+31 of the slice in both
+// operands, so the products pair up), read as one 8-register tuple.  The next
+// slice's x blocks are read at a slice's start, and its W block i right
+// after block i's two MFMAs into the same registers, so 64 operand registers
+// keep two slices in flight.  The row scales multiply the fp32 accumulators
+// in the staged epilogue, before the single rounding.
 #include "gemm_common.hpp"
 #include "kv_common.hpp"
 #include "pca_internal.hpp"
@@ -32,30 +34,31 @@ typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int BK8 = 128;                      // fp8 elements per K step (ROWB bytes)
 
+// Eight waves, two per SIMD, each 64 (m) x 128 (n) as 2 x 4 blocks: the
+// bf16 GEMM's tiling, DMA and LDS layout, with a K step of 128 fp8 bytes =
+// two 64-wide MFMA slices.  Only waves 0-3 request tiles; the other wave of
+// each SIMD issues MFMAs through their wait at the DMA.
+constexpr int kWavesF8 = 8;
+constexpr int kThreadsF8 = kWavesF8 * 64;
+constexpr int FN8 = 4, FM8 = 2;                // blocks per wave along n, m
+
+// Wait until at most N LDS reads are outstanding (LDS returns in order); the
+// operand tuples pass through the asm so the MFMAs stay after it.
 template <int N>
-__device__ __forceinline__ void lds_wait16(u32x4_t (&f)[16]) {
-    asm volatile("s_waitcnt lgkmcnt(%16)"
-                 : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(f[4]), "+v"(f[5]), "+v"(f[6]), "+v"(f[7]),
-                   "+v"(f[8]), "+v"(f[9]), "+v"(f[10]), "+v"(f[11]), "+v"(f[12]), "+v"(f[13]), "+v"(f[14]),
-                   "+v"(f[15])
+__device__ __forceinline__ void lds_wait_ops8(i32x8_t (&w)[4], i32x8_t (&x)[2], i32x8_t (&xn)[2]) {
+    asm volatile("s_waitcnt lgkmcnt(%8)"
+                 : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]), "+v"(x[0]), "+v"(x[1]), "+v"(xn[0]), "+v"(xn[1])
                  : "n"(N));
 }
 
-__device__ inline f32x16_t mfma_f8(u32x4_t a0, u32x4_t a1, u32x4_t b0, u32x4_t b1, f32x16_t c) {
-    const i32x8_t a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-    const i32x8_t b = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
-    // formats 0/0: E4M3 for A and B; block scales 127 = 2^0
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
-}
-
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreadsF8) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_fp8_kernel(Fp8GemmArgs a) {
     extern __shared__ __align__(16) uint16_t smem[];
     lds_char_t* lds = (lds_char_t*)smem;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave & 1, wn = wave >> 1;
+    const int wm = wave >> 1, wn = wave & 1;       // 4 (m) x 2 (n)
     const int r32 = lane & 31, half = lane >> 5;
 
     const int tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
@@ -65,131 +68,142 @@ void gemm_fp8_kernel(Fp8GemmArgs a) {
     const int rows_x = min(BM, a.M - m0), rows_w = min(BN, a.N - n0);
     const int nk = (a.K + BK8 - 1) / BK8;
 
-    // DMA: block b of a wave covers rows 8b .. 8b + 7 (128 bytes each); lane l
-    // fetches logical chunk (l % 8) ^ swz(row) of row 8b + l / 8
-    uint32_t offx[DMA_PER_WAVE], offw[DMA_PER_WAVE];
-    int lchunk[DMA_PER_WAVE];
-#pragma unroll
-    for (int i = 0; i < DMA_PER_WAVE; ++i) {
-        const int row = (wave * DMA_PER_WAVE + i) * 8 + lane / 8;
-        lchunk[i] = (lane % 8) ^ swz(row);
-        offx[i] = (uint32_t)((int64_t)row * a.ldx + lchunk[i] * 16);
-        offw[i] = (uint32_t)((int64_t)row * a.ldw + lchunk[i] * 16);
-    }
+    // DMA (waves 0-3, 8 blocks of each operand tile): block i of wave w covers
+    // rows (8w + i) * 8 .. + 7; lane l fetches logical chunk (l % 8) ^ swz(row)
+    // of row (8w + i) * 8 + l / 8.  swz of that row depends on i only through
+    // i & 1, so two lane chunk values serve all eight blocks, and block i adds
+    // the uniform 64 i rows.
+    const int dw = wave & 3;
+    const int row0 = dw * 64 + lane / 8;
+    int lch[2];
+    lch[0] = (lane % 8) ^ swz(row0);
+    lch[1] = (lane % 8) ^ swz(row0 + 8);
+    const uint32_t basew = (uint32_t)((int64_t)row0 * a.ldw), basex = (uint32_t)((int64_t)row0 * a.ldx);
     auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
+        if (wave >= 4) return;                        // uniform per wave
         const int k0 = kt * BK8;
         const bool tail = k0 + BK8 > a.K;
         const __amdgpu_buffer_rsrc_t rw = uniform_rsrc(a.w + (int64_t)n0 * a.ldw + k0, (int64_t)rows_w * a.ldw - k0);
         const __amdgpu_buffer_rsrc_t rx = uniform_rsrc(a.x + (int64_t)m0 * a.ldx + k0, (int64_t)rows_x * a.ldx - k0);
         lds_char_t* dst = lds + stage * STAGE_B;
 #pragma unroll
-        for (int i = 0; i < DMA_PER_WAVE; ++i) {
-            const int blk = wave * DMA_PER_WAVE + i;
-            const bool oob = tail && (k0 + lchunk[i] * 16 >= a.K);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void_t*)(dst + blk * 1024), 16,
-                                                     oob ? kOob : offw[i], 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(dst + TILE_B + blk * 1024), 16,
-                                                     oob ? kOob : offx[i], 0, 0, 0);
+        for (int i = 0; i < 8; ++i) {
+            const int blk = dw * 8 + i;
+            const bool oob = tail && (k0 + lch[i & 1] * 16 >= a.K);
+            // (the whole offset in the VGPR: the range check covers it, not soffset)
+            const uint32_t ow = basew + (uint32_t)(i * 8 * a.ldw) + (uint32_t)(lch[i & 1] * 16);
+            const uint32_t ox = basex + (uint32_t)(i * 8 * a.ldx) + (uint32_t)(lch[i & 1] * 16);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void_t*)(dst + blk * 1024), 16, oob ? kOob : ow, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(dst + TILE_B + blk * 1024), 16, oob ? kOob : ox,
+                                                     0, 0, 0);
         }
     };
 
-    // operand addresses: slice ks (bytes 64 ks .. 64 ks + 63 of the K step),
-    // part q: logical chunk 4 ks + 2 half + q of row block*32 + r32
-    uint32_t waddr[2][2], xaddr[2][2];
+    // operand reads of slice s (bytes 64 s .. 64 s + 63 of the K step), part
+    // q: logical chunk 4 s + 2 half + q of row block * 32 + r32
+    uint32_t rdaddr[2][2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int sl = 0; sl < 2; ++sl)
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const uint32_t base = (uint32_t)(uintptr_t)lds + r32 * ROWB + (((ks * 4 + half * 2 + q) ^ swz(r32)) * 16);
-            waddr[ks][q] = base + wn * 128 * ROWB;
-            xaddr[ks][q] = base + wm * 128 * ROWB;
-        }
+        for (int q = 0; q < 2; ++q)
+            rdaddr[sl][q] = (uint32_t)(uintptr_t)lds + r32 * ROWB + (((sl * 4 + half * 2 + q) ^ swz(r32)) * 16);
+    const uint32_t woff = wn * 128 * ROWB, xoff = TILE_B + wm * 64 * ROWB;
 
-    f32x16_t acc[FN][FM];
+    f32x16_t acc[FN8][FM8];
 #pragma unroll
-    for (int i = 0; i < FN; ++i)
+    for (int i = 0; i < FN8; ++i)
 #pragma unroll
-        for (int j = 0; j < FM; ++j)
+        for (int j = 0; j < FM8; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    // reads of slice ks: W blocks (f[0..7] = block i, part q at 2i + q), then
-    // X blocks (f[8..15])
-    auto read_w = [&](uint32_t soff, auto KSc, u32x4_t (&f)[16]) __attribute__((always_inline)) {
-        constexpr int ks = decltype(KSc)::value;
-        static_for<FN>([&](auto Ic) {
-            constexpr int i = decltype(Ic)::value;
-            f[2 * i] = lds_read_b128<i * 32 * ROWB>(waddr[ks][0] + soff);
-            f[2 * i + 1] = lds_read_b128<i * 32 * ROWB>(waddr[ks][1] + soff);
-        });
+    // Operands of the slice on the matrix cores: wf[2i + q] = W block i part
+    // q, xf[2j + q] = X block j part q.  The next slice's X parts are read
+    // into xn at the slice's start; its W block i is read into wf[2i..2i+1]
+    // right after block i's two MFMAs, so 64 operand registers serve two
+    // slices in flight.  LDS returns in order, so each block's wait counts
+    // the reads issued after it.
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    // one 8-register tuple per block (both 16-byte parts), as the MFMA takes it
+    i32x8_t wf[4], xf[2], xn[2];
+    auto pair = [](u32x4_t lo, u32x4_t hi) __attribute__((always_inline)) {
+        return __builtin_bit_cast(i32x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
-    auto read_x = [&](uint32_t soff, auto KSc, u32x4_t (&f)[16]) __attribute__((always_inline)) {
-        constexpr int ks = decltype(KSc)::value;
-        static_for<FM>([&](auto Jc) {
+    auto read_w = [&](uint32_t soff, auto Sc, auto Ic) __attribute__((always_inline)) {
+        constexpr int sl = decltype(Sc)::value, i = decltype(Ic)::value;
+        wf[i] = pair(lds_read_b128<i * 32 * ROWB>(rdaddr[sl][0] + soff + woff),
+                     lds_read_b128<i * 32 * ROWB>(rdaddr[sl][1] + soff + woff));
+    };
+    auto read_x = [&](uint32_t soff, auto Sc, i32x8_t (&x)[2]) __attribute__((always_inline)) {
+        constexpr int sl = decltype(Sc)::value;
+        static_for<FM8>([&](auto Jc) {
             constexpr int j = decltype(Jc)::value;
-            f[8 + 2 * j] = lds_read_b128<TILE_B + j * 32 * ROWB>(xaddr[ks][0] + soff);
-            f[8 + 2 * j + 1] = lds_read_b128<TILE_B + j * 32 * ROWB>(xaddr[ks][1] + soff);
+            x[j] = pair(lds_read_b128<j * 32 * ROWB>(rdaddr[sl][0] + soff + xoff),
+                        lds_read_b128<j * 32 * ROWB>(rdaddr[sl][1] + soff + xoff));
         });
     };
-    // the 16 MFMAs of a slice in two halves (W blocks 0-1, then 2-3)
-    auto mfmas = [&](auto Hc, const u32x4_t (&f)[16]) __attribute__((always_inline)) {
-        constexpr int h = decltype(Hc)::value;
-        static_for<8>([&](auto Ic) {
-            constexpr int i = h * 2 + decltype(Ic)::value / FM, j = decltype(Ic)::value % FM;
-            acc[i][j] = mfma_f8(f[2 * i], f[2 * i + 1], f[8 + 2 * j], f[8 + 2 * j + 1], acc[i][j]);
+    auto wait_ops = [&](auto Nc) __attribute__((always_inline)) { lds_wait_ops8<decltype(Nc)::value>(wf, xf, xn); };
+    // the slice's 8 MFMAs, block by block, with the next slice's W block read
+    // in behind each (into stage soff_next, slice SN)
+    auto run_slice = [&](uint32_t soff_next, auto SNc) __attribute__((always_inline)) {
+        static_for<FN8>([&](auto Ic) {
+            constexpr int i = decltype(Ic)::value;
+            // outstanding before block i's wait: this slice's W blocks i+1..3
+            // (2 reads each, issued in the previous slice), then xn (4), then
+            // the next slice's W blocks 0..i-1 (2 each)
+            wait_ops(std::integral_constant<int, 2 * (FN8 - 1 - i) + 4 + 2 * i>{});
+            static_for<FM8>([&](auto Jc) {
+                constexpr int j = decltype(Jc)::value;
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[i], xf[j], acc[i][j], 0, 0, 0, 127, 0,
+                                                                            127);
+                // keep the accumulators in AGPRs (the VGPRs hold the operands)
+                asm volatile("" : "+a"(acc[i][j]));
+            });
+            __builtin_amdgcn_sched_barrier(0);
+            read_w(soff_next, SNc, Ic);
+            __builtin_amdgcn_sched_barrier(0);
         });
-        // the products' next use is past the barrier and the loop's branches;
-        // an asm that reads them keeps the compiler from sinking these MFMAs
-        // down to it (they would then no longer overlap the operand reads)
-#pragma unroll
-        for (int q = 0; q < 8; ++q) asm volatile("" ::"a"(acc[h * 2 + q / FM][q % FM]));
-        __builtin_amdgcn_sched_barrier(0);
+        xf[0] = xn[0];
+        xf[1] = xn[1];
     };
-    using KS0 = std::integral_constant<int, 0>;
-    using KS1 = std::integral_constant<int, 1>;
-    using H0 = std::integral_constant<int, 0>;
-    using H1 = std::integral_constant<int, 1>;
 
     issue(0, 0);
     if (1 < nk) issue(1, 1);
-    if (1 < nk) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DMA_PER_WAVE));   // step 0 only
+    if (1 < nk) __builtin_amdgcn_s_waitcnt(vmcnt_imm(16));   // step 0 only
     else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     wg_barrier();
-    u32x4_t f0[16], f1[16];
-    read_w(0u, KS0{}, f0);
-    read_x(0u, KS0{}, f0);
-    lds_wait16<0>(f0);
+    static_for<FN8>([&](auto Ic) { read_w(0u, S0{}, Ic); });
+    read_x(0u, S0{}, xf);
     for (int kt = 0; kt < nk; ++kt) {
         const int st = kt & 1;
         const uint32_t soff = (uint32_t)(st * STAGE_B);
-        // slice 0 on the matrix cores, slice 1's operands read in between
-        mfmas(H0{}, f0);
-        read_w(soff, KS1{}, f1);
-        mfmas(H1{}, f0);
-        read_x(soff, KS1{}, f1);
-        lds_wait16<0>(f1);
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // this wave's loads of step kt + 1
+        // slice 0 of step kt; slice 1's operands (same stage) read behind it
+        read_x(soff, S1{}, xn);
+        run_slice(soff, S1{});
+        wait_ops(std::integral_constant<int, 0>{});
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));    // this wave's loads of step kt + 1
         wg_barrier();
-        // slice 1 on the matrix cores, the next step's slice 0 read in between
-        mfmas(H0{}, f1);
-        if (kt + 1 < nk) read_w(soff ^ (uint32_t)STAGE_B, KS0{}, f0);
+        // slice 1; the next step's slice 0 (other stage) read behind it, and
+        // step kt + 2's tiles requested into this stage
+        // (after the last step these reads fetch stale LDS bytes that are
+        // never used: unconditional, so no branch splits the MFMA sequence)
+        read_x(soff ^ (uint32_t)STAGE_B, S0{}, xn);
         if (kt + 2 < nk) issue(kt + 2, st);
-        mfmas(H1{}, f1);
-        if (kt + 1 < nk) read_x(soff ^ (uint32_t)STAGE_B, KS0{}, f0);
-        lds_wait16<0>(f0);
+        run_slice(soff ^ (uint32_t)STAGE_B, S0{});
     }
 
     // epilogue: y = sx[m] * sw[n] * acc, rounded once, staged through LDS and
-    // written as full rows (as in the bf16 GEMM)
+    // written as full rows
     wg_barrier();
-    lds_char_t* stg = lds + wave * (128 * 256);
-    const int m_lo = m0 + wm * 128;
+    lds_char_t* stg = lds + wave * (64 * 256);
+    const int m_lo = m0 + wm * 64;
 #pragma unroll
-    for (int j = 0; j < FM; ++j) {
+    for (int j = 0; j < FM8; ++j) {
         const int m = m_lo + j * 32 + r32;
         const float sxm = m < a.M ? a.sx[m] : 0.0f;
 #pragma unroll
-        for (int i = 0; i < FN; ++i)
+        for (int i = 0; i < FN8; ++i)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int nn = n0 + wn * 128 + i * 32 + g * 8 + half * 4;
@@ -204,7 +218,7 @@ void gemm_fp8_kernel(Fp8GemmArgs a) {
     const int c = lane & 15;
     const int n = n0 + wn * 128 + c * 8;
 #pragma unroll 4
-    for (int r = 0; r < 32; ++r) {
+    for (int r = 0; r < 16; ++r) {
         const int ml = r * 4 + (lane >> 4);
         const u32x4_t v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(
             stg + ml * 256 + ((c ^ (ml & 15)) * 16));
@@ -307,7 +321,7 @@ hipError_t launch_gemm_fp8(const Fp8GemmArgs& a, hipStream_t s) {
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
     if (attr != hipSuccess) return attr;
     const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-    hipLaunchKernelGGL(gemm_fp8_kernel, dim3(tiles), dim3(kThreads), LDS_BYTES, s, a);
+    hipLaunchKernelGGL(gemm_fp8_kernel, dim3(tiles), dim3(kThreadsF8), LDS_BYTES, s, a);
     return hipGetLastError();
 }
 
