@@ -88,5 +88,46 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* p, in
     return make_rsrc((const void*)ub, (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes));
 }
 
+// Grid shape (the data-flow article's §5.2 "wave" effect: a grid of 384
+// tiles on 256 CUs takes two rounds for one and a half rounds of work).  A
+// 128-row tile costs about 0.6 of a 256-row one (per-tile start-up and
+// epilogue, half the operand reuse).
+//  * A grid whose 128-row tiles all fit in one round of the CUs runs on them:
+//    1024 x 6144 x 4096 has 96 tiles of 256 rows, which leave 160 CUs idle,
+//    and runs 1.37-1.45x faster as 192 tiles of 128 rows.
+//  * A grid of 256-row tiles whose last round is at most half full keeps the
+//    full rounds in 256-row tiles (whole column strips) and turns the rest
+//    into one round of 128-row tiles: 2048 x 12288 x 4096 is one round of 256
+//    tiles of 256 rows plus 256 tiles of 128 rows (1.10x faster than 384
+//    tiles of 256 rows, whose second round is half idle; 3000 x 6144 x 4096:
+//    1.19x).  Only for grids of at most kMaxMixedRounds full rounds: 27808 x
+//    6144 x 4096 (ten full rounds and a fifth) measured 2% slower mixed.
+//  * Otherwise 256-row tiles throughout (a grid of only 128-row tiles
+//    measured 16-22% slower than 256-row tiles on every multi-round shape).
+// (Measured on the bf16 GEMM; the fp8 GEMM, with the same tiles, follows the
+// same plan: 2048 x 12288 x 4096 +10%, 1024 x 6144 x 4096 +30%.)
+constexpr int64_t kMaxMixedRounds = 3;
+
+struct TilePlan {
+    int bmt;       // 256, 128, or 0: split_n strips of 256-row tiles, then 128-row tiles
+    int tiles;
+    int split_n;
+};
+
+inline TilePlan plan_tiles(int64_t M, int64_t N, int64_t ncu) {
+    const int64_t tn = (N + BN - 1) / BN, tm256 = (M + 255) / 256, tm128 = (M + 127) / 128;
+    const int64_t t256 = tm256 * tn, t128 = tm128 * tn;
+    if (ncu > 0) {
+        if (t256 < t128 && t128 <= ncu) return {128, (int)t128, 0};
+        const int64_t full = t256 / ncu * ncu;               // tiles of the full rounds
+        if (full > 0 && full < t256 && full <= kMaxMixedRounds * ncu) {
+            const int64_t n1 = full / tm256;                 // strips of 256-row tiles within them
+            const int64_t small = tm128 * (tn - n1);
+            if (n1 >= 1 && n1 < tn && small <= ncu) return {0, (int)(tm256 * n1 + small), (int)n1};
+        }
+    }
+    return {256, (int)t256, 0};
+}
+
 }  // namespace gemm
 }  // namespace pca

@@ -34,13 +34,14 @@ typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int BK8 = 128;                      // fp8 elements per K step (ROWB bytes)
 
-// Eight waves, two per SIMD, each 64 (m) x 128 (n) as 2 x 4 blocks: the
-// bf16 GEMM's tiling, DMA and LDS layout, with a K step of 128 fp8 bytes =
-// two 64-wide MFMA slices.  Only waves 0-3 request tiles; the other wave of
-// each SIMD issues MFMAs through their wait at the DMA.
+// Eight waves, two per SIMD, each BMT / 4 (m) x 128 (n) as FM8 x 4 blocks
+// (BMT = 256 or 128 rows of x per tile): the bf16 GEMM's tiling, DMA and LDS
+// layout, with a K step of 128 fp8 bytes = two 64-wide MFMA slices.  Only
+// waves 0-3 request tiles; the other wave of each SIMD issues MFMAs through
+// their wait at the DMA.
 constexpr int kWavesF8 = 8;
 constexpr int kThreadsF8 = kWavesF8 * 64;
-constexpr int FN8 = 4, FM8 = 2;                // blocks per wave along n, m
+constexpr int FN8 = 4;                         // blocks per wave along n
 
 // Wait until at most N LDS reads are outstanding (LDS returns in order); the
 // operand tuples pass through the asm so the MFMAs stay after it.
@@ -50,9 +51,19 @@ __device__ __forceinline__ void lds_wait_ops8(i32x8_t (&w)[4], i32x8_t (&x)[2], 
                  : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]), "+v"(x[0]), "+v"(x[1]), "+v"(xn[0]), "+v"(xn[1])
                  : "n"(N));
 }
+template <int N>
+__device__ __forceinline__ void lds_wait_ops8(i32x8_t (&w)[4], i32x8_t (&x)[1], i32x8_t (&xn)[1]) {
+    asm volatile("s_waitcnt lgkmcnt(%6)"
+                 : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]), "+v"(x[0]), "+v"(xn[0])
+                 : "n"(N));
+}
 
-__global__ __launch_bounds__(kThreadsF8) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void gemm_fp8_kernel(Fp8GemmArgs a) {
+// One workgroup computes output tile (tm, tn) of BMT rows.
+template <int BMT>
+__device__ __forceinline__ void gemm_fp8_tile(const Fp8GemmArgs& a, int tm, int tn) {
+    constexpr int FM8 = BMT / 128;                 // blocks per wave along m
+    constexpr int WMR = 32 * FM8;                  // x rows per wave
+    constexpr int DMA_X = BMT / 32;                // 1 KiB DMA blocks of the x tile per requesting wave
     extern __shared__ __align__(16) uint16_t smem[];
     lds_char_t* lds = (lds_char_t*)smem;
     const int tid = threadIdx.x;
@@ -61,24 +72,22 @@ void gemm_fp8_kernel(Fp8GemmArgs a) {
     const int wm = wave >> 1, wn = wave & 1;       // 4 (m) x 2 (n)
     const int r32 = lane & 31, half = lane >> 5;
 
-    const int tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
-    int tm, tn;
-    tile_coords(tiles_m, tiles_n, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-    const int rows_x = min(BM, a.M - m0), rows_w = min(BN, a.N - n0);
+    const int m0 = tm * BMT, n0 = tn * BN;
+    const int rows_x = min(BMT, a.M - m0), rows_w = min(BN, a.N - n0);
     const int nk = (a.K + BK8 - 1) / BK8;
 
-    // DMA (waves 0-3, 8 blocks of each operand tile): block i of wave w covers
-    // rows (8w + i) * 8 .. + 7; lane l fetches logical chunk (l % 8) ^ swz(row)
-    // of row (8w + i) * 8 + l / 8.  swz of that row depends on i only through
-    // i & 1, so two lane chunk values serve all eight blocks, and block i adds
-    // the uniform 64 i rows.
+    // DMA (waves 0-3: 8 blocks of the W tile, DMA_X of the x tile each):
+    // block i of wave w covers rows (nb w + i) * 8 .. + 7 of its operand (nb
+    // its blocks per wave); lane l fetches logical chunk (l % 8) ^ swz(row) of
+    // row (nb w + i) * 8 + l / 8.  swz of that row depends on i only through
+    // i & 1 (nb w * 8 is a multiple of 32), so two lane chunk values serve all
+    // blocks, and block i adds the uniform 8 i rows.
     const int dw = wave & 3;
-    const int row0 = dw * 64 + lane / 8;
+    const int row0w = dw * 64 + lane / 8, row0x = dw * DMA_X * 8 + lane / 8;
     int lch[2];
-    lch[0] = (lane % 8) ^ swz(row0);
-    lch[1] = (lane % 8) ^ swz(row0 + 8);
-    const uint32_t basew = (uint32_t)((int64_t)row0 * a.ldw), basex = (uint32_t)((int64_t)row0 * a.ldx);
+    lch[0] = (lane % 8) ^ swz(row0w);
+    lch[1] = (lane % 8) ^ swz(row0w + 8);
+    const uint32_t basew = (uint32_t)((int64_t)row0w * a.ldw), basex = (uint32_t)((int64_t)row0x * a.ldx);
     auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
         if (wave >= 4) return;                        // uniform per wave
         const int k0 = kt * BK8;
@@ -86,16 +95,20 @@ void gemm_fp8_kernel(Fp8GemmArgs a) {
         const __amdgpu_buffer_rsrc_t rw = uniform_rsrc(a.w + (int64_t)n0 * a.ldw + k0, (int64_t)rows_w * a.ldw - k0);
         const __amdgpu_buffer_rsrc_t rx = uniform_rsrc(a.x + (int64_t)m0 * a.ldx + k0, (int64_t)rows_x * a.ldx - k0);
         lds_char_t* dst = lds + stage * STAGE_B;
+        // (the whole offset in the VGPR: the range check covers it, not soffset)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int blk = dw * 8 + i;
             const bool oob = tail && (k0 + lch[i & 1] * 16 >= a.K);
-            // (the whole offset in the VGPR: the range check covers it, not soffset)
             const uint32_t ow = basew + (uint32_t)(i * 8 * a.ldw) + (uint32_t)(lch[i & 1] * 16);
-            const uint32_t ox = basex + (uint32_t)(i * 8 * a.ldx) + (uint32_t)(lch[i & 1] * 16);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void_t*)(dst + blk * 1024), 16, oob ? kOob : ow, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(dst + TILE_B + blk * 1024), 16, oob ? kOob : ox,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void_t*)(dst + (dw * 8 + i) * 1024), 16, oob ? kOob : ow,
                                                      0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < DMA_X; ++i) {
+            const bool oob = tail && (k0 + lch[i & 1] * 16 >= a.K);
+            const uint32_t ox = basex + (uint32_t)(i * 8 * a.ldx) + (uint32_t)(lch[i & 1] * 16);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(dst + TILE_B + (dw * DMA_X + i) * 1024), 16,
+                                                     oob ? kOob : ox, 0, 0, 0);
         }
     };
 
@@ -107,7 +120,7 @@ void gemm_fp8_kernel(Fp8GemmArgs a) {
 #pragma unroll
         for (int q = 0; q < 2; ++q)
             rdaddr[sl][q] = (uint32_t)(uintptr_t)lds + r32 * ROWB + (((sl * 4 + half * 2 + q) ^ swz(r32)) * 16);
-    const uint32_t woff = wn * 128 * ROWB, xoff = TILE_B + wm * 64 * ROWB;
+    const uint32_t woff = wn * 128 * ROWB, xoff = TILE_B + wm * WMR * ROWB;
 
     f32x16_t acc[FN8][FM8];
 #pragma unroll
@@ -126,7 +139,7 @@ void gemm_fp8_kernel(Fp8GemmArgs a) {
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
     // one 8-register tuple per block (both 16-byte parts), as the MFMA takes it
-    i32x8_t wf[4], xf[2], xn[2];
+    i32x8_t wf[4], xf[FM8], xn[FM8];
     auto pair = [](u32x4_t lo, u32x4_t hi) __attribute__((always_inline)) {
         return __builtin_bit_cast(i32x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
@@ -135,7 +148,7 @@ void gemm_fp8_kernel(Fp8GemmArgs a) {
         wf[i] = pair(lds_read_b128<i * 32 * ROWB>(rdaddr[sl][0] + soff + woff),
                      lds_read_b128<i * 32 * ROWB>(rdaddr[sl][1] + soff + woff));
     };
-    auto read_x = [&](uint32_t soff, auto Sc, i32x8_t (&x)[2]) __attribute__((always_inline)) {
+    auto read_x = [&](uint32_t soff, auto Sc, i32x8_t (&x)[FM8]) __attribute__((always_inline)) {
         constexpr int sl = decltype(Sc)::value;
         static_for<FM8>([&](auto Jc) {
             constexpr int j = decltype(Jc)::value;
@@ -150,9 +163,9 @@ void gemm_fp8_kernel(Fp8GemmArgs a) {
         static_for<FN8>([&](auto Ic) {
             constexpr int i = decltype(Ic)::value;
             // outstanding before block i's wait: this slice's W blocks i+1..3
-            // (2 reads each, issued in the previous slice), then xn (4), then
-            // the next slice's W blocks 0..i-1 (2 each)
-            wait_ops(std::integral_constant<int, 2 * (FN8 - 1 - i) + 4 + 2 * i>{});
+            // (2 reads each, issued in the previous slice), then xn (2 FM8),
+            // then the next slice's W blocks 0..i-1 (2 each)
+            wait_ops(std::integral_constant<int, 2 * (FN8 - 1 - i) + 2 * FM8 + 2 * i>{});
             static_for<FM8>([&](auto Jc) {
                 constexpr int j = decltype(Jc)::value;
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[i], xf[j], acc[i][j], 0, 0, 0, 127, 0,
@@ -164,13 +177,13 @@ void gemm_fp8_kernel(Fp8GemmArgs a) {
             read_w(soff_next, SNc, Ic);
             __builtin_amdgcn_sched_barrier(0);
         });
-        xf[0] = xn[0];
-        xf[1] = xn[1];
+#pragma unroll
+        for (int j = 0; j < FM8; ++j) xf[j] = xn[j];
     };
 
     issue(0, 0);
     if (1 < nk) issue(1, 1);
-    if (1 < nk) __builtin_amdgcn_s_waitcnt(vmcnt_imm(16));   // step 0 only
+    if (1 < nk) __builtin_amdgcn_s_waitcnt(vmcnt_imm(8 + DMA_X));   // step 0 only
     else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     wg_barrier();
     static_for<FN8>([&](auto Ic) { read_w(0u, S0{}, Ic); });
@@ -196,8 +209,8 @@ void gemm_fp8_kernel(Fp8GemmArgs a) {
     // epilogue: y = sx[m] * sw[n] * acc, rounded once, staged through LDS and
     // written as full rows
     wg_barrier();
-    lds_char_t* stg = lds + wave * (64 * 256);
-    const int m_lo = m0 + wm * 64;
+    lds_char_t* stg = lds + wave * (WMR * 256);
+    const int m_lo = m0 + wm * WMR;
 #pragma unroll
     for (int j = 0; j < FM8; ++j) {
         const int m = m_lo + j * 32 + r32;
@@ -218,7 +231,7 @@ void gemm_fp8_kernel(Fp8GemmArgs a) {
     const int c = lane & 15;
     const int n = n0 + wn * 128 + c * 8;
 #pragma unroll 4
-    for (int r = 0; r < 16; ++r) {
+    for (int r = 0; r < WMR / 4; ++r) {
         const int ml = r * 4 + (lane >> 4);
         const u32x4_t v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(
             stg + ml * 256 + ((c ^ (ml & 15)) * 16));
@@ -233,6 +246,38 @@ void gemm_fp8_kernel(Fp8GemmArgs a) {
                 if (n + e < a.N) dst[e] = (uint16_t)((v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
         }
     }
+}
+
+// The grid (the bf16 GEMM's plan_tiles): BMT 256 or 128, tiles of that
+// height; BMT 0, the first split_n column strips in 256-row tiles, then the
+// rest of N in 128-row tiles.
+template <int BMT>
+__global__ __launch_bounds__(kThreadsF8) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_fp8_kernel(Fp8GemmArgs a, int split_n) {
+    const int tiles_n = (a.N + BN - 1) / BN;
+    int tm, tn;
+    if constexpr (BMT != 0) {
+        tile_coords_id((int)blockIdx.x, (a.M + BMT - 1) / BMT, tiles_n, tm, tn);
+        gemm_fp8_tile<BMT>(a, tm, tn);
+    } else {
+        const int tm256 = (a.M + 255) / 256, big = tm256 * split_n;
+        if ((int)blockIdx.x < big) {
+            tile_coords_id((int)blockIdx.x, tm256, split_n, tm, tn);
+            gemm_fp8_tile<256>(a, tm, tn);
+        } else {
+            tile_coords_id((int)blockIdx.x - big, (a.M + 127) / 128, tiles_n - split_n, tm, tn);
+            gemm_fp8_tile<128>(a, tm, tn + split_n);
+        }
+    }
+}
+
+template <int BMT>
+hipError_t launch_fp8_tiles(const Fp8GemmArgs& a, int tiles, int split_n, hipStream_t s) {
+    static const hipError_t attr = hipFuncSetAttribute((const void*)gemm_fp8_kernel<BMT>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((gemm_fp8_kernel<BMT>), dim3(tiles), dim3(kThreadsF8), LDS_BYTES, s, a, split_n);
+    return hipGetLastError();
 }
 
 // Row-wise E4M3 quantisation: one wave per row, amax over the row (16-byte
@@ -317,12 +362,10 @@ hipError_t launch_quantize_heads(const uint16_t* x, int64_t ldx, int64_t T, int 
 }
 
 hipError_t launch_gemm_fp8(const Fp8GemmArgs& a, hipStream_t s) {
-    static const hipError_t attr = hipFuncSetAttribute((const void*)gemm_fp8_kernel,
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
-    if (attr != hipSuccess) return attr;
-    const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-    hipLaunchKernelGGL(gemm_fp8_kernel, dim3(tiles), dim3(kThreadsF8), LDS_BYTES, s, a);
-    return hipGetLastError();
+    const TilePlan t = plan_tiles(a.M, a.N, device_cus());
+    if (t.bmt == 128) return launch_fp8_tiles<128>(a, t.tiles, 0, s);
+    if (t.bmt == 0) return launch_fp8_tiles<0>(a, t.tiles, t.split_n, s);
+    return launch_fp8_tiles<256>(a, t.tiles, 0, s);
 }
 
 hipError_t launch_quantize_rows(const uint16_t* x, int64_t ldx, int M, int K, uint8_t* q, int64_t ldq, float* scales,

@@ -98,3 +98,24 @@ def test_full_size_sampled():
     y = _gemm_gpu(xq, sx, wq, sw)
     want = PJ.fp8_projection(xq.cpu().numpy(), sx.cpu().numpy(), wq.cpu().numpy(), sw.cpu().numpy(), rows=rows)
     assert_close(y[rows].float().cpu().numpy(), want, "fp8 gemm s=8192")
+
+
+@pytest.mark.parametrize("tall_m,short_m,N", [(12288, 1000, 6144), (12288, 2048, 12288), (12288, 3000, 6216)])
+def test_grid_plans_agree(tall_m, short_m, N):
+    """As for the bf16 GEMM: every grid plan sums each output's K terms in the
+    same order, so rows of a short call (128-row tiles, or the mixed grid of
+    256-row tiles then 128-row ones) equal bitwise those of a tall call on
+    256-row tiles throughout."""
+    require_gpu()
+    K = 1040                                            # a ragged last K step
+    x = workloads.normal_bf16(116, (tall_m, K))
+    w = workloads.normal_bf16(117, (N, K), std=float(1 / np.sqrt(K)))
+    say(f"qkv_proj_fp8 tile plans M={tall_m} and {short_m}, N={N} K={K}")
+    xq, sx = _quant_gpu(x)
+    wq, sw = _quant_gpu(w)
+    tall = _gemm_gpu(xq, sx, wq, sw)
+    short = _gemm_gpu(xq[:short_m], sx[:short_m], wq, sw)
+    assert torch.equal(short, tall[:short_m]), "grid plans disagree"
+    rows = sample_rows(short_m, 24, 118, must=(0, 127, 128, 255, 256, short_m - 1))
+    want = PJ.fp8_projection(xq.cpu().numpy(), sx.cpu().numpy(), wq.cpu().numpy(), sw.cpu().numpy(), rows=rows)
+    assert_close(short[rows].float().cpu().numpy(), want, "short fp8 call vs oracle rows")
