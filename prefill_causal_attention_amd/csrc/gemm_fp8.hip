@@ -42,6 +42,7 @@ constexpr int BK8 = 128;                      // fp8 elements per K step (ROWB b
 constexpr int kWavesF8 = 8;
 constexpr int kThreadsF8 = kWavesF8 * 64;
 constexpr int FN8 = 4;                         // blocks per wave along n
+constexpr int kLdsF8 = LDS_BYTES + (BN + BM) * 4;   // operand stages, then the tile's scales
 
 // Wait until at most N LDS reads are outstanding (LDS returns in order); the
 // operand tuples pass through the asm so the MFMAs stay after it.
@@ -181,8 +182,23 @@ __device__ __forceinline__ void gemm_fp8_tile(const Fp8GemmArgs& a, int tm, int 
         for (int j = 0; j < FM8; ++j) xf[j] = xn[j];
     };
 
-    issue(0, 0);
-    if (1 < nk) issue(1, 1);
+    // the tile's row and column scales, one per thread, into an LDS area past
+    // the operand stages: requested ahead of the first tiles, so their
+    // latency hides behind that wait (read from memory in the epilogue, 32
+    // per lane in batches of four, each batch waited for, they cost 5-7%)
+    // [0, 256): sw of the tile's columns, [256, 512): sx of its rows
+    __attribute__((address_space(3))) float* lsc = (__attribute__((address_space(3))) float*)(lds + LDS_BYTES);
+    {
+        float v = 0.0f;
+        if (tid < BN) {
+            if (n0 + tid < a.N) v = a.sw[n0 + tid];
+        } else if (tid - BN < BMT && m0 + (tid - BN) < a.M) {
+            v = a.sx[m0 + tid - BN];
+        }
+        issue(0, 0);
+        if (1 < nk) issue(1, 1);
+        lsc[tid] = v;
+    }
     if (1 < nk) __builtin_amdgcn_s_waitcnt(vmcnt_imm(8 + DMA_X));   // step 0 only
     else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     wg_barrier();
@@ -213,16 +229,16 @@ __device__ __forceinline__ void gemm_fp8_tile(const Fp8GemmArgs& a, int tm, int 
     const int m_lo = m0 + wm * WMR;
 #pragma unroll
     for (int j = 0; j < FM8; ++j) {
-        const int m = m_lo + j * 32 + r32;
-        const float sxm = m < a.M ? a.sx[m] : 0.0f;
+        const float sxm = lsc[BN + wm * WMR + j * 32 + r32];         // 0 past M
 #pragma unroll
         for (int i = 0; i < FN8; ++i)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int nn = n0 + wn * 128 + i * 32 + g * 8 + half * 4;
+                const int nl = wn * 128 + i * 32 + g * 8 + half * 4;      // column within the tile
+                const f32x4_t sw4 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4_t*>(lsc + nl);   // 0 past N
                 float t[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) t[e] = acc[i][j][g * 4 + e] * sxm * (nn + e < a.N ? a.sw[nn + e] : 0.0f);
+                for (int e = 0; e < 4; ++e) t[e] = acc[i][j][g * 4 + e] * sxm * sw4[e];
                 const int ml = j * 32 + r32, ci = i * 4 + g;
                 *reinterpret_cast<__attribute__((address_space(3))) u32x2_t*>(
                     stg + ml * 256 + ((ci ^ (ml & 15)) * 16) + half * 8) = u32x2_t{pack_bf16x2(t[0], t[1]), pack_bf16x2(t[2], t[3])};
@@ -274,9 +290,9 @@ void gemm_fp8_kernel(Fp8GemmArgs a, int split_n) {
 template <int BMT>
 hipError_t launch_fp8_tiles(const Fp8GemmArgs& a, int tiles, int split_n, hipStream_t s) {
     static const hipError_t attr = hipFuncSetAttribute((const void*)gemm_fp8_kernel<BMT>,
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsF8);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((gemm_fp8_kernel<BMT>), dim3(tiles), dim3(kThreadsF8), LDS_BYTES, s, a, split_n);
+    hipLaunchKernelGGL((gemm_fp8_kernel<BMT>), dim3(tiles), dim3(kThreadsF8), kLdsF8, s, a, split_n);
     return hipGetLastError();
 }
 
