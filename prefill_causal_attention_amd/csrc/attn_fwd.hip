@@ -413,6 +413,39 @@ __device__ __forceinline__ float dma_tile_fp8(__amdgpu_buffer_rsrc_t r, __amdgpu
     return sc;
 }
 
+// The page of the lane's row of the fp8 tile at kbase (-1 past Lk or for
+// waves that load no block), read ahead of its dma_tile_fp8_pg.
+template <int HD>
+__device__ __forceinline__ int paged_lookup8(int wave, int lane, int kbase, int Lk,
+                                             const __attribute__((address_space(3))) int32_t* lbt) {
+    using C = Cfg<HD>;
+    const int c = kbase + wave * C::RPI8 + lane / (HD / 16);
+    return wave < C::NB8 && c < Lk ? lbt[c >> 4] : -1;
+}
+
+// dma_tile_fp8 with the page looked up beforehand (paged_lookup8 of the same
+// tile).  Returns the row's scale.
+template <int HD>
+__device__ __forceinline__ float dma_tile_fp8_pg(__amdgpu_buffer_rsrc_t r, __amdgpu_buffer_rsrc_t rs, int wave,
+                                                 int lane, int kbase, int n_kv, int g, int num_pages, lds_char_t* dst8,
+                                                 int page) {
+    using C = Cfg<HD>;
+    float sc = 0.0f;
+    if (wave < C::NB8) {
+        const int row = wave * C::RPI8 + lane / (HD / 16);
+        const int c = kbase + row;
+        uint32_t off = kOob, soff = kOob;
+        if ((uint32_t)page < (uint32_t)num_pages) {
+            const int64_t srow = ((int64_t)page * 16 + (c & 15)) * n_kv + g;
+            off = (uint32_t)(srow * HD + (lane % (HD / 16)) * 16);
+            soff = (uint32_t)(srow * 4);
+        }
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(dst8 + wave * 1024), 16, off, 0, 0, 0);
+        sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, soff, 0, 0));
+    }
+    return sc;
+}
+
 // After the wave's own fp8 DMA has landed (vmcnt 0): decode its 16 codes
 // (OCP E4M3, exact in fp32), multiply by the row's scale, round to bf16 and
 // store them as two 16-byte chunks of the bf16 tile, with the K/V swizzle.
@@ -1060,13 +1093,27 @@ void attn_fwd_kernel(Params p) {
         // V_{m+1} (into V_{m-1}'s); both were last read in half-step 2m.  They are
         // waited for at the end of half-step 2m + 2 and first read in 2m + 3.
         // KC/KN: K buffers of tiles j and j + 1; VC/VN: V buffers of j and j + 1.
-        // bf16 pages: the pages of the tiles requested here were looked up one
-        // tile earlier (kpg: K_{j+2}, vpg: V_{j+1}); then V_{j+2} takes K_{j+2}'s
+        // Paged: the pages of the tiles requested here were looked up one tile
+        // earlier (kpg: K_{j+2}, vpg: V_{j+1}); then V_{j+2} takes K_{j+2}'s
         // pages and K_{j+3}'s are read, so no block-table read sits in front of
-        // the requests (it cost ~7% of the chunk attention)
+        // the requests (bf16 pages: it cost ~7% of the chunk attention)
         [[maybe_unused]] int kpg[C::DMA_ITERS], vpg[C::DMA_ITERS];
+        [[maybe_unused]] int kpg8 = -1, vpg8 = -1;               // the same for fp8 pages
         auto issue_next = [&](int j, auto KCc, auto VNc) __attribute__((always_inline)) {
-            if constexpr (PAGED == 1) {
+            if constexpr (PAGED == 2) {
+                if (j + 2 < ntiles) {
+                    pend_ks = dma_tile_fp8_pg<HD>(rk, rks, wave, lane, (j + 2) * BK, p.n_kv, g, p.num_pages,
+                                                  lds + f8_of(decltype(KCc)::value), kpg8);
+                    pend_k = decltype(KCc)::value;
+                }
+                if (j + 1 < ntiles) {
+                    pend_vs = dma_tile_fp8_pg<HD>(rv, rvs, wave, lane, (j + 1) * BK, p.n_kv, g, p.num_pages,
+                                                  lds + f8_of(decltype(VNc)::value), vpg8);
+                    pend_v = decltype(VNc)::value;
+                }
+                vpg8 = kpg8;
+                kpg8 = paged_lookup8<HD>(wave, lane, (j + 3) * BK, Lk, lbt);
+            } else if constexpr (PAGED == 1) {
                 if (j + 2 < ntiles)
                     dma_tile_paged_pg<HD>(rk, wave, lane, (j + 2) * BK, p.n_kv, g, p.num_pages,
                                           lds + decltype(KCc)::value, kpg);
@@ -1107,6 +1154,9 @@ void attn_fwd_kernel(Params p) {
         if constexpr (PAGED == 1) {
             paged_lookup<HD>(wave, lane, (j0 + 1) * BK, Lk, lbt, vpg);
             paged_lookup<HD>(wave, lane, (j0 + 2) * BK, Lk, lbt, kpg);
+        } else if constexpr (PAGED == 2) {
+            vpg8 = paged_lookup8<HD>(wave, lane, (j0 + 1) * BK, Lk, lbt);
+            kpg8 = paged_lookup8<HD>(wave, lane, (j0 + 2) * BK, Lk, lbt);
         }
 
         // ---- Q tile in registers (its loads overlap the first tiles' DMA): B
