@@ -121,6 +121,32 @@ def test_short_sequence_falls_back_bitwise():
     assert torch.equal(_run(w, d_buf, _workspace(w)), _run(w, d_buf))
 
 
+@pytest.mark.parametrize("lens,H,Hk,hd", [([1024], 32, 8, 64), ([700, 700], 8, 4, 128)])
+def test_parity_more_shapes(lens, H, Hk, hd):
+    """GQA G = 4 at hd 64; and two sequences of 4 kv heads, 8 units on the
+    8 XCDs."""
+    require_gpu()
+    w = workloads.custom(64, lens, H, Hk, hd)
+    buf, *_ = workloads.qkv_inputs(w)
+    say(f"splitkv lens={lens} heads={H}/{Hk} hd={hd}")
+    d_buf = dev(buf)
+    got = _run(w, d_buf, _workspace(w))
+    assert not torch.equal(got, _run(w, d_buf)), "no row was split (the split path did not run)"
+    q, k, v = A.head_split(bits(buf), H, Hk, hd)
+    want = A.varlen_causal_attention(q, k, v, workloads.cu_seqlens(w))
+    assert_close(got.float().cpu().numpy().astype(np.float64), want, f"splitkv {lens} {H}/{Hk} hd{hd}")
+
+
+def test_units_off_the_xcd_count_fall_back_bitwise():
+    """4 units (one sequence, 4 kv heads) do not spread evenly over the 8
+    XCDs: the one-pass kernel runs."""
+    require_gpu()
+    w = workloads.custom(65, [1024], 16, 4, 128)
+    buf, *_ = workloads.qkv_inputs(w)
+    d_buf = dev(buf)
+    assert torch.equal(_run(w, d_buf, _workspace(w)), _run(w, d_buf))
+
+
 def test_workspace_errors():
     require_gpu()
     w = workloads.custom(63, [2048], 32, 32, 128)
