@@ -352,6 +352,25 @@ pca_status pca_prefill_attention_paged(const pca_bf16* q, int64_t ldq, const int
                                        pca_bf16* o, int64_t ldo, void* stream);
 
 /*
+ * pca_prefill_attention_paged_window -- pca_prefill_attention_paged with a
+ *   sliding window ("Decoding LLM inference latency" (lnwmold.com/news/496245)
+ *   §4.1): chunk row r at position P + r sees the cached keys c with
+ *   P + r - window < c <= P + r, so a chunk over a long prefix reads only
+ *   the last window keys before each row; kv tiles wholly before a wave's
+ *   window are never requested.  window == 0 means no window (exactly
+ *   pca_prefill_attention_paged); window < 0 is PCA_ERR_INVALID_ARG.  Every
+ *   other argument, and the errors, as for pca_prefill_attention_paged.
+ */
+pca_status pca_prefill_attention_paged_window(const pca_bf16* q, int64_t ldq, const int32_t* cu_seqlens_q,
+                                              int num_seqs, int max_seqlen_q, int64_t total_q,
+                                              const int32_t* ctx_lens, int max_ctx_len, const int32_t* block_table,
+                                              int max_pages_per_seq, int page_size, pca_dtype cache_dtype,
+                                              const void* k_cache, const void* v_cache, const float* k_scale,
+                                              const float* v_scale, int64_t num_pages, int n_head, int n_kv_head,
+                                              int head_dim, float scale, int causal, int window, pca_bf16* o,
+                                              int64_t ldo, void* stream);
+
+/*
  * pca_kv_cache_write -- scatter each token's K and V into its page slot.
  *   Token position p of sequence b goes to page block_table[b*max_pages_per_seq
  *   + p / page_size], slot p % page_size (data-flow article §4.2,

@@ -25,7 +25,8 @@ EXPORTED = ("pca_kv_layout", "pca_qkv_proj", "pca_qkv_proj_kv_write", "pca_rms_n
             "pca_quantize_heads_fp8", "pca_prefill_attention_fp8qk",
             "pca_prefill_attention",
             "pca_prefill_attention_window", "pca_prefill_attention_splitkv",
-            "pca_prefill_attention_splitkv_workspace", "pca_prefill_attention_paged", "pca_kv_cache_write",
+            "pca_prefill_attention_splitkv_workspace", "pca_prefill_attention_paged",
+            "pca_prefill_attention_paged_window", "pca_kv_cache_write",
             "pca_clock_stamp", "pca_last_error", "pca_version")
 
 
@@ -82,8 +83,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pca_prefill_attention_splitkv_workspace.restype = ctypes.c_int64
     lib.pca_prefill_attention_paged.argtypes = [vp, i64, vp, i32, i32, i64, vp, i32, vp, i32, i32, i32, vp, vp,
                                                 vp, vp, i64, i32, i32, i32, f32, i32, vp, i64, vp]
+    lib.pca_prefill_attention_paged_window.argtypes = [vp, i64, vp, i32, i32, i64, vp, i32, vp, i32, i32, i32, vp,
+                                                       vp, vp, vp, i64, i32, i32, i32, f32, i32, i32, vp, i64, vp]
     for fn in ("pca_kv_layout", "pca_qkv_proj", "pca_prefill_attention", "pca_kv_cache_write",
-               "pca_qkv_proj_kv_write", "pca_prefill_attention_paged", "pca_prefill_attention_window",
+               "pca_qkv_proj_kv_write", "pca_prefill_attention_paged", "pca_prefill_attention_paged_window",
+               "pca_prefill_attention_window",
                "pca_prefill_attention_splitkv",
                "pca_out_proj_residual", "pca_rms_norm_qkv_proj", "pca_rms_norm_qkv_proj_noalloc",
                "pca_quantize_rows_fp8", "pca_qkv_proj_fp8",
@@ -471,10 +475,12 @@ def prefill_attention_paged(q, o, k_cache, v_cache, block_table, ctx_lens, n_hea
                             head_dim: int, cu_seqlens=None, max_seqlen: Optional[int] = None,
                             max_ctx: Optional[int] = None, scale: Optional[float] = None,
                             cache_dtype: str = "bf16", k_scale=None, v_scale=None, page_size: int = 16,
-                            total_tokens: Optional[int] = None, stream=None):
+                            total_tokens: Optional[int] = None, window: int = 0, stream=None):
     """Causal GQA attention of chunk rows q over the cached keys of their
     sequences (prefix then the chunk itself) read through the block table.
-    ctx_lens: int32 device tensor [num_seqs], keys per sequence."""
+    ctx_lens: int32 device tensor [num_seqs], keys per sequence.
+    window > 0: sliding window over the key positions (row at position p
+    sees keys p - window < c <= p)."""
     pq, ldq = _rows(q, "q")
     po, ldo = _rows(o, "o")
     T = q.shape[0] if total_tokens is None else int(total_tokens)
@@ -491,11 +497,14 @@ def prefill_attention_paged(q, o, k_cache, v_cache, block_table, ctx_lens, n_hea
     pbt, mp = _table(block_table, "block_table")
     pk, pv = _pool(k_cache, "k_cache", cache_dtype), _pool(v_cache, "v_cache", cache_dtype)
     num_pages = k_cache.numel() // (page_size * n_kv_head * head_dim)
-    _check("pca_prefill_attention_paged", load().pca_prefill_attention_paged(
-        pq, ldq, pcu, num_seqs, int(max_seqlen), T, pctx, int(max_ctx),
-        pbt, mp, page_size, DTYPES[cache_dtype], pk, pv, _ptr(k_scale, "k_scale", "f32"),
-        _ptr(v_scale, "v_scale", "f32"), num_pages, n_head, n_kv_head, head_dim, float(scale), 1,
-        po, ldo, _stream(stream)))
+    args = (pq, ldq, pcu, num_seqs, int(max_seqlen), T, pctx, int(max_ctx),
+            pbt, mp, page_size, DTYPES[cache_dtype], pk, pv, _ptr(k_scale, "k_scale", "f32"),
+            _ptr(v_scale, "v_scale", "f32"), num_pages, n_head, n_kv_head, head_dim, float(scale), 1)
+    if window:
+        _check("pca_prefill_attention_paged_window", load().pca_prefill_attention_paged_window(
+            *args, int(window), po, ldo, _stream(stream)))
+    else:
+        _check("pca_prefill_attention_paged", load().pca_prefill_attention_paged(*args, po, ldo, _stream(stream)))
     return o
 
 

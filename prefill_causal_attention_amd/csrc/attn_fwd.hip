@@ -1488,7 +1488,10 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
         }
     }
     if (a.k8 != nullptr) return a.head_dim == 128 ? launch_cfg<128, 3, false>(a, s) : hipErrorInvalidValue;
-    if (a.block_table != nullptr) return a.k_scale != nullptr ? launch_hd<2, false>(a, s) : launch_hd<1, false>(a, s);
+    if (a.block_table != nullptr) {
+        if (a.window > 0) return a.k_scale != nullptr ? launch_hd<2, true>(a, s) : launch_hd<1, true>(a, s);
+        return a.k_scale != nullptr ? launch_hd<2, false>(a, s) : launch_hd<1, false>(a, s);
+    }
     return a.window > 0 ? launch_hd<0, true>(a, s) : launch_hd<0, false>(a, s);
 }
 

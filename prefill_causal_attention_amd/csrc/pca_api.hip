@@ -469,13 +469,15 @@ pca_status pca_prefill_attention_fp8qk(const pca_bf16* q, int64_t ldq, const uin
     return hip_status(pca::launch_attention(a, (hipStream_t)stream), "prefill_attention_fp8qk launch");
 }
 
-pca_status pca_prefill_attention_paged(const pca_bf16* q, int64_t ldq, const int32_t* cu_seqlens_q, int num_seqs,
-                                       int max_seqlen_q, int64_t total_q, const int32_t* ctx_lens, int max_ctx_len,
-                                       const int32_t* block_table, int max_pages_per_seq, int page_size,
-                                       pca_dtype cache_dtype, const void* k_cache, const void* v_cache,
-                                       const float* k_scale, const float* v_scale, int64_t num_pages,
-                                       int n_head, int n_kv_head, int head_dim, float scale, int causal,
-                                       pca_bf16* o, int64_t ldo, void* stream) {
+namespace {
+pca_status prefill_attention_paged_impl(const pca_bf16* q, int64_t ldq, const int32_t* cu_seqlens_q, int num_seqs,
+                                        int max_seqlen_q, int64_t total_q, const int32_t* ctx_lens, int max_ctx_len,
+                                        const int32_t* block_table, int max_pages_per_seq, int page_size,
+                                        pca_dtype cache_dtype, const void* k_cache, const void* v_cache,
+                                        const float* k_scale, const float* v_scale, int64_t num_pages,
+                                        int n_head, int n_kv_head, int head_dim, float scale, int causal, int window,
+                                        pca_bf16* o, int64_t ldo, void* stream) {
+    if (window < 0) return fail(PCA_ERR_INVALID_ARG, "window must be >= 0 (0: no window), got %d", window);
     if (total_q == 0 && num_seqs >= 1 && causal == 1) return ok();   // empty batch: nothing to read or write
     if (!q || !o || !k_cache || !v_cache || !block_table || !ctx_lens)
         return fail(PCA_ERR_INVALID_ARG, "null q, o, k_cache, v_cache, block_table or ctx_lens");
@@ -531,7 +533,36 @@ pca_status pca_prefill_attention_paged(const pca_bf16* q, int64_t ldq, const int
     a.block_table = block_table; a.max_pages_per_seq = max_pages_per_seq; a.ctx_lens = ctx_lens;
     a.max_ctx = max_ctx_len; a.pool_bytes = pool_bytes; a.num_pages = num_pages;
     a.k_scale = elem == 1 ? k_scale : nullptr; a.v_scale = elem == 1 ? v_scale : nullptr;
+    a.window = window;
     return hip_status(pca::launch_attention(a, (hipStream_t)stream), "prefill_attention_paged launch");
+}
+}  // namespace
+
+pca_status pca_prefill_attention_paged(const pca_bf16* q, int64_t ldq, const int32_t* cu_seqlens_q, int num_seqs,
+                                       int max_seqlen_q, int64_t total_q, const int32_t* ctx_lens, int max_ctx_len,
+                                       const int32_t* block_table, int max_pages_per_seq, int page_size,
+                                       pca_dtype cache_dtype, const void* k_cache, const void* v_cache,
+                                       const float* k_scale, const float* v_scale, int64_t num_pages,
+                                       int n_head, int n_kv_head, int head_dim, float scale, int causal,
+                                       pca_bf16* o, int64_t ldo, void* stream) {
+    return prefill_attention_paged_impl(q, ldq, cu_seqlens_q, num_seqs, max_seqlen_q, total_q, ctx_lens, max_ctx_len,
+                                        block_table, max_pages_per_seq, page_size, cache_dtype, k_cache, v_cache,
+                                        k_scale, v_scale, num_pages, n_head, n_kv_head, head_dim, scale, causal, 0, o,
+                                        ldo, stream);
+}
+
+pca_status pca_prefill_attention_paged_window(const pca_bf16* q, int64_t ldq, const int32_t* cu_seqlens_q,
+                                              int num_seqs, int max_seqlen_q, int64_t total_q,
+                                              const int32_t* ctx_lens, int max_ctx_len, const int32_t* block_table,
+                                              int max_pages_per_seq, int page_size, pca_dtype cache_dtype,
+                                              const void* k_cache, const void* v_cache, const float* k_scale,
+                                              const float* v_scale, int64_t num_pages, int n_head, int n_kv_head,
+                                              int head_dim, float scale, int causal, int window, pca_bf16* o,
+                                              int64_t ldo, void* stream) {
+    return prefill_attention_paged_impl(q, ldq, cu_seqlens_q, num_seqs, max_seqlen_q, total_q, ctx_lens, max_ctx_len,
+                                        block_table, max_pages_per_seq, page_size, cache_dtype, k_cache, v_cache,
+                                        k_scale, v_scale, num_pages, n_head, n_kv_head, head_dim, scale, causal,
+                                        window, o, ldo, stream);
 }
 
 pca_status pca_kv_cache_write(const pca_bf16* k, const pca_bf16* v, int64_t ldk, int64_t ldv,

@@ -197,6 +197,15 @@ static void attention_checks() {
                                                 (void*)A2, (void*)A3, nullptr, nullptr, 4096, 32, 8, 128, 0.088f, 1,
                                                 B(A4), 4096, nullptr));
     EXPECT(pca::g_attn.pool_bytes == 4096LL * 16 * 8 * 128 * 2 && pca::g_attn.k_scale == nullptr, "paged bf16 args");
+    EXPECT(pca::g_attn.window == 0, "paged call has no window");
+    CALL(PCA_OK, 1, pca_prefill_attention_paged_window(B(A1), 4096, cu, 8, 512, 4096, cu, 8192, cu, 512, 16,
+                                                       PCA_DTYPE_BF16, (void*)A2, (void*)A3, nullptr, nullptr, 4096,
+                                                       32, 8, 128, 0.088f, 1, 1024, B(A4), 4096, nullptr));
+    EXPECT(pca::g_attn.window == 1024 && pca::g_attn.block_table == cu, "paged window args");
+    CALL(PCA_ERR_INVALID_ARG, 0, pca_prefill_attention_paged_window(B(A1), 4096, cu, 8, 512, 4096, cu, 8192, cu, 512,
+                                                                    16, PCA_DTYPE_BF16, (void*)A2, (void*)A3, nullptr,
+                                                                    nullptr, 4096, 32, 8, 128, 0.088f, 1, INT_MIN,
+                                                                    B(A4), 4096, nullptr));
     CALL(PCA_ERR_UNSUPPORTED, 0, pca_prefill_attention_paged(B(A1), 4096, cu, 8, 512, 4096, cu, INT_MAX, cu, INT_MAX, 16,
                                                              PCA_DTYPE_BF16, (void*)A2, (void*)A3, nullptr, nullptr,
                                                              INT64_MAX / 16, 32, 8, 128, 0.088f, 1, B(A4), 4096,

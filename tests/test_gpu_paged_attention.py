@@ -40,7 +40,7 @@ def _case(seed, chunks, prefixes, H, Hk, hd, spare=3):
                 H=H, Hk=Hk, hd=hd)
 
 
-def _gpu(c, o_pad=8):
+def _gpu(c, o_pad=8, window=0):
     T = int(c["cu_q"][-1])
     nq = c["H"] * c["hd"]
     o = torch.full((T, nq + o_pad), float("nan"), dtype=torch.bfloat16, device="cuda")
@@ -50,7 +50,8 @@ def _gpu(c, o_pad=8):
     cu = dev(torch.from_numpy(c["cu_q"])) if len(c["ctx"]) > 1 else None
     pca.prefill_attention_paged(dev(c["q"]), o[:, :nq], kc, vc, d_bt, dev(torch.from_numpy(c["ctx"])),
                                 c["H"], c["Hk"], c["hd"], cu_seqlens=cu,
-                                max_seqlen=int(np.diff(c["cu_q"]).max()), max_ctx=int(c["ctx"].max()))
+                                max_seqlen=int(np.diff(c["cu_q"]).max()), max_ctx=int(c["ctx"].max()),
+                                window=window)
     torch.cuda.synchronize()
     assert torch.isnan(o[:, nq:].float()).all(), "wrote outside the heads"
     return o[:, :nq]
@@ -254,3 +255,57 @@ def test_table_entries_outside_the_pool(fp8):
     zc["bt"] = zbt
     want = _oracle_fp8(zc) if fp8 else _oracle(zc)
     assert_close(got, want, f"paged {'fp8' if fp8 else 'bf16'} zero page")
+
+
+def _oracle_window(c, window, kc, vc, ks=None, vs=None):
+    """Each sequence's cached keys gathered through the table, then the
+    window rule over key positions (oracle.prefix.window_causal_attention)."""
+    qb = bits(c["q"]).reshape(-1, c["H"], c["hd"])
+    cu, out = c["cu_q"], []
+    for b in range(len(c["ctx"])):
+        s0, s1, ctx = int(cu[b]), int(cu[b + 1]), int(c["ctx"][b])
+        k, v = PX.cached_keys(kc, vc, c["bt"], b, ctx, ks, vs)
+        out.append(PX.window_causal_attention(qb[s0:s1], k, v, window, prefix_len=ctx - (s1 - s0)))
+    return np.concatenate(out)
+
+
+@pytest.mark.parametrize("chunks,prefixes,H,Hk,hd,W", [
+    ([37], [100], 4, 2, 128, 48),                 # window inside the chunk's own span for late rows
+    ([129, 1, 50], [0, 300, 17], 8, 2, 128, 70),  # varlen, a 1-row chunk
+    ([200], [333], 4, 4, 32, 1),                  # W = 1: each row its own value
+    ([96, 40], [512, 1], 10, 2, 128, 300),        # G = 5, window reaching into the prefix
+])
+def test_window_over_pages_parity(chunks, prefixes, H, Hk, hd, W):
+    """pca_prefill_attention_paged_window (bf16 pages) against the window rule
+    over the gathered keys."""
+    require_gpu()
+    c = _case(81, chunks, prefixes, H, Hk, hd)
+    say(f"prefill_attention_paged_window chunks={chunks} prefixes={prefixes} heads={H}/{Hk} hd={hd} W={W}")
+    got = _gpu(c, window=W).float().cpu().numpy()
+    assert_close(got, _oracle_window(c, W, c["kc"], c["vc"]), f"paged window W={W}")
+
+
+def test_window_over_pages_wide_equals_plain_bitwise():
+    """A window covering every key is exactly the paged call without one."""
+    require_gpu()
+    c = _case(82, [129, 50], [300, 17], 8, 2, 128)
+    assert torch.equal(_gpu(c, window=100000), _gpu(c))
+
+
+def test_window_over_fp8_pages_parity():
+    """fp8 pages with a window: dequantised on load, against the oracle's
+    decode of the same codes and scales."""
+    require_gpu()
+    c = _case_fp8(83, [96, 40], [512, 1], 10, 2, 128)
+    W = 200
+    T, nq = int(c["cu_q"][-1]), c["H"] * c["hd"]
+    o = torch.full((T, nq), float("nan"), dtype=torch.bfloat16, device="cuda")
+    d_bt = dev(torch.from_numpy(np.where(c["bt"] < 0, 0, c["bt"]).astype(np.int32)))
+    pca.prefill_attention_paged(dev(c["q"]), o, dev(torch.from_numpy(c["kc"])), dev(torch.from_numpy(c["vc"])), d_bt,
+                                dev(torch.from_numpy(c["ctx"])), c["H"], c["Hk"], c["hd"],
+                                cu_seqlens=dev(torch.from_numpy(c["cu_q"])), max_seqlen=int(np.diff(c["cu_q"]).max()),
+                                max_ctx=int(c["ctx"].max()), cache_dtype="fp8_e4m3", k_scale=dev(torch.from_numpy(c["ks"])),
+                                v_scale=dev(torch.from_numpy(c["vs"])), window=W)
+    torch.cuda.synchronize()
+    want = _oracle_window(c, W, c["kc"], c["vc"], c["ks"], c["vs"])
+    assert_close(o.float().cpu().numpy(), want, f"paged fp8 window W={W}")

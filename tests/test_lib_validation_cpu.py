@@ -60,6 +60,15 @@ def test_paged_attention_validation():
     assert st == 0
 
 
+def test_paged_window_attention_validation():
+    """The windowed call checks its window, then everything the paged call checks."""
+    order = PAGED_ORDER[:-2] + ["win"] + PAGED_ORDER[-2:]
+    base = dict(PAGED_BASE, win=64)
+    bad = {("win", -1): 1, ("win", -(1 << 30)): 1, ("q", 0): 1, ("causal", 0): 1, ("hd", 96): 2, ("ps", 32): 2,
+           ("ks", FAKE): 1, ("mxc", 256): 1, ("scale", 0.0): 1}
+    _expect("pca_prefill_attention_paged_window", base, order, bad, {"scale": C})
+
+
 WIN_ORDER = ["q", "k", "v", "ldq", "ldk", "ldv", "cu", "ns", "mx", "T", "nh", "nkv", "hd", "scale", "causal", "win",
              "o", "ldo"]
 WIN_BASE = dict(q=FAKE, k=FAKE, v=FAKE, ldq=4096, ldk=1024, ldv=1024, cu=None, ns=1, mx=64, T=64, nh=32, nkv=8, hd=128,
