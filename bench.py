@@ -428,6 +428,18 @@ def main():
             "case": f"{nseq} sequences x {Lq}-row chunk over a {P}-key cached prefix, bf16 pages",
             "ms": t_paged, "flop": pflop, "tflops": pflop / (t_paged * 1e-3) / 1e12,
             "flop_count": "exact causal pairs, 4*hd*n_head per (query, visible key)"}
+        # the same chunks with a 1024-key sliding window over the key positions
+        W = 1024
+
+        def paged_window():
+            pca.prefill_attention_paged(pq, po, pk, pv, pbt, pctx, w.n_head, w.n_kv_head, w.head_dim,
+                                        cu_seqlens=pcu, max_seqlen=Lq, max_ctx=ctx, window=W)
+        t_pw = timed(paged_window, args.extra_reps)
+        pwflop = 4.0 * w.head_dim * w.n_head * nseq * Lq * W        # every chunk row sees exactly W keys here
+        extras["prefill_attention_paged_window"] = {
+            "case": f"{nseq} sequences x {Lq}-row chunk over a {P}-key cached prefix, bf16 pages, window {W}",
+            "ms": t_pw, "flop": pwflop, "tflops": pwflop / (t_pw * 1e-3) / 1e12,
+            "flop_count": "exact visible pairs, 4*hd*n_head per (query, key in its window)"}
         del pk, pv, pq, po
 
         if args.split_reps > 0:
