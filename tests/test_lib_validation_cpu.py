@@ -67,6 +67,13 @@ def test_paged_window_attention_validation():
     bad = {("win", -1): 1, ("win", -(1 << 30)): 1, ("q", 0): 1, ("causal", 0): 1, ("hd", 96): 2, ("ps", 32): 2,
            ("ks", FAKE): 1, ("mxc", 256): 1, ("scale", 0.0): 1}
     _expect("pca_prefill_attention_paged_window", base, order, bad, {"scale": C})
+    # an empty chunk batch is a no-op that needs no buffers; a negative window is still refused
+    a = dict(base, T=0, q=None, o=None, kc=None, vc=None, bt=None, ctx=None)
+    st, _ = _status("pca_prefill_attention_paged_window", *[C(a[k]) if k == "scale" else a[k] for k in order], None)
+    assert st == 0
+    a["win"] = -5
+    st, msg = _status("pca_prefill_attention_paged_window", *[C(a[k]) if k == "scale" else a[k] for k in order], None)
+    assert st == 1 and "window" in msg
 
 
 WIN_ORDER = ["q", "k", "v", "ldq", "ldk", "ldv", "cu", "ns", "mx", "T", "nh", "nkv", "hd", "scale", "causal", "win",
