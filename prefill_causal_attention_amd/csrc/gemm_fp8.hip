@@ -324,6 +324,46 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t* x, i
     if (lane == 0) scales[m] = amax / 448.0f;
 }
 
+// The same for rows of at most NI * 512 elements, held in registers between
+// the amax and the encoding, so x is read once (the loop above reads each row
+// twice; the second pass mostly hits the caches but still costs the loads).
+template <int NI>
+__global__ __launch_bounds__(256) void quantize_rows_reg_kernel(const uint16_t* x, int64_t ldx, int M, int K,
+                                                                uint8_t* q, int64_t ldq, float* scales) {
+    const int lane = threadIdx.x & 63;
+    const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (m >= M) return;                                   // uniform per wave
+    const uint16_t* row = x + (int64_t)m * ldx;
+    u32x4_t v[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int k = lane * 8 + i * 512;                 // K is a multiple of 16
+        v[i] = k < K ? *reinterpret_cast<const u32x4_t*>(row + k) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            amax = __builtin_fmaxf(amax, __builtin_fmaxf(__builtin_fabsf(bf16_lo(v[i][t])), __builtin_fabsf(bf16_hi(v[i][t]))));
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, off));
+    // binary32 round-to-nearest division (no fast-math): scale = amax / 448, inv = 448 / amax
+    const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int k = lane * 8 + i * 512;
+        if (k < K) {
+            const uint32_t lo = e4m3x4(bf16_lo(v[i][0]) * inv, bf16_hi(v[i][0]) * inv, bf16_lo(v[i][1]) * inv,
+                                       bf16_hi(v[i][1]) * inv);
+            const uint32_t hi = e4m3x4(bf16_lo(v[i][2]) * inv, bf16_hi(v[i][2]) * inv, bf16_lo(v[i][3]) * inv,
+                                       bf16_hi(v[i][3]) * inv);
+            *reinterpret_cast<u32x2_t*>(q + (int64_t)m * ldq + k) = u32x2_t{lo, hi};
+        }
+    }
+    if (lane == 0) scales[m] = amax / 448.0f;
+}
+
 // Per-(token, head) E4M3 rows with power-of-two scales (the fp8 operands of
 // the attention scores): R = head_dim / 8 lanes hold one row, 16 bytes each;
 // y = x * prescale in binary32, the row's amax by DPP (unsigned max of the
@@ -386,8 +426,13 @@ hipError_t launch_gemm_fp8(const Fp8GemmArgs& a, hipStream_t s) {
 
 hipError_t launch_quantize_rows(const uint16_t* x, int64_t ldx, int M, int K, uint8_t* q, int64_t ldq, float* scales,
                                 hipStream_t s) {
-    hipLaunchKernelGGL(quantize_rows_kernel, dim3((uint32_t)((M + 3) / 4)), dim3(256), 0, s, x, ldx, M, K, q, ldq,
-                       scales);
+    const dim3 grid((uint32_t)((M + 3) / 4));
+    if (K <= 8 * 512)
+        hipLaunchKernelGGL(quantize_rows_reg_kernel<8>, grid, dim3(256), 0, s, x, ldx, M, K, q, ldq, scales);
+    else if (K <= 16 * 512)
+        hipLaunchKernelGGL(quantize_rows_reg_kernel<16>, grid, dim3(256), 0, s, x, ldx, M, K, q, ldq, scales);
+    else
+        hipLaunchKernelGGL(quantize_rows_kernel, grid, dim3(256), 0, s, x, ldx, M, K, q, ldq, scales);
     return hipGetLastError();
 }
 
