@@ -407,22 +407,33 @@ namespace {
 
 // One wave per row: 16-byte loads along the row, fp32 sum of squares, a
 // cross-lane reduction, then 1 / sqrt(mean + eps) (IEEE division and square
-// root, no fast-math).  HBM-bound: reads x once.
+// root, no fast-math).  HBM-bound: reads x once.  The loads go out eight at a
+// time (4096 elements of the row per batch) before any of them is summed, so
+// a wave has 128 bytes per lane in flight instead of waiting on each load;
+// each lane still adds its elements in row order.
 __global__ __launch_bounds__(256) void rms_stats_kernel(const uint16_t* x, int64_t ldx, int M, int K, float eps,
                                                         float* inv_rms) {
+    constexpr int NB = 8;
     const int lane = threadIdx.x & 63;
     const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (m >= M) return;                                   // uniform per wave
     const uint16_t* row = x + (int64_t)m * ldx;
     float acc = 0.0f;
-    for (int k = lane * 8; k < K; k += 64 * 8) {          // K is a multiple of 8
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(row + k);
+    for (int k0 = lane * 8; k0 < K; k0 += NB * 512) {     // K is a multiple of 8
+        u32x4_t v[NB];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const float lo = bf16_lo(v[t]), hi = bf16_hi(v[t]);
-            acc = __builtin_fmaf(lo, lo, acc);
-            acc = __builtin_fmaf(hi, hi, acc);
+        for (int i = 0; i < NB; ++i) {
+            const int k = k0 + i * 512;
+            v[i] = k < K ? *reinterpret_cast<const u32x4_t*>(row + k) : u32x4_t{0u, 0u, 0u, 0u};
         }
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const float lo = bf16_lo(v[i][t]), hi = bf16_hi(v[i][t]);
+                acc = __builtin_fmaf(lo, lo, acc);
+                acc = __builtin_fmaf(hi, hi, acc);
+            }
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
