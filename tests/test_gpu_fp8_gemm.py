@@ -27,7 +27,7 @@ def _quant_gpu(x, pad=16):
     return q[:, :K], s[:M]
 
 
-@pytest.mark.parametrize("M,K", [(5, 16), (77, 4096), (300, 1040), (40, 8192), (9, 12288)])   # 12288: the two-pass loop
+@pytest.mark.parametrize("M,K", [(5, 16), (77, 4096), (300, 1040), (40, 8192), (17, 6160), (9, 12288)])   # 12288: the two-pass loop
 def test_quantize_rows_bit_exact(M, K):
     require_gpu()
     x = workloads.normal_bf16(111, (M, K))
